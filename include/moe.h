@@ -1,0 +1,200 @@
+/*
+ * moe.h -- C ABI of the one-GPU MoE layer hot path for AMD Instinct MI355X
+ * (gfx950).  Plain pointers and sizes only.
+ *
+ * What is computed follows the UniEP paper (arXiv 2604.19241): the "MoE
+ * workflow" paragraph (routing probabilities and top-k, a stable expert-grouped
+ * permutation, GroupGEMM -> SwiGLU -> GroupGEMM, gate-weighted combine, and a
+ * backward whose weight gradient is a transposed GroupGEMM), the "Deterministic
+ * Token Mapping" section (destination row = exclusive prefix of per-expert
+ * counts + the token's stable index inside its expert, no atomics deciding
+ * order), the "Top-k accumulation constraint" paragraph (a token's K
+ * contributions are summed together in one fixed order) and the MoonEP page
+ * (the dispatch gradient sums each token's K copies).
+ *
+ * Notation: T tokens, H hidden, F expert intermediate, E router experts,
+ * K top-k, e_local local experts [e_begin, e_begin+e_local), R routed local
+ * rows (= offsets[e_local], lives on the device), cap_rows the row capacity
+ * of every permuted buffer.  All matrices are row-major, last index
+ * contiguous.  bf16 values are raw 16-bit patterns; fp32 -> bf16 rounding is
+ * round-to-nearest-even.
+ *
+ * Conventions common to every entry point:
+ *  - All data pointers are DEVICE pointers, owned by the caller, and must be
+ *    16-byte aligned.  The library allocates nothing and keeps no state
+ *    between calls; calls on different streams with disjoint buffers may
+ *    run concurrently.
+ *  - Arguments are validated on the host before anything is enqueued; a
+ *    negative moe_status is returned and nothing runs on error.  Launch
+ *    failures are reported as MOE_EHIP.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = default stream) and
+ *    returns without waiting.  No call ever reads device memory from the
+ *    host, so R and per-expert row counts never leave the device.
+ *  - Results are bitwise identical from run to run: no floating-point
+ *    atomics, every sum has a fixed order.
+ *  - Rows of the permuted buffers at or beyond R are unspecified.
+ *  - Limits: H and F multiples of 64; 1 <= K <= 16, K <= E <= 512;
+ *    e_local <= 512; T*K < 2^31; cap_rows <= T*K.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t moe_bf16;  /* raw bf16 bit pattern */
+typedef void* moe_stream;   /* hipStream_t */
+
+enum moe_status {
+    MOE_OK = 0,
+    MOE_EINVAL = -1,      /* NULL pointer, or a size/count out of range */
+    MOE_ESHAPE = -2,      /* H or F not a multiple of 64, K > E, ... */
+    MOE_EALIGN = -3,      /* a pointer not 16-byte aligned */
+    MOE_EWORKSPACE = -4,  /* workspace NULL or smaller than required */
+    MOE_EHIP = -5         /* the HIP runtime reported a launch error */
+};
+
+enum moe_epilogue {
+    MOE_EPI_NONE = 0,       /* c = bf16(acc) */
+    MOE_EPI_SWIGLU_BWD = 1  /* acc is dh[rows,F]; writes c = [bf16(da) | bf16(db)] of width 2F */
+};
+
+/* Human-readable text of a moe_status value (static storage). */
+const char* moe_strerror(int status);
+
+/* Version of this ABI (incremented on any signature change). */
+int moe_abi_version(void);
+
+/*
+ * Routing (UniEP "MoE workflow": the router yields a probability
+ * distribution over experts per token, and each token goes to its top-k).
+ *   logits   fp32 [T,E]  router scores x.W_r (+bias), in.
+ *   topk_idx int32 [T,K] out: the K experts with the largest scores, ordered
+ *            by (score descending, expert id ascending); -0 == +0.
+ *   gates    fp32 [T,K] out: softmax probabilities of the chosen experts
+ *            renormalised over the K choices (they sum to 1).
+ */
+int moe_route(const float* logits, int T, int E, int K,
+              int32_t* topk_idx, float* gates, moe_stream stream);
+
+/* Bytes of workspace moe_permute needs for these sizes. */
+size_t moe_permute_workspace_size(int T, int K, int e_local);
+
+/*
+ * Stable expert-grouped permutation (UniEP "MoE workflow": tokens are
+ * grouped by expert in a deterministic order, a stable sort preserving the
+ * source sequence; "Deterministic Token Mapping": destination = exclusive
+ * prefix of counts + stable local index).
+ *   topk_idx int32 [T,K] in.  Pairs with e_begin <= idx < e_begin+e_local
+ *            are local; others are skipped.
+ *   x        bf16 [T,H] in.
+ *   counts   int32 [e_local]   out: local pairs per expert.
+ *   offsets  int32 [e_local+1] out: offsets[0]=0, offsets[j+1]=offsets[j]+counts[j].
+ *   pos      int32 [T,K] out: destination row of pair (t,k), or -1.
+ *   src      int32 [cap_rows] out: src[pos[t,k]] = t*K+k.
+ *   x_perm   bf16 [cap_rows,H] out: x_perm[pos[t,k]] = x[t] (bit copy).
+ *   status   int32 [1] out: 0, or 1 if R > cap_rows (rows >= cap_rows are
+ *            dropped: their pos is -1 and nothing is written for them;
+ *            counts/offsets still hold the true totals).
+ *   ws       device workspace of ws_bytes >= moe_permute_workspace_size().
+ * Rows are ordered by expert, then by token: bit-exact and independent of
+ * thread scheduling.
+ */
+int moe_permute(const int32_t* topk_idx, int T, int K, int e_begin, int e_local,
+                const moe_bf16* x, int H, int cap_rows,
+                int32_t* counts, int32_t* offsets, int32_t* pos, int32_t* src,
+                moe_bf16* x_perm, int32_t* status, void* ws, size_t ws_bytes,
+                moe_stream stream);
+
+/*
+ * Gate-scaled gather of the output gradient into expert-grouped order
+ * (UniEP "MoE workflow", backward: gradients with respect to the output are
+ * dispatched to the experts).
+ *   d_out   bf16 [T,H] in;  pos int32 [T,K] in (from moe_permute);
+ *   gates   fp32 [T,K] in, or NULL for weight 1.
+ *   dy_perm bf16 [cap_rows,H] out: dy_perm[pos[t,k]] = bf16(gate[t,k]*d_out[t]).
+ */
+int moe_gather(const moe_bf16* d_out, const int32_t* pos, const float* gates,
+               int T, int K, int H, moe_bf16* dy_perm, moe_stream stream);
+
+/*
+ * Padding-free gate/up GroupGEMM with fused SwiGLU (UniEP "MoE workflow":
+ * a GroupGEMM projects the tokens, then SwiGLU; "Scoreboard-based
+ * Synchronization": padding-free GroupGEMM over irregular per-expert tiles).
+ * For every row r of local expert j (offsets[j] <= r < offsets[j+1], rows at
+ * or beyond cap_rows ignored):
+ *   a = x_perm[r] . w_gate[j],  b = x_perm[r] . w_up[j]   (fp32 accumulate)
+ *   h[r] = bf16(silu(a) * b),   silu(a) = a / (1 + exp(-a))
+ *   ab_save[r] = [bf16(a) | bf16(b)]   (optional, for the backward)
+ *   x_perm  bf16 [cap_rows,H];  w_gate, w_up bf16 [e_local,H,F];
+ *   offsets int32 [e_local+1] (device);  h bf16 [cap_rows,F];
+ *   ab_save bf16 [cap_rows,2F] or NULL.
+ */
+int moe_grouped_gemm_swiglu(const moe_bf16* x_perm, const moe_bf16* w_gate,
+                            const moe_bf16* w_up, const int32_t* offsets,
+                            int e_local, int H, int F, int cap_rows,
+                            moe_bf16* h, moe_bf16* ab_save, moe_stream stream);
+
+/*
+ * Generic padding-free GroupGEMM over expert row groups (UniEP "MoE
+ * workflow": the second GroupGEMM projects back to H; backward: the dgrad
+ * GEMMs mirror the forward).
+ * For rows r of expert j:
+ *   trans_w = 0: w0[j] is [Kd,N] and acc = a[r,0:Kd] . w0[j]
+ *   trans_w = 1: w0[j] is [N,Kd] and acc = a[r,0:Kd] . w0[j]^T
+ *   w1 != NULL (trans_w = 1 only): a has 2*Kd columns and
+ *        acc = a[r,0:Kd] . w0[j]^T + a[r,Kd:2Kd] . w1[j]^T   (one accumulator)
+ *   epilogue MOE_EPI_NONE:       c[r,0:N] = bf16(acc)
+ *   epilogue MOE_EPI_SWIGLU_BWD: acc is dh; with a_, b_ = ab[r,0:N], ab[r,N:2N]
+ *        and s = sigmoid(a_): c[r,0:N] = bf16(dh*b_*s*(1+a_*(1-s))),
+ *        c[r,N:2N] = bf16(dh*a_*s).
+ *   lda, ldc: row strides in elements (multiples of 8).
+ * Forward down projection: (h, F, w_down, NULL, 0, ..., Kd=F, N=H) -> y.
+ * Backward: (dy_perm, H, w_down, NULL, 1, ..., Kd=H, N=F, SWIGLU_BWD, ab) -> dab;
+ *           (dab, 2F, w_gate, w_up, 1, ..., Kd=F, N=H) -> dx_perm.
+ */
+int moe_grouped_gemm(const moe_bf16* a, int lda, const moe_bf16* w0, const moe_bf16* w1,
+                     int trans_w, const int32_t* offsets, int e_local, int Kd, int N,
+                     int cap_rows, int epilogue, const moe_bf16* ab,
+                     moe_bf16* c, int ldc, moe_stream stream);
+
+/*
+ * Gate-weighted combine back to token order (UniEP "MoE workflow": results
+ * are weighted by their gating scores and aggregated per token; "Top-k
+ * accumulation constraint": a token's K contributions are summed only all
+ * together, in one fixed order).
+ *   out[t] = bf16( sum over k ascending with pos[t,k] >= 0 of gate[t,k]*y[pos[t,k]] )
+ * in fp32 from +0; a token with no local pair gets +0.  gates == NULL means
+ * weight 1: the backward's combine-gradient dX[t] = sum_k dx_perm[pos[t,k]]
+ * (MoonEP: the dispatch gradient sums each token's K copies).
+ *   y bf16 [cap_rows,H];  pos int32 [T,K];  gates fp32 [T,K] or NULL;
+ *   out bf16 [T,H].
+ */
+int moe_combine(const moe_bf16* y, const int32_t* pos, const float* gates,
+                int T, int K, int H, moe_bf16* out, moe_stream stream);
+
+/*
+ * Transposed GroupGEMM for weight gradients (UniEP "MoE workflow",
+ * backward: the weight gradient needs a transposed GroupGEMM that reduces
+ * over the token dimension; splitting that reduction changes the summation
+ * tree, so it runs in one fixed order).
+ *   dw[j] = a_j^T . b_j  (fp32 [e_local,M,N]), a_j = rows offsets[j]..offsets[j+1]-1
+ *   of a (bf16 [.,M], row stride lda), b_j likewise of b (bf16 [.,N], ldb).
+ * Each output element is one fp32 sum over the group's rows in a fixed
+ * blocked order (no split over rows, no atomics); an empty group writes 0.
+ *   dW_gate: (x_perm, H, dab, 2F, M=H, N=F);  dW_up: b = dab + F;
+ *   dW_down: (h, F, dy_perm, H, M=F, N=H).   M, N multiples of 64.
+ */
+int moe_wgrad(const moe_bf16* a, int lda, const moe_bf16* b, int ldb,
+              const int32_t* offsets, int e_local, int M, int N, int cap_rows,
+              float* dw, moe_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

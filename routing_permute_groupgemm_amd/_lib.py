@@ -1,0 +1,199 @@
+"""ctypes binding of libmoe.so (include/moe.h).
+
+Argument marshalling only: torch tensors are checked for dtype/contiguity,
+their device pointers and the current HIP stream are passed through, and a
+negative status becomes a MoeError.  Every computation runs in the HIP
+kernels.  There is no fallback: if the library is missing, loading fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+
+_p = ctypes.c_void_p
+_i = ctypes.c_int
+_z = ctypes.c_size_t
+
+# every symbol declared in include/moe.h, with its ctypes signature
+SIGNATURES = {
+    "moe_strerror": ([_i], ctypes.c_char_p),
+    "moe_abi_version": ([], _i),
+    "moe_route": ([_p, _i, _i, _i, _p, _p, _p], _i),
+    "moe_permute_workspace_size": ([_i, _i, _i], _z),
+    "moe_permute": ([_p, _i, _i, _i, _i, _p, _i, _i, _p, _p, _p, _p, _p, _p, _p, _z, _p], _i),
+    "moe_gather": ([_p, _p, _p, _i, _i, _i, _p, _p], _i),
+    "moe_grouped_gemm_swiglu": ([_p, _p, _p, _p, _i, _i, _i, _i, _p, _p, _p], _i),
+    "moe_grouped_gemm": ([_p, _i, _p, _p, _i, _p, _i, _i, _i, _i, _i, _p, _p, _i, _p], _i),
+    "moe_combine": ([_p, _p, _p, _i, _i, _i, _p, _p], _i),
+    "moe_wgrad": ([_p, _i, _p, _i, _p, _i, _i, _i, _i, _p, _p], _i),
+}
+
+MOE_EPI_NONE = 0
+MOE_EPI_SWIGLU_BWD = 1
+
+_lib = None
+
+
+class MoeError(RuntimeError):
+    pass
+
+
+def load() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError(f"{_LIB_PATH} is not built; run __graft_entry__.build() first")
+        lib = ctypes.CDLL(_LIB_PATH)
+        for name, (args, res) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = lib
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise MoeError(f"libmoe status {status}: {load().moe_strerror(status).decode()}")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _need(t, dtype, name):
+    if t.dtype != dtype or not t.is_contiguous() or not t.is_cuda:
+        raise MoeError(f"{name}: expected a contiguous {dtype} CUDA tensor, got {t.dtype} "
+                       f"contiguous={t.is_contiguous()} device={t.device}")
+
+
+def moe_route(logits, K, topk_idx=None, gates=None, stream=None):
+    _need(logits, torch.float32, "logits")
+    T, E = logits.shape
+    if topk_idx is None:
+        topk_idx = torch.empty((T, K), dtype=torch.int32, device=logits.device)
+    if gates is None:
+        gates = torch.empty((T, K), dtype=torch.float32, device=logits.device)
+    _check(load().moe_route(_ptr(logits), T, E, K, _ptr(topk_idx), _ptr(gates), _stream(stream)))
+    return topk_idx, gates
+
+
+def moe_permute_workspace_size(T, K, e_local) -> int:
+    return int(load().moe_permute_workspace_size(T, K, e_local))
+
+
+def moe_permute(topk_idx, e_begin, e_local, x, cap_rows, out=None, ws=None, stream=None):
+    """-> dict(counts, offsets, pos, src, x_perm, status) (all device tensors)."""
+    _need(topk_idx, torch.int32, "topk_idx")
+    _need(x, torch.bfloat16, "x")
+    T, K = topk_idx.shape
+    H = x.shape[1]
+    dev = x.device
+    o = out or {}
+    counts = o.get("counts")
+    if counts is None:
+        counts = torch.empty(max(e_local, 1), dtype=torch.int32, device=dev)
+    offsets = o.get("offsets")
+    if offsets is None:
+        offsets = torch.empty(e_local + 1, dtype=torch.int32, device=dev)
+    pos = o.get("pos")
+    if pos is None:
+        pos = torch.empty((T, K), dtype=torch.int32, device=dev)
+    src = o.get("src")
+    if src is None:
+        src = torch.empty(max(cap_rows, 1), dtype=torch.int32, device=dev)
+    x_perm = o.get("x_perm")
+    if x_perm is None:
+        x_perm = torch.empty((max(cap_rows, 1), H), dtype=torch.bfloat16, device=dev)
+    status = o.get("status")
+    if status is None:
+        status = torch.empty(4, dtype=torch.int32, device=dev)
+    need = moe_permute_workspace_size(T, K, e_local)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _check(load().moe_permute(_ptr(topk_idx), T, K, e_begin, e_local, _ptr(x), H, cap_rows,
+                              _ptr(counts), _ptr(offsets), _ptr(pos), _ptr(src), _ptr(x_perm),
+                              _ptr(status), _ptr(ws), ws.numel(), _stream(stream)))
+    return dict(counts=counts[:e_local], offsets=offsets, pos=pos, src=src, x_perm=x_perm,
+                status=status, ws=ws)
+
+
+def moe_gather(d_out, pos, gates, dy_perm, stream=None):
+    _need(d_out, torch.bfloat16, "d_out")
+    _need(pos, torch.int32, "pos")
+    if gates is not None:
+        _need(gates, torch.float32, "gates")
+    _need(dy_perm, torch.bfloat16, "dy_perm")
+    T, K = pos.shape
+    _check(load().moe_gather(_ptr(d_out), _ptr(pos), _ptr(gates), T, K, d_out.shape[1], _ptr(dy_perm),
+                             _stream(stream)))
+    return dy_perm
+
+
+def moe_grouped_gemm_swiglu(x_perm, w_gate, w_up, offsets, cap_rows, h=None, ab_save=None, stream=None):
+    _need(x_perm, torch.bfloat16, "x_perm")
+    _need(w_gate, torch.bfloat16, "w_gate")
+    _need(w_up, torch.bfloat16, "w_up")
+    _need(offsets, torch.int32, "offsets")
+    EL, H, F = w_gate.shape
+    if h is None:
+        h = torch.empty((x_perm.shape[0], F), dtype=torch.bfloat16, device=x_perm.device)
+    _check(load().moe_grouped_gemm_swiglu(_ptr(x_perm), _ptr(w_gate), _ptr(w_up), _ptr(offsets), EL, H, F,
+                                          cap_rows, _ptr(h), _ptr(ab_save), _stream(stream)))
+    return h
+
+
+def moe_grouped_gemm(a, w0, w1, trans_w, offsets, Kd, N, cap_rows, c, epilogue=MOE_EPI_NONE, ab=None,
+                     lda=None, ldc=None, stream=None):
+    _need(a, torch.bfloat16, "a")
+    _need(w0, torch.bfloat16, "w0")
+    if w1 is not None:
+        _need(w1, torch.bfloat16, "w1")
+    _need(offsets, torch.int32, "offsets")
+    _need(c, torch.bfloat16, "c")
+    if ab is not None:
+        _need(ab, torch.bfloat16, "ab")
+    EL = w0.shape[0]
+    lda = a.shape[1] if lda is None else lda
+    ldc = c.shape[1] if ldc is None else ldc
+    _check(load().moe_grouped_gemm(_ptr(a), lda, _ptr(w0), _ptr(w1), int(trans_w), _ptr(offsets), EL, Kd, N,
+                                   cap_rows, epilogue, _ptr(ab), _ptr(c), ldc, _stream(stream)))
+    return c
+
+
+def moe_combine(y, pos, gates, out=None, stream=None):
+    _need(y, torch.bfloat16, "y")
+    _need(pos, torch.int32, "pos")
+    if gates is not None:
+        _need(gates, torch.float32, "gates")
+    T, K = pos.shape
+    H = y.shape[1]
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
+    _check(load().moe_combine(_ptr(y), _ptr(pos), _ptr(gates), T, K, H, _ptr(out), _stream(stream)))
+    return out
+
+
+def moe_wgrad(a, lda, b, ldb, offsets, e_local, M, N, cap_rows, dw=None, a_col0=0, b_col0=0, stream=None):
+    """dw[j] = a_j^T b_j. a_col0/b_col0 offset the first column (e.g. b_col0=F for dW_up from dab)."""
+    _need(a, torch.bfloat16, "a")
+    _need(b, torch.bfloat16, "b")
+    _need(offsets, torch.int32, "offsets")
+    if dw is None:
+        dw = torch.empty((e_local, M, N), dtype=torch.float32, device=a.device)
+    _need(dw, torch.float32, "dw")
+    pa = a.data_ptr() + 2 * a_col0
+    pb = b.data_ptr() + 2 * b_col0
+    _check(load().moe_wgrad(pa, lda, pb, ldb, _ptr(offsets), e_local, M, N, cap_rows, _ptr(dw),
+                            _stream(stream)))
+    return dw

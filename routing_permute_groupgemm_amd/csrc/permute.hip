@@ -1,0 +1,284 @@
+// Stable expert-grouped permutation (a counting sort of the T*K routing pairs).
+//
+// UniEP paper, "MoE workflow": tokens are grouped by destination expert in a
+// deterministic order (a stable sort that keeps the source order);
+// "Deterministic Token Mapping": a token's destination is the exclusive
+// prefix of the per-expert counts plus its stable index inside the expert,
+// computed without atomics deciding any order.  Here the flat pair index
+// p = t*K + k is the sort's source order; since a token chooses an expert at
+// most once, ordering by p inside an expert is ordering by token.
+//
+// Four launches, none of which reads device data back to the host:
+//  1. count:   per block of TB tokens, an LDS histogram of local experts
+//              (integer adds commute, so the result has no order dependence);
+//              written expert-major to the workspace: ws[j*nblk + b].
+//  2. scan:    one block scans ws in place (exclusive, expert-major), so
+//              ws[j*nblk+b] becomes the first row of expert j owned by block b;
+//              also writes counts, offsets and the overflow status.
+//  3. rank:    each block ranks its pairs inside each expert with wave
+//              ballots (a match of equal expert ids, then a popcount of the
+//              lower lanes) and per-wave running counters in LDS, processed
+//              strictly in pair order; writes pos and src.
+//  4. copy:    one wave per token reads the token's row once (16-byte
+//              loads) and writes it to each of its local destination rows.
+#include "moe_common.hpp"
+
+namespace moe {
+
+constexpr int kPermTB = 256;  // tokens per block for count / rank
+constexpr int kMaxLocal = 512;
+
+__global__ __launch_bounds__(256) void perm_count_kernel(const int32_t* __restrict__ idx, int T, int K,
+                                                         int e_begin, int e_local, int nblk,
+                                                         int32_t* __restrict__ ws) {
+    __shared__ int hist[kMaxLocal];
+    for (int j = threadIdx.x; j < e_local; j += 256) hist[j] = 0;
+    __syncthreads();
+    const int64_t p0 = (int64_t)blockIdx.x * kPermTB * K;
+    const int64_t p1 = min(p0 + (int64_t)kPermTB * K, (int64_t)T * K);
+    for (int64_t p = p0 + threadIdx.x; p < p1; p += 256) {
+        int j = idx[p] - e_begin;
+        if ((unsigned)j < (unsigned)e_local) atomicAdd(&hist[j], 1);
+    }
+    __syncthreads();
+    for (int j = threadIdx.x; j < e_local; j += 256) ws[(int64_t)j * nblk + blockIdx.x] = hist[j];
+}
+
+// Inclusive scan of one value per thread over a 1024-thread block.
+__device__ __forceinline__ int block_inclusive_scan_1024(int v, int* sh_wave /*[16]*/) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        int o = __shfl_up(v, off, 64);
+        if (lane >= off) v += o;
+    }
+    if (lane == 63) sh_wave[wave] = v;
+    __syncthreads();
+    if (wave == 0) {
+        int w = lane < 16 ? sh_wave[lane] : 0;
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) {
+            int o = __shfl_up(w, off, 64);
+            if (lane >= off) w += o;
+        }
+        if (lane < 16) sh_wave[lane] = w;
+    }
+    __syncthreads();
+    int add = wave > 0 ? sh_wave[wave - 1] : 0;
+    __syncthreads();
+    return v + add;
+}
+
+__global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t* __restrict__ ws, int e_local, int nblk,
+                                                         int64_t cap_rows, int32_t* __restrict__ counts,
+                                                         int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ status) {
+    __shared__ int sh_wave[16];
+    __shared__ int sh_carry;
+    const int64_t n = (int64_t)e_local * nblk;
+    if (n == 0) {  // no tokens or no local experts: every count and offset is 0
+        for (int j = threadIdx.x; j <= e_local; j += 1024) {
+            offsets[j] = 0;
+            if (j < e_local) counts[j] = 0;
+        }
+        if (threadIdx.x == 0) status[0] = 0;
+        return;
+    }
+    if (threadIdx.x == 0) sh_carry = 0;
+    __syncthreads();
+    // chunks of 1024*ITEMS, each thread owns ITEMS consecutive entries
+    constexpr int ITEMS = 8;
+    for (int64_t base = 0; base < n; base += 1024 * ITEMS) {
+        int vals[ITEMS];
+        int sum = 0;
+        const int64_t my0 = base + (int64_t)threadIdx.x * ITEMS;
+#pragma unroll
+        for (int i = 0; i < ITEMS; ++i) {
+            vals[i] = (my0 + i < n) ? ws[my0 + i] : 0;
+            sum += vals[i];
+        }
+        int incl = block_inclusive_scan_1024(sum, sh_wave);
+        int run = sh_carry + incl - sum;
+#pragma unroll
+        for (int i = 0; i < ITEMS; ++i) {
+            if (my0 + i < n) {
+                ws[my0 + i] = run;
+                // the first block of expert j holds offsets[j]
+                int64_t q = my0 + i;
+                if (q % nblk == 0) offsets[q / nblk] = run;
+            }
+            run += vals[i];
+        }
+        __syncthreads();
+        if (threadIdx.x == 1023) sh_carry = run;
+        __syncthreads();
+    }
+    const int total = sh_carry;
+    if (threadIdx.x == 0) {
+        offsets[e_local] = total;
+        status[0] = (int64_t)total > cap_rows ? 1 : 0;
+    }
+    __syncthreads();
+    for (int j = threadIdx.x; j < e_local; j += 1024) {
+        int hi = (j + 1 < e_local) ? ws[(int64_t)(j + 1) * nblk] : total;
+        counts[j] = hi - ws[(int64_t)j * nblk];
+    }
+}
+
+// Lanes whose key equals this lane's key (keys < 2^nbits; inactive lanes excluded).
+__device__ __forceinline__ uint64_t match_key(int key, bool active, int nbits) {
+    uint64_t m = __ballot(active);
+    for (int b = 0; b < nbits; ++b) {
+        bool bit = (key >> b) & 1;
+        uint64_t on = __ballot(active && bit);
+        m &= bit ? on : ~on;
+    }
+    return m;
+}
+
+template <int KMAX>
+__global__ __launch_bounds__(256) void perm_rank_kernel(const int32_t* __restrict__ idx, int T, int K,
+                                                        int e_begin, int e_local, int nbits, int nblk,
+                                                        const int32_t* __restrict__ ws, int64_t cap_rows,
+                                                        int32_t* __restrict__ pos, int32_t* __restrict__ src) {
+    __shared__ int cnt[4][kMaxLocal];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int j = lane; j < e_local; j += 64) cnt[wave][j] = 0;
+    __syncthreads();
+    const int64_t npairs = (int64_t)T * K;
+    const int64_t p0 = (int64_t)blockIdx.x * kPermTB * K + (int64_t)wave * (kPermTB / 4) * K;
+    const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    int rk[KMAX], jj[KMAX];
+    // wave `wave` owns pairs [p0, p0 + 64*K): K iterations of 64 consecutive pairs
+#pragma unroll
+    for (int it = 0; it < KMAX; ++it) {
+        rk[it] = 0;
+        jj[it] = -1;
+        if (it < K) {
+            const int64_t p = p0 + (int64_t)it * 64 + lane;
+            int j = p < npairs ? idx[p] - e_begin : -1;
+            bool local = (unsigned)j < (unsigned)e_local;
+            uint64_t m = match_key(local ? j : 0, local, nbits);
+            if (local) {
+                int before = __popcll(m & lower);
+                int base = cnt[wave][j];
+                if (before == 0) cnt[wave][j] = base + __popcll(m);
+                rk[it] = base + before;
+                jj[it] = j;
+            }
+        }
+    }
+    __syncthreads();
+    // exclusive prefix of the four waves' counts, per expert
+    for (int j = threadIdx.x; j < e_local; j += 256) {
+        int s = 0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            int c = cnt[w][j];
+            cnt[w][j] = s;
+            s += c;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < KMAX; ++it) {
+        if (it < K) {
+            const int64_t p = p0 + (int64_t)it * 64 + lane;
+            if (p < npairs) {
+                int j = jj[it];
+                int row = -1;
+                if (j >= 0) {
+                    int64_t r = (int64_t)ws[(int64_t)j * nblk + blockIdx.x] + cnt[wave][j] + rk[it];
+                    if (r < cap_rows) {
+                        row = (int)r;
+                        src[r] = (int32_t)p;
+                    }
+                }
+                pos[p] = row;
+            }
+        }
+    }
+}
+
+// x_perm[pos[t,k]] = x[t]; 16-byte vectors; one wave per token, 4 tokens per block.
+template <int UNROLL>
+__global__ __launch_bounds__(256) void perm_copy_kernel(const u32x4* __restrict__ x, int T, int K, int H,
+                                                        const int32_t* __restrict__ pos,
+                                                        u32x4* __restrict__ x_perm) {
+    const int lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    const int my_pos = lane < K ? pos[t * K + lane] : -1;
+    if (__ballot(my_pos >= 0) == 0ull) return;  // no local pair
+    const int nv = H >> 3;                        // 16-byte vectors per row
+    const u32x4* xr = x + t * nv;
+    for (int v0 = 0; v0 < nv; v0 += 64 * UNROLL) {
+        u32x4 buf[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            int v = v0 + u * 64 + lane;
+            if (v < nv) buf[u] = __builtin_nontemporal_load(xr + v);
+        }
+        for (int k = 0; k < K; ++k) {
+            int r = __shfl(my_pos, k, 64);
+            if (r < 0) continue;
+            u32x4* dst = x_perm + (int64_t)r * nv;
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                int v = v0 + u * 64 + lane;
+                if (v < nv) dst[v] = buf[u];
+            }
+        }
+    }
+}
+
+}  // namespace moe
+
+extern "C" size_t moe_permute_workspace_size(int T, int K, int e_local) {
+    (void)K;
+    if (T < 0 || e_local < 0) return 0;
+    int64_t nblk = (T + moe::kPermTB - 1) / moe::kPermTB;
+    int64_t n = nblk * (int64_t)e_local;
+    return (size_t)((n * 4 + 255) / 256 * 256 + 256);
+}
+
+extern "C" int moe_permute(const int32_t* topk_idx, int T, int K, int e_begin, int e_local,
+                           const moe_bf16* x, int H, int cap_rows, int32_t* counts, int32_t* offsets,
+                           int32_t* pos, int32_t* src, moe_bf16* x_perm, int32_t* status, void* ws,
+                           size_t ws_bytes, moe_stream stream) {
+    using namespace moe;
+    using moe_host::misaligned;
+    if (T < 0 || K < 1 || K > 16 || e_begin < 0 || e_local < 0 || e_local > kMaxLocal || H < 0 ||
+        cap_rows < 0)
+        return MOE_EINVAL;
+    if ((int64_t)T * K >= (1ll << 31) || (int64_t)cap_rows > (int64_t)T * K) return MOE_EINVAL;
+    if (H % 64 != 0) return MOE_ESHAPE;
+    if (!offsets || !status) return MOE_EINVAL;
+    if (e_local > 0 && !counts) return MOE_EINVAL;
+    if (T > 0 && (!topk_idx || !pos)) return MOE_EINVAL;
+    if (cap_rows > 0 && (!src || (H > 0 && (!x || !x_perm)))) return MOE_EINVAL;
+    if (misaligned(topk_idx) || misaligned(x) || misaligned(counts) || misaligned(offsets) ||
+        misaligned(pos) || misaligned(src) || misaligned(x_perm) || misaligned(status) || misaligned(ws))
+        return MOE_EALIGN;
+    const size_t need = moe_permute_workspace_size(T, K, e_local);
+    if (!ws || ws_bytes < need) return MOE_EWORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    const int nblk = (T + kPermTB - 1) / kPermTB;
+    int nbits = 0;
+    while ((1 << nbits) < e_local) ++nbits;
+    int32_t* w = (int32_t*)ws;
+    if (nblk > 0 && e_local > 0)
+        perm_count_kernel<<<nblk, 256, 0, s>>>(topk_idx, T, K, e_begin, e_local, nblk, w);
+    perm_scan_kernel<<<1, 1024, 0, s>>>(w, e_local, nblk, cap_rows, counts, offsets, status);
+    if (nblk > 0) {
+        if (K <= 8)
+            perm_rank_kernel<8><<<nblk, 256, 0, s>>>(topk_idx, T, K, e_begin, e_local, nbits, nblk, w,
+                                                    cap_rows, pos, src);
+        else
+            perm_rank_kernel<16><<<nblk, 256, 0, s>>>(topk_idx, T, K, e_begin, e_local, nbits, nblk, w,
+                                                     cap_rows, pos, src);
+        if (H > 0)
+            perm_copy_kernel<4><<<(T + 3) / 4, 256, 0, s>>>((const u32x4*)x, T, K, H, pos, (u32x4*)x_perm);
+    }
+    return moe_host::launch_status();
+}

@@ -1,0 +1,137 @@
+// Routing: softmax over router scores and top-k with a total order.
+//
+// UniEP paper, "MoE workflow": the router gives each token a probability
+// distribution over the experts and each token is sent to its top-k.  The
+// chosen experts are ordered by (score descending, expert id ascending);
+// selecting on the fp32 scores equals selecting on the probabilities
+// (softmax is monotonic) and is immune to rounding ties.  The gates are the
+// chosen probabilities renormalised over the K choices; the softmax
+// normaliser cancels, so g_k = exp(s_k - s_max) / sum_k' exp(s_k' - s_max).
+//
+// One wave64 per token.  Each lane holds E/64 scores as 64-bit keys
+// (order-preserving score bits << 32 | ~expert id), so the K rounds of a
+// wave-wide max give the total order directly; the winner's key is cleared.
+// Loads of a row are coalesced (lane-strided), the kernel is HBM-bound.
+#include "moe_common.hpp"
+
+namespace moe {
+
+__device__ __forceinline__ uint64_t score_key(float s, int e) {
+    if (s == 0.0f) s = 0.0f;  // -0 and +0 compare equal: canonicalise to +0
+    uint32_t u = __float_as_uint(s);
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)u << 32) | (uint32_t)(0xffffffffu - (uint32_t)e);
+}
+
+__device__ __forceinline__ float key_score(uint64_t k) {
+    uint32_t u = (uint32_t)(k >> 32);
+    u = (u & 0x80000000u) ? (u & 0x7fffffffu) : ~u;
+    return __uint_as_float(u);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        uint64_t o = __shfl_xor(v, off, 64);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+template <int EPL>
+__global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int T, int E, int K,
+                                                    int32_t* __restrict__ topk_idx,
+                                                    float* __restrict__ gates) {
+    const int lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    const float* row = logits + t * E;
+    uint64_t key[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        int e = i * 64 + lane;
+        key[i] = e < E ? score_key(__builtin_nontemporal_load(row + e), e) : 0ull;
+    }
+    int my_idx = 0;
+    float my_score = 0.0f, s_max = 0.0f;
+    for (int k = 0; k < K; ++k) {
+        uint64_t best = key[0];
+#pragma unroll
+        for (int i = 1; i < EPL; ++i) best = key[i] > best ? key[i] : best;
+        best = wave_max_u64(best);
+#pragma unroll
+        for (int i = 0; i < EPL; ++i)
+            if (key[i] == best) key[i] = 0ull;
+        float s = key_score(best);
+        if (k == 0) s_max = s;
+        if (lane == k) {
+            my_idx = (int)(0xffffffffu - (uint32_t)best);
+            my_score = s;
+        }
+    }
+    // gates: lanes 0..K-1 hold one choice each; the sum runs over k ascending
+    float ex = lane < K ? expf(my_score - s_max) : 0.0f;
+    float z = 0.0f;
+    for (int k = 0; k < K; ++k) z += __shfl(ex, k, 64);
+    if (lane < K) {
+        topk_idx[t * K + lane] = my_idx;
+        gates[t * K + lane] = ex / z;
+    }
+}
+
+}  // namespace moe
+
+extern "C" int moe_route(const float* logits, int T, int E, int K, int32_t* topk_idx, float* gates,
+                         moe_stream stream) {
+    using namespace moe;
+    if (T < 0 || E < 1 || E > 512 || K < 1 || K > 16) return MOE_EINVAL;
+    if (K > E) return MOE_ESHAPE;
+    if ((int64_t)T * K >= (1ll << 31) || (int64_t)T * E >= (1ll << 40)) return MOE_EINVAL;
+    if (T == 0) return MOE_OK;
+    if (!logits || !topk_idx || !gates) return MOE_EINVAL;
+    if (moe_host::misaligned(logits) || moe_host::misaligned(topk_idx) || moe_host::misaligned(gates))
+        return MOE_EALIGN;
+    hipStream_t s = (hipStream_t)stream;
+    dim3 grid((T + 3) / 4), block(256);
+    int epl = (E + 63) / 64;
+    switch (epl) {
+        case 1: route_kernel<1><<<grid, block, 0, s>>>(logits, T, E, K, topk_idx, gates); break;
+        case 2: route_kernel<2><<<grid, block, 0, s>>>(logits, T, E, K, topk_idx, gates); break;
+        case 3: route_kernel<3><<<grid, block, 0, s>>>(logits, T, E, K, topk_idx, gates); break;
+        case 4: route_kernel<4><<<grid, block, 0, s>>>(logits, T, E, K, topk_idx, gates); break;
+        case 5: route_kernel<5><<<grid, block, 0, s>>>(logits, T, E, K, topk_idx, gates); break;
+        case 6: route_kernel<6><<<grid, block, 0, s>>>(logits, T, E, K, topk_idx, gates); break;
+        case 7: route_kernel<7><<<grid, block, 0, s>>>(logits, T, E, K, topk_idx, gates); break;
+        default: route_kernel<8><<<grid, block, 0, s>>>(logits, T, E, K, topk_idx, gates); break;
+    }
+    return moe_host::launch_status();
+}
+
+extern "C" const char* moe_strerror(int status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_EINVAL: return "invalid argument (NULL pointer or size out of range)";
+        case MOE_ESHAPE: return "unsupported shape (H/F not a multiple of 64, K > E, ...)";
+        case MOE_EALIGN: return "pointer not 16-byte aligned";
+        case MOE_EWORKSPACE: return "workspace missing or too small";
+        case MOE_EHIP: return "HIP launch error";
+        default: return "unknown status";
+    }
+}
+
+extern "C" int moe_abi_version(void) { return 1; }
+
+namespace moe_host {
+int num_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+}  // namespace moe_host

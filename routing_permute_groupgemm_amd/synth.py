@@ -66,8 +66,15 @@ class MoeShape:
 
     @property
     def cap(self) -> int:
-        """Row capacity of the permuted buffers: T*K can never overflow."""
-        return self.T * self.K
+        """Row capacity of the permuted buffers.
+
+        All experts local: T*K (never overflows).  A local share of the
+        experts: twice the expected routed rows T*K*E_L/E (overflow is
+        detectable through the permutation's status word).
+        """
+        if self.EL == self.E:
+            return self.T * self.K
+        return min(self.T * self.K, 2 * ((self.T * self.K * self.EL + self.E - 1) // self.E))
 
     def scaled(self, **kw) -> "MoeShape":
         return dataclasses.replace(self, **kw)

@@ -1,0 +1,116 @@
+"""The C-ABI library loads, exports every symbol include/moe.h declares, and
+rejects bad arguments on the host before touching the GPU (CPU only)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from routing_permute_groupgemm_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_symbols()
+    for need in ("moe_route", "moe_permute", "moe_grouped_gemm_swiglu", "moe_grouped_gemm", "moe_combine",
+                 "moe_wgrad", "moe_gather"):
+        assert need in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    nm = subprocess.run(["nm", "-D", "--defined-only", _lib._LIB_PATH], capture_output=True, text=True,
+                        check=True).stdout
+    exported = set(re.findall(r"\s[TW]\s+(moe_\w+)", nm))
+    for name in declared_symbols():
+        assert name in exported, f"{name} declared in moe.h but not exported"
+        assert hasattr(lib, name)
+    assert set(_lib.SIGNATURES) == set(declared_symbols())
+
+
+def test_no_torch_types_in_header():
+    text = open(HEADER).read()
+    assert "torch" not in text.lower().replace("pytorch", "")
+    assert "extern \"C\"" in text
+
+
+def test_strerror_and_version():
+    lib = _lib.load()
+    assert lib.moe_abi_version() == 1
+    for code in (0, -1, -2, -3, -4, -5):
+        assert lib.moe_strerror(code)
+    assert lib.moe_strerror(-99) == b"unknown status"
+
+
+def test_workspace_size_host_only():
+    lib = _lib.load()
+    assert lib.moe_permute_workspace_size(131072, 8, 32) >= 512 * 32 * 4
+    assert lib.moe_permute_workspace_size(0, 8, 32) > 0
+
+
+# Invalid arguments are rejected before anything is enqueued (no GPU needed).
+FAKE = 0x10000  # aligned, never dereferenced: validation fails first
+MIS = 0x10002   # misaligned
+
+
+@pytest.mark.parametrize("args,want", [
+    ((FAKE, 16, 8, 9, FAKE, FAKE, None), -2),       # K > E
+    ((FAKE, 16, 8, 0, FAKE, FAKE, None), -1),       # K < 1
+    ((FAKE, 16, 8, 17, FAKE, FAKE, None), -1),      # K > 16
+    ((FAKE, 16, 600, 8, FAKE, FAKE, None), -1),     # E > 512
+    ((None, 16, 8, 2, FAKE, FAKE, None), -1),       # NULL logits
+    ((MIS, 16, 8, 2, FAKE, FAKE, None), -3),        # misaligned
+    ((FAKE, -1, 8, 2, FAKE, FAKE, None), -1),       # negative T
+])
+def test_route_rejects(args, want):
+    assert _lib.load().moe_route(*args) == want
+
+
+def test_route_zero_tokens_is_noop():
+    assert _lib.load().moe_route(None, 0, 8, 2, None, None, None) == 0
+
+
+def test_permute_rejects():
+    lib = _lib.load()
+    ok = dict(idx=FAKE, T=16, K=2, eb=0, el=8, x=FAKE, H=64, cap=32, counts=FAKE, offsets=FAKE, pos=FAKE,
+              src=FAKE, xp=FAKE, st=FAKE, ws=FAKE, wsb=1 << 20)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return lib.moe_permute(a["idx"], a["T"], a["K"], a["eb"], a["el"], a["x"], a["H"], a["cap"], a["counts"],
+                               a["offsets"], a["pos"], a["src"], a["xp"], a["st"], a["ws"], a["wsb"], None)
+
+    assert call(H=96) == -2            # H not a multiple of 64
+    assert call(wsb=4) == -4           # workspace too small
+    assert call(ws=None) == -4
+    assert call(x=MIS) == -3
+    assert call(cap=33) == -1          # cap > T*K
+    assert call(el=513) == -1
+    assert call(offsets=None) == -1
+
+
+def test_gemm_rejects():
+    lib = _lib.load()
+    # H not multiple of 64
+    assert lib.moe_grouped_gemm_swiglu(FAKE, FAKE, FAKE, FAKE, 4, 96, 64, 16, FAKE, None, None) == -2
+    assert lib.moe_grouped_gemm_swiglu(FAKE, FAKE, FAKE, None, 4, 64, 64, 16, FAKE, None, None) == -1
+    assert lib.moe_grouped_gemm_swiglu(FAKE, MIS, FAKE, FAKE, 4, 64, 64, 16, FAKE, None, None) == -3
+    # w1 only with trans_w = 1; lda too small; bad epilogue; SWIGLU_BWD needs ab
+    assert lib.moe_grouped_gemm(FAKE, 64, FAKE, FAKE, 0, FAKE, 4, 64, 64, 16, 0, None, FAKE, 64, None) == -1
+    assert lib.moe_grouped_gemm(FAKE, 64, FAKE, FAKE, 1, FAKE, 4, 64, 64, 16, 0, None, FAKE, 64, None) == -1
+    assert lib.moe_grouped_gemm(FAKE, 64, FAKE, None, 0, FAKE, 4, 64, 64, 16, 7, None, FAKE, 64, None) == -1
+    assert lib.moe_grouped_gemm(FAKE, 64, FAKE, None, 1, FAKE, 4, 64, 64, 16, 1, None, FAKE, 128, None) == -1
+    assert lib.moe_wgrad(FAKE, 64, FAKE, 64, FAKE, 4, 96, 64, 16, FAKE, None) == -2
+    assert lib.moe_wgrad(FAKE, 32, FAKE, 64, FAKE, 4, 64, 64, 16, FAKE, None) == -1
+    assert lib.moe_combine(FAKE, FAKE, None, 8, 2, 100, FAKE, None) == -2
+    assert lib.moe_combine(FAKE, None, None, 8, 2, 64, FAKE, None) == -1
+    assert lib.moe_gather(FAKE, FAKE, None, 8, 0, 64, FAKE, None) == -1

@@ -1,0 +1,213 @@
+"""Parity at the full workload sizes, in the launch configuration the
+benchmark times (same pipeline calls, same capacity).
+
+Index outputs are compared in full against the oracle; the row copy by a
+property (x_perm[r] == x[src[r] // K] for every row); the floating-point
+steps on sampled rows/tokens/columns that the oracle computes one by one.
+Per-step inputs downstream of the permutation are seeded synthetic operands
+of the real shapes fed identically to both sides, so no oracle input comes
+from the GPU."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import assert_close, assert_equal
+from routing_permute_groupgemm_amd import _lib, pipeline, synth
+
+pytestmark = pytest.mark.gpu
+
+
+def bits(t):
+    return pipeline.to_numpy_bits(t)
+
+
+class Case:
+    pass
+
+
+@pytest.fixture(scope="module", params=list(synth.WORKLOADS))
+def case(request):
+    name = request.param
+    shape = synth.WORKLOADS[name]
+    print(f"\n[fullsize] {name}: generating inputs", flush=True)
+    c = Case()
+    c.shape = shape
+    c.inp = synth.make_inputs(shape, seed=0, d_out=shape.backward)
+    c.dev = pipeline.to_device(c.inp)
+    c.buf = pipeline.MoeBuffers.allocate(shape, backward=shape.backward)
+    print(f"[fullsize] {name}: running GPU forward{'+backward' if shape.backward else ''}", flush=True)
+    pipeline.forward(c.buf, c.dev)
+    if shape.backward:
+        pipeline.backward(c.buf, c.dev)
+    torch.cuda.synchronize()
+    c.ref_idx, c.ref_g = oracle.route(c.inp["logits"], shape.K)
+    c.ref_pm = oracle.permute(c.ref_idx, shape.e_begin, shape.EL, c.inp["x"], shape.cap)
+    c.R = min(int(c.ref_pm["offsets"][-1]), shape.cap)
+    c.rng = np.random.default_rng(7)
+    yield c
+    del c.buf, c.dev
+    torch.cuda.empty_cache()
+
+
+def sample_rows(c, n_random=24):
+    off = c.ref_pm["offsets"]
+    counts = np.diff(off)
+    nz = np.nonzero(counts)[0]
+    pick = {nz[0], nz[-1], nz[np.argmax(counts[nz])], nz[np.argmin(counts[nz])]}
+    rows = set()
+    for j in pick:
+        lo, hi = int(off[j]), int(min(off[j + 1], c.shape.cap))
+        if lo < hi:
+            rows |= {lo, hi - 1, (lo + hi) // 2}
+    rows |= set(c.rng.integers(0, c.R, n_random).tolist())
+    return np.array(sorted(r for r in rows if r < c.R), np.int64)
+
+
+def test_route_full(case):
+    assert_equal("topk_idx", bits(case.buf.topk_idx), case.ref_idx)
+    assert_close("gates", bits(case.buf.gates), case.ref_g)
+
+
+def test_permute_full(case):
+    c, pm = case, case.ref_pm
+    assert_equal("counts", bits(c.buf.counts)[:c.shape.EL], pm["counts"])
+    assert_equal("offsets", bits(c.buf.offsets), pm["offsets"])
+    assert_equal("pos", bits(c.buf.pos), pm["pos"])
+    assert_equal("src", bits(c.buf.src)[:c.R], pm["src"][:c.R])
+    assert int(bits(c.buf.status)[0]) == pm["status"] == 0
+    # the row copy, checked for every row on the device
+    src = c.buf.src[:c.R].long()
+    assert torch.equal(c.buf.x_perm[:c.R].view(torch.int16), c.dev["x"][src // c.shape.K].view(torch.int16))
+    counts = pm["counts"]
+    print(f"[fullsize] {c.shape.name}: R={c.R} rows/expert {counts.min()}..{counts.max()} "
+          f"maxvio={synth.maxvio(counts, c.shape.T, c.shape.K, c.shape.E):.2f}", flush=True)
+
+
+def test_expert_up_sampled_rows(case):
+    c = case
+    rows = sample_rows(c)
+    h, ab = oracle.expert_up(c.ref_pm["x_perm"], c.inp["w_gate"], c.inp["w_up"], c.ref_pm["offsets"],
+                             c.shape.cap, rows=rows, want_ab=True)
+    assert_close("h", bits(c.buf.h)[rows], h[rows])
+    if c.buf.ab is not None:
+        assert_close("ab_save", bits(c.buf.ab)[rows], ab[rows])
+
+
+def test_expert_down_sampled_rows(case):
+    c = case
+    s = c.shape
+    hin = synth.operand_bf16((s.cap, s.F), seed=0, tag=1)
+    dh = pipeline.to_device(dict(h=hin))["h"]
+    y = torch.empty((s.cap, s.H), dtype=torch.bfloat16, device="cuda")
+    _lib.moe_grouped_gemm(dh, c.dev["w_down"], None, 0, c.buf.offsets, s.F, s.H, s.cap, y)
+    torch.cuda.synchronize()
+    rows = sample_rows(c)
+    ref = oracle.expert_down(hin, c.inp["w_down"], c.ref_pm["offsets"], s.cap, rows=rows)
+    assert_close("y", bits(y)[rows], ref[rows])
+
+
+def test_combine_sampled_tokens(case):
+    c = case
+    s = c.shape
+    yin = synth.operand_bf16((s.cap, s.H), seed=0, tag=2)
+    yd = pipeline.to_device(dict(y=yin))["y"]
+    out = _lib.moe_combine(yd, c.buf.pos, c.buf.gates)
+    out1 = _lib.moe_combine(yd, c.buf.pos, None)
+    torch.cuda.synchronize()
+    toks = np.unique(np.concatenate([[0, s.T - 1], c.rng.integers(0, s.T, 48),
+                                     np.nonzero(np.all(c.ref_pm["pos"] < 0, axis=1))[0][:4]])).astype(np.int64)
+    # gates: the oracle's own (bit-exact indices; gate values are the oracle's)
+    ref = oracle.combine(yin, c.ref_pm["pos"], c.ref_g, tokens=toks)
+    ref1 = oracle.combine(yin, c.ref_pm["pos"], None, tokens=toks)
+    assert_close("out", bits(out)[toks], ref[toks])
+    assert_close("out_ungated", bits(out1)[toks], ref1[toks])
+
+
+def _bwd_only(c):
+    if not c.shape.backward:
+        pytest.skip("forward-only workload")
+
+
+def test_gather_sampled_rows(case):
+    c = case
+    _bwd_only(c)
+    s = c.shape
+    rows = sample_rows(c)
+    ref = oracle.bwd_gather(c.inp["d_out"], c.ref_pm["src"], c.ref_pm["offsets"], c.ref_g, s.K, s.cap)
+    assert_close("dy_perm", bits(c.buf.dy_perm)[rows], ref[rows])
+
+
+def test_dgrad_down_swiglu_sampled_rows(case):
+    c = case
+    _bwd_only(c)
+    s = c.shape
+    dy = synth.operand_bf16((s.cap, s.H), seed=0, tag=3, std=0.125)
+    ab = synth.operand_bf16((s.cap, 2 * s.F), seed=0, tag=4)
+    d = pipeline.to_device(dict(dy=dy, ab=ab))
+    dab = torch.empty((s.cap, 2 * s.F), dtype=torch.bfloat16, device="cuda")
+    _lib.moe_grouped_gemm(d["dy"], c.dev["w_down"], None, 1, c.buf.offsets, s.H, s.F, s.cap, dab,
+                          epilogue=_lib.MOE_EPI_SWIGLU_BWD, ab=d["ab"])
+    torch.cuda.synchronize()
+    rows = sample_rows(c)
+    ref = oracle.bwd_down(dy, c.inp["w_down"], ab, c.ref_pm["offsets"], s.cap, rows=rows)
+    assert_close("dab", bits(dab)[rows], ref[rows])
+
+
+def test_dgrad_up_sampled_rows(case):
+    c = case
+    _bwd_only(c)
+    s = c.shape
+    dabin = synth.operand_bf16((s.cap, 2 * s.F), seed=0, tag=5, std=0.1)
+    d = pipeline.to_device(dict(dab=dabin))
+    dx = torch.empty((s.cap, s.H), dtype=torch.bfloat16, device="cuda")
+    _lib.moe_grouped_gemm(d["dab"], c.dev["w_gate"], c.dev["w_up"], 1, c.buf.offsets, s.F, s.H, s.cap, dx)
+    torch.cuda.synchronize()
+    rows = sample_rows(c)
+    ref = oracle.bwd_up(dabin, c.inp["w_gate"], c.inp["w_up"], c.ref_pm["offsets"], s.cap, rows=rows)
+    assert_close("dx_perm", bits(dx)[rows], ref[rows])
+
+
+@pytest.mark.parametrize("which", ["gate", "down"])
+def test_wgrad_sampled(case, which):
+    c = case
+    _bwd_only(c)
+    s = c.shape
+    if which == "gate":
+        M, N, lda, ldb = s.H, s.F, s.H, 2 * s.F
+        A = synth.operand_bf16((s.cap, s.H), seed=0, tag=6)
+        B = synth.operand_bf16((s.cap, 2 * s.F), seed=0, tag=7, std=0.1)
+    else:
+        M, N, lda, ldb = s.F, s.H, s.F, s.H
+        A = synth.operand_bf16((s.cap, s.F), seed=0, tag=8)
+        B = synth.operand_bf16((s.cap, s.H), seed=0, tag=9, std=0.1)
+    d = pipeline.to_device(dict(A=A, B=B))
+    dw = _lib.moe_wgrad(d["A"], lda, d["B"], ldb, c.buf.offsets, s.EL, M, N, s.cap)
+    dw2 = _lib.moe_wgrad(d["A"], lda, d["B"], ldb, c.buf.offsets, s.EL, M, N, s.cap)
+    torch.cuda.synchronize()
+    assert torch.equal(dw.view(torch.int32), dw2.view(torch.int32)), "wgrad rerun differs"
+    counts = c.ref_pm["counts"]
+    groups = np.unique([int(np.argmax(counts)), int(np.argmin(counts)), 0]).astype(np.int32)
+    cols = np.unique(np.concatenate([[0, N - 1], c.rng.integers(0, N, 10)])).astype(np.int32)
+    ref = np.zeros((s.EL, M, N), np.float32)
+    oracle.wgrad(A, lda, B, ldb, c.ref_pm["offsets"], M, N, s.cap, groups=groups, cols=cols, out=ref)
+    got = dw.cpu().numpy()
+    for j in groups:
+        assert_close(f"dw[{j}]", got[j][:, cols], ref[j][:, cols])
+
+
+def test_full_layer_rerun_bitwise(case):
+    c = case
+    s = c.shape
+    b2 = pipeline.MoeBuffers.allocate(s, backward=s.backward)
+    pipeline.forward(b2, c.dev)
+    if s.backward:
+        pipeline.backward(b2, c.dev)
+    torch.cuda.synchronize()
+    fields = ["topk_idx", "gates", "pos", "out"] + (["dx", "dw_gate", "dw_up", "dw_down"] if s.backward else [])
+    for f in fields:
+        assert torch.equal(getattr(c.buf, f).view(torch.uint8), getattr(b2, f).view(torch.uint8)), f
+    R = c.R
+    for f in ["src", "x_perm", "h", "y"] + (["ab", "dy_perm", "dab", "dx_perm"] if s.backward else []):
+        assert torch.equal(getattr(c.buf, f)[:R].view(torch.uint8), getattr(b2, f)[:R].view(torch.uint8)), f
+    del b2

@@ -1,0 +1,170 @@
+"""GPU parity of the whole layer (forward + backward) against the CPU oracle
+at sizes the oracle finishes in seconds, plus edge cases and determinism.
+
+Integer outputs (top-k indices, counts, offsets, pos, src) and the row copy
+x_perm must be bit-exact; floating outputs must satisfy
+|gpu - oracle| <= 1e-2 + 1e-2*|oracle| elementwise; GPU reruns must be
+bitwise identical.  Every call goes through the C ABI (libmoe.so)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import assert_close, assert_equal
+from routing_permute_groupgemm_amd import _lib, pipeline, synth
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS
+# Scaled-down copies of every workload: same E, K, routing recipe; several
+# row tiles per expert, ragged tails, N not always a multiple of 128.
+SMALL = {
+    "tiny": W["tiny"].scaled(backward=True),
+    "ep_share_small": W["ep_share_4k"].scaled(T=512, H=256, F=192, backward=True),
+    "skew_small": W["skew_8k"].scaled(T=1024, H=256, F=128, backward=True),
+    "fwdbwd_small": W["fwdbwd_16k"].scaled(T=1024, H=192, F=128),
+    "long_small": W["ep_share_128k"].scaled(T=2048, H=128, F=64),
+}
+
+
+def bits(t):
+    return pipeline.to_numpy_bits(t)
+
+
+def run_gpu(shape, inp, cap=None):
+    dev = pipeline.to_device(inp)
+    buf = pipeline.MoeBuffers.allocate(shape, cap=cap, backward=True)
+    pipeline.forward(buf, dev)
+    pipeline.backward(buf, dev)
+    torch.cuda.synchronize()
+    return buf, dev
+
+
+def check_layer(shape, inp, buf, cap):
+    print(f"[parity] {shape.name} T={shape.T} H={shape.H} F={shape.F} E={shape.E} K={shape.K} "
+          f"EL={shape.EL} cap={cap}", flush=True)
+    ref = oracle.forward(inp, shape.e_begin, shape.EL, shape.K, cap)
+    refb = oracle.backward(inp, ref, cap)
+    R = min(int(ref["offsets"][-1]), cap)
+    assert_equal("topk_idx", bits(buf.topk_idx), ref["topk_idx"])
+    assert_close("gates", bits(buf.gates), ref["gates"])
+    assert_equal("counts", bits(buf.counts)[:shape.EL], ref["counts"])
+    assert_equal("offsets", bits(buf.offsets), ref["offsets"])
+    assert_equal("pos", bits(buf.pos), ref["pos"])
+    assert_equal("status", bits(buf.status)[0], ref["status"])
+    assert_equal("src", bits(buf.src)[:R], ref["src"][:R])
+    assert_equal("x_perm", bits(buf.x_perm)[:R], ref["x_perm"][:R])
+    assert_close("h", bits(buf.h)[:R], ref["h"][:R])
+    assert_close("ab_save", bits(buf.ab)[:R], ref["ab"][:R])
+    assert_close("y", bits(buf.y)[:R], ref["y"][:R])
+    assert_close("out", bits(buf.out), ref["out"])
+    assert_close("dy_perm", bits(buf.dy_perm)[:R], refb["dy_perm"][:R])
+    assert_close("dab", bits(buf.dab)[:R], refb["dab"][:R])
+    assert_close("dx_perm", bits(buf.dx_perm)[:R], refb["dx_perm"][:R])
+    assert_close("dx", bits(buf.dx), refb["dx"])
+    assert_close("dw_gate", bits(buf.dw_gate), refb["dw_gate"])
+    assert_close("dw_up", bits(buf.dw_up), refb["dw_up"])
+    assert_close("dw_down", bits(buf.dw_down), refb["dw_down"])
+    return ref
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_layer_forward_backward_matches_oracle(name):
+    shape = SMALL[name]
+    inp = synth.make_inputs(shape, seed=0, d_out=True)
+    buf, _ = run_gpu(shape, inp)
+    check_layer(shape, inp, buf, shape.cap)
+
+
+@pytest.mark.parametrize("name", ["tiny", "skew_small"])
+def test_layer_reruns_are_bitwise_identical(name):
+    shape = SMALL[name]
+    inp = synth.make_inputs(shape, seed=1, d_out=True)
+    b1, dev = run_gpu(shape, inp)
+    for _ in range(2):
+        b2 = pipeline.MoeBuffers.allocate(shape, backward=True)
+        pipeline.forward(b2, dev)
+        pipeline.backward(b2, dev)
+        torch.cuda.synchronize()
+        R = int(bits(b1.offsets)[-1])
+        for f in ("topk_idx", "gates", "pos", "out", "dx", "dw_gate", "dw_up", "dw_down"):
+            assert torch.equal(getattr(b1, f).view(torch.uint8), getattr(b2, f).view(torch.uint8)), f
+        for f in ("src", "x_perm", "h", "ab", "y", "dy_perm", "dab", "dx_perm"):
+            a, b = getattr(b1, f)[:R], getattr(b2, f)[:R]
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f
+
+
+def _inputs_with_logits(shape, logits, seed=3):
+    inp = synth.make_inputs(shape, seed=seed, d_out=True)
+    inp["logits"] = logits.astype(np.float32)
+    return inp
+
+
+def test_all_tokens_to_one_expert_and_empty_experts():
+    shape = synth.MoeShape("one_hot", 90, T=300, H=128, F=128, E=8, K=2, backward=True)
+    rng = np.random.default_rng(0)
+    logits = rng.standard_normal((shape.T, shape.E)).astype(np.float32)
+    logits[:, 5] += 100.0   # expert 5 is everyone's first choice
+    logits[:, 2] += 50.0    # expert 2 everyone's second; six experts stay empty
+    inp = _inputs_with_logits(shape, logits)
+    buf, _ = run_gpu(shape, inp)
+    ref = check_layer(shape, inp, buf, shape.cap)
+    assert sorted(ref["counts"].tolist()) == [0] * 6 + [300, 300]
+
+
+def test_local_share_single_expert_and_nonlocal_tokens():
+    shape = synth.MoeShape("single_local", 91, T=200, H=64, F=64, E=8, K=2, e_begin=3, e_local=1,
+                           backward=True)
+    inp = synth.make_inputs(shape, seed=0, d_out=True)
+    buf, _ = run_gpu(shape, inp)
+    ref = check_layer(shape, inp, buf, shape.cap)
+    assert np.any(np.all(ref["pos"] < 0, axis=1))  # some tokens have no local pair -> zero rows
+
+
+@pytest.mark.parametrize("T,K,E", [(1, 2, 8), (7, 3, 8), (65, 1, 16), (40, 8, 8), (33, 16, 64)])
+def test_small_token_counts_and_k_extremes(T, K, E):
+    shape = synth.MoeShape(f"edge_T{T}_K{K}", 92, T=T, H=128, F=64, E=E, K=K, backward=True)
+    inp = synth.make_inputs(shape, seed=T, d_out=True)
+    buf, _ = run_gpu(shape, inp)
+    check_layer(shape, inp, buf, shape.cap)
+
+
+def test_capacity_overflow_drops_tail_rows_and_sets_status():
+    shape = synth.MoeShape("overflow", 93, T=256, H=128, F=128, E=8, K=2, backward=True)
+    inp = synth.make_inputs(shape, seed=0, d_out=True)
+    cap = 300  # R = 512 > cap
+    buf, _ = run_gpu(shape, inp, cap=cap)
+    ref = check_layer(shape, inp, buf, cap)
+    assert ref["status"] == 1 and int(bits(buf.status)[0]) == 1
+
+
+def test_zero_tokens():
+    offsets = torch.full((9,), -7, dtype=torch.int32, device="cuda")
+    counts = torch.full((8,), -7, dtype=torch.int32, device="cuda")
+    status = torch.full((4,), -7, dtype=torch.int32, device="cuda")
+    idx = torch.empty((0, 2), dtype=torch.int32, device="cuda")
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    _lib.moe_permute(idx, 0, 8, x, 0, out=dict(offsets=offsets, counts=counts, status=status))
+    torch.cuda.synchronize()
+    assert offsets.tolist() == [0] * 9 and counts.tolist() == [0] * 8 and status[0].item() == 0
+
+
+def test_wgrad_empty_expert_writes_zeros_and_grid_independence():
+    """An expert with no rows gets exact zeros; a rerun (the persistent grid
+    visits tiles in a different interleaving across workgroups) is identical."""
+    rng = np.random.default_rng(5)
+    counts = np.array([0, 130, 1, 64, 0, 257], np.int32)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R = int(offsets[-1])
+    M, N = 192, 128
+    a = synth.f32_to_bf16_bits(rng.standard_normal((R, M)).astype(np.float32))
+    b = synth.f32_to_bf16_bits(rng.standard_normal((R, N)).astype(np.float32))
+    dev = pipeline.to_device(dict(a=a, b=b, offsets=offsets))
+    dw = torch.full((len(counts), M, N), float("nan"), dtype=torch.float32, device="cuda")
+    _lib.moe_wgrad(dev["a"], M, dev["b"], N, dev["offsets"], len(counts), M, N, R, dw=dw)
+    dw2 = _lib.moe_wgrad(dev["a"], M, dev["b"], N, dev["offsets"], len(counts), M, N, R)
+    torch.cuda.synchronize()
+    ref = oracle.wgrad(a, M, b, N, offsets, M, N, R)
+    assert_close("dw", dw.cpu().numpy(), ref)
+    assert torch.equal(dw.view(torch.int32), dw2.view(torch.int32))
+    assert np.all(dw[0].cpu().numpy() == 0) and np.all(dw[4].cpu().numpy() == 0)
