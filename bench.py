@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""Throughput of the one-GPU MoE layer hot path on MI355X.
+
+One step = one pass of the whole path over one batch of seeded synthetic
+input already resident in HBM: route -> permute -> gate/up GroupGEMM with
+SwiGLU -> down GroupGEMM -> combine, plus (workloads with a backward) the
+gate-scaled gather, both dgrad GroupGEMMs, the combine-gradient and the three
+weight-gradient GroupGEMMs.  Every step is a libmoe C-ABI call on one stream.
+
+Prints one JSON line: tokens/s, plus the roofline of the dominant kernel
+(achieved algorithmic bytes or flops per launch / its mean launch time, from
+HIP events recorded on the launch stream over the timed steps) and the CPU
+oracle's throughput on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+GEMM_SRC = os.path.join(ROOT, "routing_permute_groupgemm_amd", "csrc", "gemm.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="ep_share_4k")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU-oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration under rocprofv3)")
+    return ap.parse_args()
+
+
+def algorithmic_work(shape, R, T_act, n_active):
+    """Per-launch algorithmic bytes and flops of every step (real rows only, no padding)."""
+    T, H, F, E, K, EL = shape.T, shape.H, shape.F, shape.E, shape.K, shape.EL
+    w = {}
+    w["route"] = dict(bytes=4 * T * E + 8 * T * K, flops=0)
+    w["permute"] = dict(bytes=4 * T * K * 3 + 4 * R + 2 * H * T_act + 2 * H * R + 8 * EL, flops=0)
+    ab = 2 * R * 2 * F if shape.backward else 0
+    w["expert_up"] = dict(bytes=2 * n_active * H * 2 * F + 2 * R * H + 2 * R * F + ab, flops=4 * R * H * F)
+    w["expert_down"] = dict(bytes=2 * n_active * F * H + 2 * R * F + 2 * R * H, flops=2 * R * F * H)
+    w["combine"] = dict(bytes=2 * H * R + 8 * T * K + 2 * H * T, flops=0)
+    if shape.backward:
+        w["bwd_gather"] = dict(bytes=2 * H * T_act + 2 * H * R + 8 * T * K, flops=0)
+        w["bwd_down_dgrad"] = dict(bytes=2 * n_active * F * H + 2 * R * H + 4 * R * 2 * F,
+                                   flops=2 * R * H * F)
+        w["bwd_up_dgrad"] = dict(bytes=2 * n_active * 2 * H * F + 2 * R * 2 * F + 2 * R * H,
+                                 flops=2 * R * 2 * F * H)
+        w["bwd_combine"] = dict(bytes=2 * H * R + 4 * T * K + 2 * H * T, flops=0)
+        for name, (m, n) in (("wgrad_gate", (H, F)), ("wgrad_up", (H, F)), ("wgrad_down", (F, H))):
+            w[name] = dict(bytes=2 * R * m + 2 * R * n + 4 * EL * m * n, flops=2 * R * m * n)
+    return w
+
+
+def roofline(work, ms):
+    b, f = work["bytes"], work["flops"]
+    t_hbm = b / (HBM_PEAK_GBS * 1e9)
+    t_mfma = f / (MFMA_BF16_PEAK_TFS * 1e12)
+    if f and t_mfma >= t_hbm:
+        ach = f / (ms * 1e-3) / 1e12
+        return dict(bound="mfma", achieved=round(ach, 2), peak=MFMA_BF16_PEAK_TFS, unit="TFLOP/s",
+                    frac=round(ach / MFMA_BF16_PEAK_TFS, 4))
+    ach = b / (ms * 1e-3) / 1e9
+    return dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=round(ach / HBM_PEAK_GBS, 4))
+
+
+def src_hash():
+    with open(GEMM_SRC, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if the kernel is unchanged since."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            db = json.load(fh)
+        rec = db[f"{kernel}@{workload}"]
+        if rec.get("gemm_src_sha") != src_hash():
+            return None
+        return int(rec["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(shape, inp, budget_s):
+    """The oracle as it stands on contiguous token chunks of the same workload until the budget is spent."""
+    import oracle
+    T, K, EL = shape.T, shape.K, shape.EL
+    chunk = max(16, min(T, 256))
+    t0 = time.perf_counter()
+    done = 0
+    while done < T:
+        lo, hi = done, min(T, done + chunk)
+        sub = {k: inp[k][lo:hi] for k in ("logits", "x")}
+        sub.update({k: inp[k] for k in ("w_gate", "w_up", "w_down")})
+        cap = (hi - lo) * K
+        fwd = oracle.forward(sub, shape.e_begin, EL, K, cap)
+        if shape.backward:
+            sub["d_out"] = inp["d_out"][lo:hi]
+            oracle.backward(sub, fwd, cap)
+        done = hi
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return dict(value=round(done / dt, 2), unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
+                sample=f"first {done} of {T} tokens in chunks of {chunk} "
+                       f"({'forward+backward' if shape.backward else 'forward'}), {dt:.1f} s")
+
+
+def calib_copy():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calib_copy_bytes_read": n, "calib_copy_bytes_written": n, "launches": 5}))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
+              "(expert-parallel sharding across GPUs is not built)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    if args.calib_copy:
+        calib_copy()
+        return
+    from routing_permute_groupgemm_amd import _lib, pipeline, synth
+
+    _lib.load()
+    shape = synth.WORKLOADS[args.workload]
+    print(f"[bench] {shape.name}: generating inputs", file=sys.stderr, flush=True)
+    inp = synth.make_inputs(shape, seed=args.seed)
+    dev = pipeline.to_device(inp)
+    buf = pipeline.MoeBuffers.allocate(shape)
+    stream = torch.cuda.current_stream()
+
+    steps = [("route", lambda: pipeline.route(buf, dev["logits"])),
+             ("permute", lambda: pipeline.permute(buf, dev["x"])),
+             ("expert_up", lambda: pipeline.expert_up(buf, dev["w_gate"], dev["w_up"])),
+             ("expert_down", lambda: pipeline.expert_down(buf, dev["w_down"])),
+             ("combine", lambda: pipeline.combine(buf))]
+    if shape.backward:
+        H, F, EL, cap = shape.H, shape.F, shape.EL, buf.cap
+        steps += [
+            ("bwd_gather", lambda: _lib.moe_gather(dev["d_out"], buf.pos, buf.gates, buf.dy_perm)),
+            ("bwd_down_dgrad", lambda: _lib.moe_grouped_gemm(buf.dy_perm, dev["w_down"], None, 1, buf.offsets, H,
+                                                             F, cap, buf.dab, epilogue=_lib.MOE_EPI_SWIGLU_BWD,
+                                                             ab=buf.ab)),
+            ("bwd_up_dgrad", lambda: _lib.moe_grouped_gemm(buf.dab, dev["w_gate"], dev["w_up"], 1, buf.offsets, F,
+                                                           H, cap, buf.dx_perm)),
+            ("bwd_combine", lambda: _lib.moe_combine(buf.dx_perm, buf.pos, None, out=buf.dx)),
+            ("wgrad_gate", lambda: _lib.moe_wgrad(buf.x_perm, H, buf.dab, 2 * F, buf.offsets, EL, H, F, cap,
+                                                  dw=buf.dw_gate)),
+            ("wgrad_up", lambda: _lib.moe_wgrad(buf.x_perm, H, buf.dab, 2 * F, buf.offsets, EL, H, F, cap,
+                                                dw=buf.dw_up, b_col0=F)),
+            ("wgrad_down", lambda: _lib.moe_wgrad(buf.h, F, buf.dy_perm, H, buf.offsets, EL, F, H, cap,
+                                                  dw=buf.dw_down)),
+        ]
+
+    def one_step(evs=None):
+        for i, (_, fn) in enumerate(steps):
+            if evs is not None:
+                evs[i].record(stream)
+            fn()
+        if evs is not None:
+            evs[len(steps)].record(stream)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(steps) + 1)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for k in range(args.steps):
+        one_step(evs[k])
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+    per = {name: float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)]))
+           for i, (name, _) in enumerate(steps)}
+    print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
+
+    status = int(buf.status[0].item())
+    offsets = buf.offsets.cpu().numpy()
+    counts = np.diff(offsets)
+    R = int(min(offsets[-1], buf.cap))
+    pos = buf.pos.cpu().numpy()
+    T_act = int(np.sum(np.any(pos >= 0, axis=1)))
+    n_active = int(np.sum(counts > 0))
+    work = algorithmic_work(shape, R, T_act, n_active)
+    dom = max(per, key=per.get)
+    rl = roofline(work[dom], per[dom])
+    rl["kernel"] = dom
+    rl["traffic"] = measured_traffic(dom, shape.name)
+    gemm_names = [n for n in per if work[n]["flops"]]
+    gemm_flops = sum(work[n]["flops"] for n in gemm_names)
+    gemm_ms = sum(per[n] for n in gemm_names)
+    result = {
+        "metric": "MoE layer tokens/s on 1 GPU; GroupGEMM % bf16 MFMA peak; permute GB/s",
+        "value": round(shape.T / (ms_per_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": shape.name, "T": shape.T, "H": shape.H, "F": shape.F, "E": shape.E, "K": shape.K,
+                   "e_local": shape.EL, "cap_rows": buf.cap, "pass": "fwd+bwd" if shape.backward else "fwd",
+                   "routed_rows": R, "maxvio": round(synth.maxvio(counts, shape.T, shape.K, shape.E), 3),
+                   "seed": args.seed, "parallelism": "single GPU"},
+        "roofline": rl,
+        "groupgemm_mfma_frac": round(gemm_flops / (gemm_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4),
+        "permute_gbps": round(work["permute"]["bytes"] / (per["permute"] * 1e-3) / 1e9, 1),
+        "step_ms": {k: round(v, 4) for k, v in per.items()},
+    }
+    if status != 0:
+        result["warning"] = "row capacity overflow: rows were dropped"
+    if not args.no_cpu_baseline:
+        print(f"[bench] cpu baseline (~{args.cpu_seconds:.0f} s)", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(shape, inp, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -46,6 +46,8 @@ def lib():
     if _lib is None:
         _lib = ctypes.CDLL(build())
         L = _lib
+        L.oracle_num_threads.argtypes = []
+        L.oracle_num_threads.restype = ctypes.c_int
         L.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
         L.oracle_f32_to_bf16.restype = ctypes.c_uint16
         L.oracle_route.argtypes = [_p, _i, _i, _i, _p, _p]
@@ -70,6 +72,10 @@ def _ptr(a):
 
 def _c(a, dtype):
     return np.ascontiguousarray(a, dtype=dtype)
+
+
+def num_threads() -> int:
+    return int(lib().oracle_num_threads())
 
 
 def f32_to_bf16(v: float) -> int:
