@@ -32,17 +32,17 @@
 // Workgroups are persistent, and block ids are remapped so each XCD (own L2)
 // walks a contiguous run of tiles; tiles are visited in groups of 4 row
 // blocks so neighbouring tiles share A rows and B columns.
+#include <stdlib.h>
+
 #include <algorithm>
 
 #include "moe_common.hpp"
 
 namespace moe {
 
-constexpr int kBM = 128, kBN = 128, kBK = 64;
 constexpr int kGroupM = 4;
 constexpr int kMaxGroups = 512;
-constexpr int kStageBytes = 32768;  // A 16 KiB + B 16 KiB
-constexpr int kLdsBytes = 2 * kStageBytes;
+constexpr int kLdsBudget = 128 * 1024;  // LDS per workgroup for the stage ring
 
 enum : int { LAY_KC = 0, LAY_MN = 1 };
 enum : int { EPI_BF16 = 0, EPI_SWIGLU = 1, EPI_SWIGLU_BWD = 2, EPI_F32 = 3 };
@@ -71,58 +71,137 @@ struct GemmParams {
     float* cf;            // WGRAD: fp32 out [e_local, M, N]
 };
 
-// 16-byte chunk swizzles of 128-byte LDS rows.
-// KC tiles are read 32 rows x 16 B at a time: chunk ^= (row/2)%8 spreads 16
-// consecutive rows over all banks.  MN tiles are read as 4-row x 32-byte
-// patches (transposing reads): chunk ^= 4*((row/2)%2) puts rows r and r+2 on
-// different banks.
-__device__ __forceinline__ int swz_kc(int row) { return (row >> 1) & 7; }
-__device__ __forceinline__ int swz_mn(int row) { return ((row >> 1) & 1) << 2; }
+typedef __attribute__((ext_vector_type(4))) int i32x4;
 
-__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t voff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (MOE_LDS void*)lds, 16, voff, 0, 0, 0);
+// Buffer resource (raw, stride 0): loads at or past `bytes` return zero.
+__device__ __forceinline__ i32x4 make_srd(const void* base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)base;
+    i32x4 r;
+    r[0] = (int)(uint32_t)a;
+    r[1] = (int)((a >> 32) & 0xffff);
+    r[2] = (int)bytes;
+    r[3] = 0x00020000;
+    return r;
 }
 
-// KC fragment: 32 rows starting at rb, k16-step kk; lane holds row rb+l%32, 8 k values.
-__device__ __forceinline__ bf16x8 frag_kc(const uint8_t* tile, int rb, int kk, int lane) {
-    int row = rb + (lane & 31);
-    int ch = (kk * 2 + (lane >> 5)) ^ swz_kc(row);
-    u32x4 v = *(const MOE_LDS u32x4*)(tile + row * 128 + (ch << 4));
-    return __builtin_bit_cast(bf16x8, v);
+// 16 bytes per lane from global memory straight into LDS at lds + 16*lane.
+// Written as inline asm so the compiler does not treat every later LDS read
+// as dependent on it (it would wait for all outstanding loads, serialising
+// the LDS stages); the kernel waits for it explicitly (vmcnt + barrier).
+__device__ __forceinline__ void lds_load16(i32x4 srd, uint32_t lds, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds), "v"(voff), "s"(srd)
+                 : "memory");
 }
 
-// MN fragment: 32 columns starting at cb (0..127) of a [64][128] tile stored as
-// two [64][64] sub-tiles; lane holds column cb+l%32 and 8 consecutive k.
-__device__ __forceinline__ bf16x8 frag_mn(const uint8_t* tile, int cb, int kk, int lane) {
-    const int g = lane >> 4, q = lane & 15;
-    const int krow = kk * 16 + 8 * (g >> 1) + (q >> 2);
-    const int col = (cb & 63) + 16 * (g & 1) + 4 * (q & 3);
-    const uint8_t* sub = tile + (cb >> 6) * 8192;
-    const int off = ((col >> 3) ^ swz_mn(krow)) * 16 + (col & 7) * 2;
-    s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS s16x4*)(sub + krow * 128 + off));
-    s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS s16x4*)(sub + (krow + 4) * 128 + off));
-    u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-    u32x4 v = {l2[0], l2[1], h2[0], h2[1]};
-    return __builtin_bit_cast(bf16x8, v);
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const MOE_LDS void*)p;
 }
 
-__device__ __forceinline__ float silu_f(float a) { return a / (1.0f + __expf(-a)); }
+// s_waitcnt vmcnt(n) for a compile-time n (lgkmcnt and expcnt left alone).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// ---- LDS tile layouts -------------------------------------------------------
+// KC ("contraction-contiguous"): the tile is [rows][BK] bf16, BK*2 bytes per row,
+// 16-byte chunks XOR-swizzled by row so that the 32 rows x 16 B a fragment read
+// touches spread over all banks.  MN: the tile is [BK][cols] stored as
+// [BK][64] sub-tiles with 128-byte rows, read by the transposing
+// ds_read_b64_tr_b16; a 4-row x 32-byte read patch is spread by a 4-chunk XOR.
+template <int BK>
+struct Lay {
+    static constexpr int kRowBytes = BK * 2;          // KC row
+    static constexpr int kChunks = BK / 8;            // 16-byte chunks per KC row
+    static constexpr int kRowsPerLoad = 1024 / kRowBytes;
+    static constexpr int kSubBytes = BK * 128;        // MN sub-tile [BK][64]
+    static constexpr int kLoadsPerSub = BK / 8;
+    __device__ static __forceinline__ int swz_kc(int row) {
+        return BK == 64 ? ((row >> 1) & 7) : ((row >> 2) & 3);
+    }
+    __device__ static __forceinline__ int swz_mn(int krow) { return ((krow >> 1) & 1) << 2; }
+
+    // lane holds row rb + l%32 and k values 16*kk + 8*(l/32) + 0..7
+    __device__ static __forceinline__ bf16x8 frag_kc(const uint8_t* tile, int rb, int kk, int lane) {
+        const int row = rb + (lane & 31);
+        const int ch = (kk * 2 + (lane >> 5)) ^ swz_kc(row);
+        u32x4 v = *(const MOE_LDS u32x4*)(tile + row * kRowBytes + (ch << 4));
+        return __builtin_bit_cast(bf16x8, v);
+    }
+    // lane holds column cb + l%32 and k values 16*kk + 8*(l/32) + 0..7
+    __device__ static __forceinline__ bf16x8 frag_mn(const uint8_t* tile, int cb, int kk, int lane) {
+        const int g = lane >> 4, q = lane & 15;
+        const int krow = kk * 16 + 8 * (g >> 1) + (q >> 2);
+        const int col = (cb & 63) + 16 * (g & 1) + 4 * (q & 3);
+        const uint8_t* sub = tile + (cb >> 6) * kSubBytes;
+        const int off = ((col >> 3) ^ swz_mn(krow)) * 16 + (col & 7) * 2;
+        s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS s16x4*)(sub + krow * 128 + off));
+        s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS s16x4*)(sub + (krow + 4) * 128 + off));
+        u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        u32x4 v = {l2[0], l2[1], h2[0], h2[1]};
+        return __builtin_bit_cast(bf16x8, v);
+    }
+    // per-lane byte offset of an LDS-direct load into a KC tile: load q fills
+    // rows q*kRowsPerLoad + l/kChunks; `v` is q's part of the swizzle period
+    __device__ static __forceinline__ uint32_t lane_kc(int lane, int v, int64_t ld) {
+        const int r = lane / kChunks, c = lane % kChunks;
+        return (uint32_t)((r * ld + (c ^ swz_kc(v * kRowsPerLoad + r)) * 8) * 2);
+    }
+    __device__ static __forceinline__ int kc_period(int q) { return BK == 64 ? (q & 1) : 0; }
+    // ... into an MN sub-tile (load q fills k-rows 8*(q%kLoadsPerSub) + l/8)
+    __device__ static __forceinline__ uint32_t lane_mn(int lane, int64_t ld) {
+        return (uint32_t)(((lane >> 3) * ld + ((lane & 7) ^ swz_mn(lane >> 3)) * 8) * 2);
+    }
+};
+
+__device__ __forceinline__ float sigmoid_f(float a) { return __builtin_amdgcn_rcpf(1.0f + __expf(-a)); }
+__device__ __forceinline__ float silu_f(float a) { return a * sigmoid_f(a); }
 
 __device__ __forceinline__ int xcd_remap(int b, int G) { return (b & 7) * (G >> 3) + (b >> 3); }
 
-template <int LB, int EPI, int SCHED>
-__global__ __launch_bounds__(256) void gg_kernel(GemmParams p) {
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes];
+// Block tile BM x BN (B columns; for SWIGLU the gate half then the up half),
+// contraction step BK, a ring of STAGES LDS stages, WM x WN waves each owning a
+// (BM/WM) x (BN/WN) tile of 32x32 MFMA tiles.
+template <int BM, int BN, int BK, int WM, int WN>
+struct Tile {
+    static constexpr int kWaves = WM * WN;
+    static constexpr int kThreads = 64 * kWaves;
+    static constexpr int kMTW = BM / WM / 32;
+    static constexpr int kNTW = BN / WN / 32;
+    static constexpr int kABytes = BM * BK * 2;
+    static constexpr int kStage = (BM + BN) * BK * 2;
+    static constexpr int kStages = kLdsBudget / kStage < 4 ? kLdsBudget / kStage : 4;
+    static constexpr int kLoads = kStage / 1024;  // 1 KiB LDS-direct loads per stage
+    static constexpr int kALoads = kABytes / 1024;
+    static constexpr int kLoadsPerWave = kLoads / kWaves;
+    static constexpr int kKK = BK / 16;           // MFMA k-steps per stage
+    static_assert(kStages >= 3, "the pipeline needs at least three stages");
+    static_assert(kLoads % kWaves == 0, "loads must split evenly over the waves");
+    static_assert(kALoads % kLoadsPerWave == 0, "a wave's loads must be all A or all B");
+    static_assert(kLoadsPerWave * (kStages - 1) < 64, "vmcnt range");
+};
+
+template <int BM, int BN, int BK, int WM, int WN, int LB, int EPI, int SCHED>
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(1, 2)))
+void gg_kernel(GemmParams p) {
+    using TL = Tile<BM, BN, BK, WM, WN>;
+    using LY = Lay<BK>;
+    constexpr int MTW = TL::kMTW, NTW = TL::kNTW, LPW = TL::kLoadsPerWave, S = TL::kStages, KK = TL::kKK;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[S * TL::kStage];
     __shared__ int s_off[kMaxGroups + 1];    // clamped row offsets
     __shared__ int s_start[kMaxGroups + 1];  // ROWS: first m-tile of each expert; WGRAD: sorted order
-    __shared__ int s_wave[4];
+    __shared__ int s_wave[16];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
+    const int wm = wave / WN, wn = wave % WN;
     const int EL = p.e_local;
 
     // ---- per-workgroup schedule setup (device-resident row counts) ----
-    for (int j = tid; j <= EL; j += 256) {
+    for (int j = tid; j <= EL; j += TL::kThreads) {
         int64_t o = p.offsets[j];
         s_off[j] = (int)(o < p.cap ? o : p.cap);
     }
@@ -131,12 +210,18 @@ __global__ __launch_bounds__(256) void gg_kernel(GemmParams p) {
     int tiles_n;  // tiles along N (ROWS) ; tiles per group (WGRAD)
     int tiles_mw = 0;
     if (SCHED == SCHED_ROWS) {
-        tiles_n = EPI == EPI_SWIGLU ? (p.N + 63) / 64 : (p.N + kBN - 1) / kBN;
-        // exclusive scan of per-expert m-tile counts, 2 experts per thread
-        int j0 = 2 * tid, c0 = 0, c1 = 0;
-        if (j0 < EL) c0 = (s_off[j0 + 1] - s_off[j0] + kBM - 1) / kBM;
-        if (j0 + 1 < EL) c1 = (s_off[j0 + 2] - s_off[j0 + 1] + kBM - 1) / kBM;
-        int v = c0 + c1;
+        tiles_n = EPI == EPI_SWIGLU ? (p.N + BN / 2 - 1) / (BN / 2) : (p.N + BN - 1) / BN;
+        // exclusive scan of per-expert m-tile counts; each thread owns a run of experts
+        constexpr int PER = (kMaxGroups + TL::kThreads - 1) / TL::kThreads;
+        const int j0 = tid * PER;
+        int cnt[PER], sum = 0;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            int j = j0 + i;
+            cnt[i] = j < EL ? (s_off[j + 1] - s_off[j] + BM - 1) / BM : 0;
+            sum += cnt[i];
+        }
+        int v = sum;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
             int t = __shfl_up(v, o, 64);
@@ -146,17 +231,20 @@ __global__ __launch_bounds__(256) void gg_kernel(GemmParams p) {
         __syncthreads();
         int add = 0;
         for (int w = 0; w < wave; ++w) add += s_wave[w];
-        int excl = add + v - (c0 + c1);
-        if (j0 < EL) s_start[j0] = excl;
-        if (j0 + 1 < EL) s_start[j0 + 1] = excl + c0;
-        if (tid == 255) s_start[EL] = add + v;
+        int run = add + v - sum;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            if (j0 + i < EL) s_start[j0 + i] = run;
+            run += cnt[i];
+        }
+        if (tid == TL::kThreads - 1) s_start[EL] = run;
         __syncthreads();
         n_tiles_total = s_start[EL] * tiles_n;
     } else {
-        tiles_mw = (p.M + kBM - 1) / kBM;
-        tiles_n = tiles_mw * ((p.N + kBN - 1) / kBN);
+        tiles_mw = (p.M + BM - 1) / BM;
+        tiles_n = tiles_mw * ((p.N + BN - 1) / BN);
         // order experts by row count, longest first (ties: lower id first)
-        for (int j = tid; j < EL; j += 256) {
+        for (int j = tid; j < EL; j += TL::kThreads) {
             int cj = s_off[j + 1] - s_off[j], rank = 0;
             for (int i = 0; i < EL; ++i) {
                 int ci = s_off[i + 1] - s_off[i];
@@ -167,6 +255,32 @@ __global__ __launch_bounds__(256) void gg_kernel(GemmParams p) {
         __syncthreads();
         n_tiles_total = EL * tiles_n;
     }
+
+    // per-lane parts of the LDS-direct load offsets
+    uint32_t lt_a0, lt_a1 = 0, lt_b0, lt_b1 = 0;
+    if (SCHED == SCHED_ROWS) {
+        lt_a0 = LY::lane_kc(lane, 0, p.lda);
+        lt_a1 = LY::lane_kc(lane, 1, p.lda);
+        if (LB == LAY_KC) {
+            lt_b0 = LY::lane_kc(lane, 0, p.ldw);
+            lt_b1 = LY::lane_kc(lane, 1, p.ldw);
+        } else {
+            lt_b0 = LY::lane_mn(lane, p.ldw);
+        }
+    } else {
+        lt_a0 = LY::lane_mn(lane, p.lda);
+        lt_b0 = LY::lane_mn(lane, p.ldb);
+    }
+
+    // B column (within the BN-wide tile) of this wave's nt-th 32-column MFMA tile
+    auto col_of = [&](int nt) {
+        if (EPI == EPI_SWIGLU) {
+            constexpr int HW = BN / 2 / WN;  // h columns per wave
+            const int half = nt / (NTW / 2), i = nt % (NTW / 2);
+            return half * (BN / 2) + wn * HW + 32 * i;
+        }
+        return wn * (BN / WN) + 32 * nt;
+    };
 
     const int G = gridDim.x;
     for (int tile = xcd_remap(blockIdx.x, G); tile < n_tiles_total; tile += G) {
@@ -187,9 +301,9 @@ __global__ __launch_bounds__(256) void gg_kernel(GemmParams p) {
                 else hi = mid - 1;
             }
             j = lo;
-            row0 = s_off[j] + (mi - s_start[j]) * kBM;
-            valid = min(kBM, s_off[j + 1] - row0);
-            KT = (p.two_seg ? 2 * p.Kd : p.Kd) / kBK;
+            row0 = s_off[j] + (mi - s_start[j]) * BM;
+            valid = min(BM, s_off[j + 1] - row0);
+            KT = (p.two_seg ? 2 * p.Kd : p.Kd) / BK;
         } else {
             j = s_start[tile / tiles_n];
             const int r = tile % tiles_n;
@@ -197,135 +311,181 @@ __global__ __launch_bounds__(256) void gg_kernel(GemmParams p) {
             ni = r / tiles_mw;
             row0 = s_off[j];
             valid = s_off[j + 1] - row0;
-            KT = (valid + kBK - 1) / kBK;
+            KT = (valid + BK - 1) / BK;
         }
+        // the decode is identical in every lane: tell the compiler so that the
+        // buffer descriptors below live in scalar registers
+        j = __builtin_amdgcn_readfirstlane(j);
+        row0 = __builtin_amdgcn_readfirstlane(row0);
+        valid = __builtin_amdgcn_readfirstlane(valid);
+        ni = __builtin_amdgcn_readfirstlane(ni);
+        mi_w = __builtin_amdgcn_readfirstlane(mi_w);
+        KT = __builtin_amdgcn_readfirstlane(KT);
 
-        // ---- loaders ----
-        // A, ROWS (KC): rows row0.. of a, resource bounded by the valid rows.
-        __amdgpu_buffer_rsrc_t rsA = make_rsrc(p.a + (int64_t)row0 * p.lda,
-                                               SCHED == SCHED_ROWS ? (uint32_t)(valid * p.lda * 2) : 0u);
-        auto issue = [&](int kt, int stage) {
-            uint8_t* sA = smem + stage * kStageBytes;
-            uint8_t* sB = sA + 16384;
-            const int k0 = kt * kBK;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int q = wave * 4 + u;  // 1 KiB chunk index 0..15
-                const int lrow = q * 8 + (lane >> 3), phys = lane & 7;
+        // ---- LDS-direct loader: load q fills 1 KiB of the stage ----
+        // Every bound that matters (ragged rows, matrix end) sits in the
+        // per-lane offset, which the buffer descriptor checks; out-of-range
+        // lanes read zero.
+        const i32x4 rsA = make_srd(p.a + (int64_t)row0 * p.lda,
+                                   SCHED == SCHED_ROWS ? (uint32_t)(valid * p.lda * 2) : 0u);
+        auto issue = [&](int kt, int slot) {
+            const uint32_t sA = lds_addr(smem) + slot * TL::kStage;
+            const uint32_t sB = sA + TL::kABytes;
+            const int k0 = kt * BK;
+            // re-materialise the lane terms each stage (cheap adds) rather than
+            // keeping one hoisted offset per load alive across the loop
+            uint32_t la0 = lt_a0, la1 = lt_a1, lb0 = lt_b0, lb1 = lt_b1;
+            asm volatile("" : "+v"(la0), "+v"(la1), "+v"(lb0), "+v"(lb1));
+            if (wave * LPW < TL::kALoads) {
                 // ---------------- A ----------------
                 if (SCHED == SCHED_ROWS) {
-                    const int lch = phys ^ swz_kc(lrow);
-                    uint32_t voff = (uint32_t)((lrow * p.lda + k0 + lch * 8) * 2);
-                    lds_load16(rsA, sA + q * 1024, voff);
-                } else {
-                    const int krow = lrow & 63, s = lrow >> 6;
-                    const int lch = phys ^ swz_mn(krow);
-                    const int rows_left = valid - k0;
-                    __amdgpu_buffer_rsrc_t r = make_rsrc(p.a + (int64_t)(row0 + k0) * p.lda,
-                                                         (uint32_t)(min(kBK, rows_left) * p.lda * 2));
-                    const int col = mi_w * kBM + s * 64 + lch * 8;
-                    uint32_t voff = col < p.M ? (uint32_t)((krow * p.lda + col) * 2) : kOOB;
-                    lds_load16(r, sA + q * 1024, voff);
-                }
-                // ---------------- B ----------------
-                if (SCHED == SCHED_WGRAD) {
-                    const int krow = lrow & 63, s = lrow >> 6;
-                    const int lch = phys ^ swz_mn(krow);
-                    const int rows_left = valid - k0;
-                    __amdgpu_buffer_rsrc_t r = make_rsrc(p.b + (int64_t)(row0 + k0) * p.ldb,
-                                                         (uint32_t)(min(kBK, rows_left) * p.ldb * 2));
-                    const int col = ni * kBN + s * 64 + lch * 8;
-                    uint32_t voff = col < p.N ? (uint32_t)((krow * p.ldb + col) * 2) : kOOB;
-                    lds_load16(r, sB + q * 1024, voff);
-                } else if (LB == LAY_MN) {
-                    // weight [Kd][ldw], N contiguous: two [64 k][64 col] sub-tiles
-                    const int krow = lrow & 63, s = lrow >> 6;
-                    const int lch = phys ^ swz_mn(krow);
-                    const uint16_t* w;
-                    int col;
-                    if (EPI == EPI_SWIGLU) {
-                        w = s ? p.w1 : p.w0;
-                        col = ni * 64 + lch * 8;
-                    } else {
-                        w = p.w0;
-                        col = ni * kBN + s * 64 + lch * 8;
+#pragma unroll
+                    for (int u = 0; u < LPW; ++u) {
+                        const int q = wave * LPW + u;
+                        const uint32_t lt = LY::kc_period(q) ? la1 : la0;
+                        const uint32_t voff = lt + (uint32_t)((q * LY::kRowsPerLoad * p.lda + k0) * 2);
+                        lds_load16(rsA, sA + q * 1024, voff);
                     }
-                    __amdgpu_buffer_rsrc_t r = make_rsrc(w + (int64_t)j * p.w_stride + (int64_t)k0 * p.ldw,
-                                                         (uint32_t)(kBK * p.ldw * 2));
-                    uint32_t voff = col < p.N ? (uint32_t)((krow * p.ldw + col) * 2) : kOOB;
-                    lds_load16(r, sB + q * 1024, voff);
                 } else {
-                    // weight [N][Kd], contraction contiguous; second segment from w1
-                    const int lch = phys ^ swz_kc(lrow);
-                    const bool seg1 = p.two_seg && k0 >= p.Kd;
-                    const uint16_t* w = seg1 ? p.w1 : p.w0;
-                    const int kk0 = seg1 ? k0 - p.Kd : k0;
-                    const int n0 = ni * kBN;
-                    __amdgpu_buffer_rsrc_t r = make_rsrc(w + (int64_t)j * p.w_stride + (int64_t)n0 * p.ldw,
-                                                         (uint32_t)(min(kBN, p.N - n0) * p.ldw * 2));
-                    uint32_t voff = (uint32_t)((lrow * p.ldw + kk0 + lch * 8) * 2);
-                    lds_load16(r, sB + q * 1024, voff);
+                    const i32x4 r = make_srd(p.a + (int64_t)(row0 + k0) * p.lda,
+                                             (uint32_t)(min(BK, valid - k0) * p.lda * 2));
+#pragma unroll
+                    for (int u = 0; u < LPW; ++u) {
+                        const int q = wave * LPW + u;
+                        const int col = mi_w * BM + (q / LY::kLoadsPerSub) * 64;
+                        const uint32_t voff =
+                            col < p.M ? la0 + (uint32_t)(((q % LY::kLoadsPerSub) * 8 * p.lda + col) * 2) : kOOB;
+                        lds_load16(r, sA + q * 1024, voff);
+                    }
+                }
+            } else {
+                // ---------------- B ----------------
+#pragma unroll
+                for (int u = 0; u < LPW; ++u) {
+                    const int q = wave * LPW + u - TL::kALoads;
+                    if (SCHED == SCHED_WGRAD) {
+                        const i32x4 r = make_srd(p.b + (int64_t)(row0 + k0) * p.ldb,
+                                                 (uint32_t)(min(BK, valid - k0) * p.ldb * 2));
+                        const int col = ni * BN + (q / LY::kLoadsPerSub) * 64;
+                        const uint32_t voff =
+                            col < p.N ? lb0 + (uint32_t)(((q % LY::kLoadsPerSub) * 8 * p.ldb + col) * 2) : kOOB;
+                        lds_load16(r, sB + q * 1024, voff);
+                    } else if (LB == LAY_MN) {
+                        // weight [Kd][ldw], N contiguous: [BK][64] sub-tiles
+                        const int sub = q / LY::kLoadsPerSub;
+                        const uint16_t* w;
+                        int col;
+                        if (EPI == EPI_SWIGLU) {
+                            constexpr int HS = BN / 128;  // sub-tiles per half
+                            w = sub < HS ? p.w0 : p.w1;
+                            col = ni * (BN / 2) + (sub % HS) * 64;
+                        } else {
+                            w = p.w0;
+                            col = ni * BN + sub * 64;
+                        }
+                        const i32x4 r = make_srd(w + (int64_t)j * p.w_stride, (uint32_t)(p.Kd * p.ldw * 2));
+                        const uint32_t voff =
+                            col < p.N ? lb0 + (uint32_t)((((q % LY::kLoadsPerSub) * 8 + k0) * p.ldw + col) * 2)
+                                      : kOOB;
+                        lds_load16(r, sB + q * 1024, voff);
+                    } else {
+                        // weight [N][Kd], contraction contiguous; second segment from w1
+                        const bool seg1 = p.two_seg && k0 >= p.Kd;
+                        const uint16_t* w = seg1 ? p.w1 : p.w0;
+                        const int kk0 = seg1 ? k0 - p.Kd : k0;
+                        const int n0 = ni * BN;
+                        const i32x4 r = make_srd(w + (int64_t)j * p.w_stride + (int64_t)n0 * p.ldw,
+                                                 (uint32_t)(min(BN, p.N - n0) * p.ldw * 2));
+                        const uint32_t lt = LY::kc_period(q) ? lb1 : lb0;
+                        const uint32_t voff = lt + (uint32_t)((q * LY::kRowsPerLoad * p.ldw + kk0) * 2);
+                        lds_load16(r, sB + q * 1024, voff);
+                    }
                 }
             }
         };
+        // wait until at most `n` stages of this wave's loads are still in flight
+        auto wait_stages = [&](int n) {
+            if (n <= 0) wait_vmcnt<0>();
+            else if (n == 1) wait_vmcnt<LPW>();
+            else wait_vmcnt<(2 * LPW < 64 ? 2 * LPW : 63)>();
+        };
 
-        f32x16 acc[2][2];
+        f32x16 acc[MTW][NTW];
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
+        for (int a = 0; a < MTW; ++a)
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
+            for (int b = 0; b < NTW; ++b)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
 
-        if (KT > 0) issue(0, 0);
-        for (int kt = 0; kt < KT; ++kt) {
-            const int stage = kt & 1;
-            if (kt + 1 < KT) {
-                issue(kt + 1, stage ^ 1);
-                __builtin_amdgcn_s_waitcnt(0x0F70 | 8);  // vmcnt(8): this stage's 8 loads are done
-            } else {
-                __builtin_amdgcn_s_waitcnt(0x0F70);      // vmcnt(0)
+        bf16x8 af[2][MTW], bfv[2][NTW];
+        auto load_frags = [&](int slot, int kk, int buf) {
+            const uint8_t* sA = smem + slot * TL::kStage;
+            const uint8_t* sB = sA + TL::kABytes;
+#pragma unroll
+            for (int mt = 0; mt < MTW; ++mt) {
+                const int rb = wm * (BM / WM) + mt * 32;
+                af[buf][mt] = SCHED == SCHED_ROWS ? LY::frag_kc(sA, rb, kk, lane) : LY::frag_mn(sA, rb, kk, lane);
             }
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt) {
+                const int cb = col_of(nt);
+                bfv[buf][nt] = (SCHED == SCHED_ROWS && LB == LAY_KC) ? LY::frag_kc(sB, cb, kk, lane)
+                                                                     : LY::frag_mn(sB, cb, kk, lane);
+            }
+        };
+
+        // Pipeline over a ring of S stages.  Loads run S-1 stages ahead.  At the
+        // end of k-step kt the stage two ahead is waited for and a barrier makes
+        // it visible, so the first fragments of stage kt+1 can be read while the
+        // last MFMAs of stage kt run; the same barrier frees stage kt's slot,
+        // which the loads issued at k-step kt+1 refill.
+        if (KT > 0) {
+            const int pre = min(S - 1, KT);
+            for (int t = 0; t < pre; ++t) issue(t, t);
+            wait_stages(pre - min(2, KT));
             __syncthreads();
-            const uint8_t* sA = smem + stage * kStageBytes;
-            const uint8_t* sB = sA + 16384;
+            load_frags(0, 0, 0);
+        }
+        for (int kt = 0; kt < KT; ++kt) {
+            const int slot = kt % S;
+            if (kt + S - 1 < KT) issue(kt + S - 1, (kt + S - 1) % S);
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                bf16x8 af[2], bfv[2];
+            for (int kk = 0; kk < KK; ++kk) {
+                const int cur = kk & 1;  // KK is even, so the parity restarts each stage
+                // next fragments; on the last k-step this reads a stale slot that
+                // no load is writing (harmless, never used) so that no branch
+                // makes the compiler's LDS wait counts pessimistic
+                if (kk + 1 < KK) load_frags(slot, kk + 1, cur ^ 1);
+                else load_frags((kt + 1) % S, 0, cur ^ 1);
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int mt = 0; mt < 2; ++mt) {
-                    const int rb = wm * 64 + mt * 32;
-                    af[mt] = SCHED == SCHED_ROWS ? frag_kc(sA, rb, kk, lane) : frag_mn(sA, rb, kk, lane);
-                }
+                for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
-                    const int cb = EPI == EPI_SWIGLU ? nt * 64 + wn * 32 : wn * 64 + nt * 32;
-                    bfv[nt] = (SCHED == SCHED_ROWS && LB == LAY_KC) ? frag_kc(sB, cb, kk, lane)
-                                                                    : frag_mn(sB, cb, kk, lane);
-                }
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                    for (int nt = 0; nt < 2; ++nt)
-                        acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfv[nt], af[mt], acc[mt][nt], 0, 0, 0);
+                    for (int nt = 0; nt < NTW; ++nt)
+                        acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfv[cur][nt], af[cur][mt],
+                                                                              acc[mt][nt], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
             }
+            // stages issued beyond kt+2: those up to min(kt+S-1, KT-1)
+            wait_stages(min(kt + S - 1, KT - 1) - (kt + 2));
             __syncthreads();
         }
 
         // ---- epilogue: lane holds row (l%32) and columns 8*j4 + 4*(l/32) + 0..3 ----
         const int cq = 4 * (lane >> 5);
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-            const int mloc = wm * 64 + mt * 32 + (lane & 31);
+        for (int mt = 0; mt < MTW; ++mt) {
+            const int mloc = wm * (BM / WM) + mt * 32 + (lane & 31);
             if (SCHED == SCHED_WGRAD) {
-                const int m = mi_w * kBM + mloc;
+                const int m = mi_w * BM + mloc;
                 if (m >= p.M) continue;
                 float* orow = p.cf + ((int64_t)j * p.M + m) * p.N;
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt)
+                for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
                     for (int j4 = 0; j4 < 4; ++j4) {
-                        const int n = ni * kBN + wn * 64 + nt * 32 + 8 * j4 + cq;
+                        const int n = ni * BN + col_of(nt) + 8 * j4 + cq;
                         if (n < p.N) {
                             f32x4 v = {acc[mt][nt][4 * j4], acc[mt][nt][4 * j4 + 1], acc[mt][nt][4 * j4 + 2],
                                        acc[mt][nt][4 * j4 + 3]};
@@ -338,32 +498,32 @@ __global__ __launch_bounds__(256) void gg_kernel(GemmParams p) {
             const int64_t row = row0 + mloc;
             if (EPI == EPI_SWIGLU) {
 #pragma unroll
-                for (int j4 = 0; j4 < 4; ++j4) {
-                    const int hc = ni * 64 + wn * 32 + 8 * j4 + cq;
-                    if (hc >= p.N) continue;
-                    float hv[4];
+                for (int i2 = 0; i2 < NTW / 2; ++i2) {
+                    const f32x16& ga = acc[mt][i2];
+                    const f32x16& ub = acc[mt][NTW / 2 + i2];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        float a = acc[mt][0][4 * j4 + i], b = acc[mt][1][4 * j4 + i];
-                        hv[i] = silu_f(a) * b;
-                    }
-                    u32x2 hw = {pack_bf2(hv[0], hv[1]), pack_bf2(hv[2], hv[3])};
-                    *(u32x2*)(p.c + row * p.ldc + hc) = hw;
-                    if (p.c2) {
-                        u32x2 aw = {pack_bf2(acc[mt][0][4 * j4], acc[mt][0][4 * j4 + 1]),
-                                    pack_bf2(acc[mt][0][4 * j4 + 2], acc[mt][0][4 * j4 + 3])};
-                        u32x2 bw = {pack_bf2(acc[mt][1][4 * j4], acc[mt][1][4 * j4 + 1]),
-                                    pack_bf2(acc[mt][1][4 * j4 + 2], acc[mt][1][4 * j4 + 3])};
-                        *(u32x2*)(p.c2 + row * 2 * p.N + hc) = aw;
-                        *(u32x2*)(p.c2 + row * 2 * p.N + p.N + hc) = bw;
+                    for (int j4 = 0; j4 < 4; ++j4) {
+                        const int hc = ni * (BN / 2) + col_of(i2) + 8 * j4 + cq;
+                        if (hc >= p.N) continue;
+                        float hv[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) hv[i] = silu_f(ga[4 * j4 + i]) * ub[4 * j4 + i];
+                        u32x2 hw = {pack_bf2(hv[0], hv[1]), pack_bf2(hv[2], hv[3])};
+                        *(u32x2*)(p.c + row * p.ldc + hc) = hw;
+                        if (p.c2) {
+                            u32x2 aw = {pack_bf2(ga[4 * j4], ga[4 * j4 + 1]), pack_bf2(ga[4 * j4 + 2], ga[4 * j4 + 3])};
+                            u32x2 bw = {pack_bf2(ub[4 * j4], ub[4 * j4 + 1]), pack_bf2(ub[4 * j4 + 2], ub[4 * j4 + 3])};
+                            *(u32x2*)(p.c2 + row * 2 * p.N + hc) = aw;
+                            *(u32x2*)(p.c2 + row * 2 * p.N + p.N + hc) = bw;
+                        }
                     }
                 }
             } else {
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt)
+                for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
                     for (int j4 = 0; j4 < 4; ++j4) {
-                        const int n = ni * kBN + wn * 64 + nt * 32 + 8 * j4 + cq;
+                        const int n = ni * BN + col_of(nt) + 8 * j4 + cq;
                         if (n >= p.N) continue;
                         float v[4];
 #pragma unroll
@@ -379,7 +539,7 @@ __global__ __launch_bounds__(256) void gg_kernel(GemmParams p) {
                             for (int i = 0; i < 4; ++i) {
                                 float a = (i & 1) ? bf_hi(aw[i >> 1]) : bf_lo(aw[i >> 1]);
                                 float b = (i & 1) ? bf_hi(bw[i >> 1]) : bf_lo(bw[i >> 1]);
-                                float s = 1.0f / (1.0f + __expf(-a));
+                                float s = sigmoid_f(a);
                                 da[i] = v[i] * b * s * (1.0f + a * (1.0f - s));
                                 db[i] = v[i] * a * s;
                             }
@@ -394,16 +554,40 @@ __global__ __launch_bounds__(256) void gg_kernel(GemmParams p) {
     }
 }
 
-template <int LB, int EPI, int SCHED>
-static int launch(const GemmParams& p, int grid, hipStream_t s) {
-    gg_kernel<LB, EPI, SCHED><<<grid, 256, 0, s>>>(p);
+// Tile configurations: big (256x256, four 128x128 waves) and small (128x128, four 64x64 waves).
+enum : int { CFG_BIG = 0, CFG_SMALL = 1 };
+
+static int tile_config() {
+    static int cfg = -1;
+    if (cfg < 0) {
+        const char* e = getenv("MOE_GEMM_TILE");
+        cfg = (e && atoi(e) == 128) ? CFG_SMALL : CFG_BIG;
+    }
+    return cfg;
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int LB, int EPI, int SCHED>
+static int launch_cfg(const GemmParams& p, hipStream_t s) {
+    using TL = Tile<BM, BN, BK, WM, WN>;
+    int64_t total_upper;
+    if (SCHED == SCHED_ROWS) {
+        const int tn = EPI == EPI_SWIGLU ? (p.N + BN / 2 - 1) / (BN / 2) : (p.N + BN - 1) / BN;
+        total_upper = ((p.cap + BM - 1) / BM + p.e_local) * (int64_t)tn;
+    } else {
+        total_upper = (int64_t)p.e_local * ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+    }
+    const int per_cu = TL::kStage * TL::kStages > 80 * 1024 ? 1 : 2;
+    int64_t g = std::min<int64_t>(total_upper, (int64_t)moe_host::num_cus() * per_cu);
+    const int grid = (int)((g + 7) / 8 * 8);
+    if (grid == 0) return MOE_OK;
+    gg_kernel<BM, BN, BK, WM, WN, LB, EPI, SCHED><<<grid, TL::kThreads, 0, s>>>(p);
     return moe_host::launch_status();
 }
 
-static int rows_grid(int64_t cap, int e_local, int tiles_n) {
-    int64_t upper = ((cap + kBM - 1) / kBM + e_local) * (int64_t)tiles_n;
-    int64_t g = std::min<int64_t>(upper, (int64_t)moe_host::num_cus() * 2);
-    return (int)((g + 7) / 8 * 8);
+template <int LB, int EPI, int SCHED>
+static int launch(const GemmParams& p, hipStream_t s) {
+    if (tile_config() == CFG_SMALL) return launch_cfg<128, 128, 32, 2, 2, LB, EPI, SCHED>(p, s);
+    return launch_cfg<256, 256, 32, 2, 2, LB, EPI, SCHED>(p, s);
 }
 
 }  // namespace moe
@@ -422,7 +606,7 @@ extern "C" int moe_grouped_gemm_swiglu(const moe_bf16* x_perm, const moe_bf16* w
     if (misaligned(x_perm) || misaligned(w_gate) || misaligned(w_up) || misaligned(offsets) || misaligned(h) ||
         misaligned(ab_save))
         return MOE_EALIGN;
-    if ((int64_t)kBM * H * 2 >= (1ll << 31) || (int64_t)kBK * F * 2 >= (1ll << 31)) return MOE_EINVAL;
+    if ((int64_t)256 * H * 2 >= (1ll << 31) || (int64_t)64 * F * 2 >= (1ll << 31)) return MOE_EINVAL;
     GemmParams p{};
     p.a = x_perm;
     p.lda = H;
@@ -439,8 +623,7 @@ extern "C" int moe_grouped_gemm_swiglu(const moe_bf16* x_perm, const moe_bf16* w
     p.ldc = F;
     p.c2 = ab_save;
     if (H == 0) return MOE_EINVAL;
-    int grid = rows_grid(cap_rows, e_local, F / 64);
-    return launch<LAY_MN, EPI_SWIGLU, SCHED_ROWS>(p, grid, (hipStream_t)stream);
+    return launch<LAY_MN, EPI_SWIGLU, SCHED_ROWS>(p, (hipStream_t)stream);
 }
 
 extern "C" int moe_grouped_gemm(const moe_bf16* a, int lda, const moe_bf16* w0, const moe_bf16* w1, int trans_w,
@@ -461,8 +644,8 @@ extern "C" int moe_grouped_gemm(const moe_bf16* a, int lda, const moe_bf16* w0, 
     if (misaligned(a) || misaligned(w0) || misaligned(w1) || misaligned(offsets) || misaligned(ab) ||
         misaligned(c))
         return MOE_EALIGN;
-    if ((int64_t)kBM * lda * 2 >= (1ll << 31) || (int64_t)kBN * Kd * 2 >= (1ll << 31) ||
-        (int64_t)kBK * N * 2 >= (1ll << 31))
+    if ((int64_t)256 * lda * 2 >= (1ll << 31) || (int64_t)256 * Kd * 2 >= (1ll << 31) ||
+        (int64_t)64 * N * 2 >= (1ll << 31))
         return MOE_EINVAL;
     GemmParams p{};
     p.a = a;
@@ -480,14 +663,13 @@ extern "C" int moe_grouped_gemm(const moe_bf16* a, int lda, const moe_bf16* w0, 
     p.c = c;
     p.ldc = ldc;
     p.ab = ab;
-    int grid = rows_grid(cap_rows, e_local, (N + kBN - 1) / kBN);
     hipStream_t s = (hipStream_t)stream;
     if (trans_w) {
-        if (epilogue == MOE_EPI_SWIGLU_BWD) return launch<LAY_KC, EPI_SWIGLU_BWD, SCHED_ROWS>(p, grid, s);
-        return launch<LAY_KC, EPI_BF16, SCHED_ROWS>(p, grid, s);
+        if (epilogue == MOE_EPI_SWIGLU_BWD) return launch<LAY_KC, EPI_SWIGLU_BWD, SCHED_ROWS>(p, s);
+        return launch<LAY_KC, EPI_BF16, SCHED_ROWS>(p, s);
     }
-    if (epilogue == MOE_EPI_SWIGLU_BWD) return launch<LAY_MN, EPI_SWIGLU_BWD, SCHED_ROWS>(p, grid, s);
-    return launch<LAY_MN, EPI_BF16, SCHED_ROWS>(p, grid, s);
+    if (epilogue == MOE_EPI_SWIGLU_BWD) return launch<LAY_MN, EPI_SWIGLU_BWD, SCHED_ROWS>(p, s);
+    return launch<LAY_MN, EPI_BF16, SCHED_ROWS>(p, s);
 }
 
 extern "C" int moe_wgrad(const moe_bf16* a, int lda, const moe_bf16* b, int ldb, const int32_t* offsets,
@@ -500,7 +682,7 @@ extern "C" int moe_wgrad(const moe_bf16* a, int lda, const moe_bf16* b, int ldb,
     if (e_local == 0 || M == 0 || N == 0) return MOE_OK;
     if (!dw || (cap_rows > 0 && (!a || !b))) return MOE_EINVAL;
     if (misaligned(a) || misaligned(b) || misaligned(offsets) || misaligned(dw)) return MOE_EALIGN;
-    if ((int64_t)kBK * lda * 2 >= (1ll << 31) || (int64_t)kBK * ldb * 2 >= (1ll << 31)) return MOE_EINVAL;
+    if ((int64_t)64 * lda * 2 >= (1ll << 31) || (int64_t)64 * ldb * 2 >= (1ll << 31)) return MOE_EINVAL;
     GemmParams p{};
     p.a = a;
     p.lda = lda;
@@ -512,8 +694,5 @@ extern "C" int moe_wgrad(const moe_bf16* a, int lda, const moe_bf16* b, int ldb,
     p.M = M;
     p.N = N;
     p.cf = dw;
-    int64_t total = (int64_t)e_local * ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
-    int64_t g = std::min<int64_t>(total, (int64_t)moe_host::num_cus() * 2);
-    int grid = (int)((g + 7) / 8 * 8);
-    return launch<LAY_MN, EPI_F32, SCHED_WGRAD>(p, grid, (hipStream_t)stream);
+    return launch<LAY_MN, EPI_F32, SCHED_WGRAD>(p, (hipStream_t)stream);
 }
