@@ -74,12 +74,16 @@ struct GemmParams {
 typedef __attribute__((ext_vector_type(4))) int i32x4;
 
 // Buffer resource (raw, stride 0): loads at or past `bytes` return zero.
+// Buffer descriptor (gfx9 layout: base, stride 0, byte range, format dword).
+// Callers pass wave-uniform values; readfirstlane states that to the compiler
+// (a no-op on values it already holds in scalar registers) so the descriptor
+// can always live in SGPRs as the buffer instructions require.
 __device__ __forceinline__ i32x4 make_srd(const void* base, uint32_t bytes) {
     const uint64_t a = (uint64_t)base;
     i32x4 r;
-    r[0] = (int)(uint32_t)a;
-    r[1] = (int)((a >> 32) & 0xffff);
-    r[2] = (int)bytes;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffff));
+    r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
     r[3] = 0x00020000;
     return r;
 }
@@ -165,7 +169,7 @@ __device__ __forceinline__ int xcd_remap(int b, int G) { return (b & 7) * (G >> 
 // Block tile BM x BN (B columns; for SWIGLU the gate half then the up half),
 // contraction step BK, a ring of STAGES LDS stages, WM x WN waves each owning a
 // (BM/WM) x (BN/WN) tile of 32x32 MFMA tiles.
-template <int BM, int BN, int BK, int WM, int WN>
+template <int BM, int BN, int BK, int WM, int WN, int LDS_BUDGET = kLdsBudget>
 struct Tile {
     static constexpr int kWaves = WM * WN;
     static constexpr int kThreads = 64 * kWaves;
@@ -173,21 +177,20 @@ struct Tile {
     static constexpr int kNTW = BN / WN / 32;
     static constexpr int kABytes = BM * BK * 2;
     static constexpr int kStage = (BM + BN) * BK * 2;
-    static constexpr int kStages = kLdsBudget / kStage < 4 ? kLdsBudget / kStage : 4;
+    static constexpr int kStages = LDS_BUDGET / kStage < 4 ? LDS_BUDGET / kStage : 4;
     static constexpr int kLoads = kStage / 1024;  // 1 KiB LDS-direct loads per stage
     static constexpr int kALoads = kABytes / 1024;
     static constexpr int kLoadsPerWave = kLoads / kWaves;
     static constexpr int kKK = BK / 16;           // MFMA k-steps per stage
     static_assert(kStages >= 3, "the pipeline needs at least three stages");
-    static_assert(kLoads % kWaves == 0, "loads must split evenly over the waves");
-    static_assert(kALoads % kLoadsPerWave == 0, "a wave's loads must be all A or all B");
+    static_assert(kLoads % kWaves == 0 && kALoads % kWaves == 0, "loads must split evenly over the waves");
     static_assert(kLoadsPerWave * (kStages - 1) < 64, "vmcnt range");
 };
 
-template <int BM, int BN, int BK, int WM, int WN, int LB, int EPI, int SCHED>
+template <int BM, int BN, int BK, int WM, int WN, int LB, int EPI, int SCHED, int LDSB>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void gg_kernel(GemmParams p) {
-    using TL = Tile<BM, BN, BK, WM, WN>;
+    using TL = Tile<BM, BN, BK, WM, WN, LDSB>;
     using LY = Lay<BK>;
     constexpr int MTW = TL::kMTW, NTW = TL::kNTW, LPW = TL::kLoadsPerWave, S = TL::kStages, KK = TL::kKK;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[S * TL::kStage];
@@ -328,51 +331,51 @@ void gg_kernel(GemmParams p) {
         // lanes read zero.
         const i32x4 rsA = make_srd(p.a + (int64_t)row0 * p.lda,
                                    SCHED == SCHED_ROWS ? (uint32_t)(valid * p.lda * 2) : 0u);
-        auto issue = [&](int kt, int slot) {
+        // Load u (0..LPW-1) of this wave for stage kt into LDS slot `slot`.  A
+        // stage past the end of the contraction (live == false) is loaded from
+        // the out-of-range offset: zeros, no memory traffic, and the same number
+        // of loads per stage, so the vmcnt bookkeeping stays fixed.
+        auto load_one = [&](int kt, int slot, int u, bool live) {
             const uint32_t sA = lds_addr(smem) + slot * TL::kStage;
             const uint32_t sB = sA + TL::kABytes;
             const int k0 = kt * BK;
-            // re-materialise the lane terms each stage (cheap adds) rather than
+            // re-materialise the lane terms each load (cheap adds) rather than
             // keeping one hoisted offset per load alive across the loop
             uint32_t la0 = lt_a0, la1 = lt_a1, lb0 = lt_b0, lb1 = lt_b1;
             asm volatile("" : "+v"(la0), "+v"(la1), "+v"(lb0), "+v"(lb1));
-            if (wave * LPW < TL::kALoads) {
-                // ---------------- A ----------------
-                if (SCHED == SCHED_ROWS) {
-#pragma unroll
-                    for (int u = 0; u < LPW; ++u) {
-                        const int q = wave * LPW + u;
+            {
+                // load u of wave w fills A block u*W + w (u < LA) or B block
+                // (u - LA)*W + w: A/B and the sub-tile follow from u at compile
+                // time, so the stream of loads has no branches
+                constexpr int LA = TL::kALoads / TL::kWaves;
+                constexpr bool kSubPerLoad = LY::kLoadsPerSub == TL::kWaves;
+                // MN blocks: sub-tile (64 columns) and 8-k-row group of block v*W + w
+                auto mn_sub = [&](int v) { return kSubPerLoad ? v : (v * TL::kWaves + wave) / LY::kLoadsPerSub; };
+                auto mn_kr = [&](int v) { return kSubPerLoad ? wave : (v * TL::kWaves + wave) % LY::kLoadsPerSub; };
+                if (u < LA) {
+                    const int q = u * TL::kWaves + wave;
+                    if (SCHED == SCHED_ROWS) {
                         const uint32_t lt = LY::kc_period(q) ? la1 : la0;
                         const uint32_t voff = lt + (uint32_t)((q * LY::kRowsPerLoad * p.lda + k0) * 2);
-                        lds_load16(rsA, sA + q * 1024, voff);
+                        lds_load16(rsA, sA + q * 1024, live ? voff : kOOB);
+                    } else {
+                        const i32x4 r = make_srd(p.a + (int64_t)(row0 + k0) * p.lda,
+                                                 (uint32_t)(max(0, min(BK, valid - k0)) * p.lda * 2));
+                        const int col = mi_w * BM + mn_sub(u) * 64;
+                        const uint32_t voff = col < p.M ? la0 + (uint32_t)((mn_kr(u) * 8 * p.lda + col) * 2) : kOOB;
+                        lds_load16(r, sA + q * 1024, live ? voff : kOOB);
                     }
                 } else {
-                    const i32x4 r = make_srd(p.a + (int64_t)(row0 + k0) * p.lda,
-                                             (uint32_t)(min(BK, valid - k0) * p.lda * 2));
-#pragma unroll
-                    for (int u = 0; u < LPW; ++u) {
-                        const int q = wave * LPW + u;
-                        const int col = mi_w * BM + (q / LY::kLoadsPerSub) * 64;
-                        const uint32_t voff =
-                            col < p.M ? la0 + (uint32_t)(((q % LY::kLoadsPerSub) * 8 * p.lda + col) * 2) : kOOB;
-                        lds_load16(r, sA + q * 1024, voff);
-                    }
-                }
-            } else {
-                // ---------------- B ----------------
-#pragma unroll
-                for (int u = 0; u < LPW; ++u) {
-                    const int q = wave * LPW + u - TL::kALoads;
+                    const int q = (u - LA) * TL::kWaves + wave;
                     if (SCHED == SCHED_WGRAD) {
                         const i32x4 r = make_srd(p.b + (int64_t)(row0 + k0) * p.ldb,
-                                                 (uint32_t)(min(BK, valid - k0) * p.ldb * 2));
-                        const int col = ni * BN + (q / LY::kLoadsPerSub) * 64;
-                        const uint32_t voff =
-                            col < p.N ? lb0 + (uint32_t)(((q % LY::kLoadsPerSub) * 8 * p.ldb + col) * 2) : kOOB;
-                        lds_load16(r, sB + q * 1024, voff);
+                                                 (uint32_t)(max(0, min(BK, valid - k0)) * p.ldb * 2));
+                        const int col = ni * BN + mn_sub(u - LA) * 64;
+                        const uint32_t voff = col < p.N ? lb0 + (uint32_t)((mn_kr(u - LA) * 8 * p.ldb + col) * 2) : kOOB;
+                        lds_load16(r, sB + q * 1024, live ? voff : kOOB);
                     } else if (LB == LAY_MN) {
                         // weight [Kd][ldw], N contiguous: [BK][64] sub-tiles
-                        const int sub = q / LY::kLoadsPerSub;
+                        const int sub = mn_sub(u - LA);
                         const uint16_t* w;
                         int col;
                         if (EPI == EPI_SWIGLU) {
@@ -385,9 +388,8 @@ void gg_kernel(GemmParams p) {
                         }
                         const i32x4 r = make_srd(w + (int64_t)j * p.w_stride, (uint32_t)(p.Kd * p.ldw * 2));
                         const uint32_t voff =
-                            col < p.N ? lb0 + (uint32_t)((((q % LY::kLoadsPerSub) * 8 + k0) * p.ldw + col) * 2)
-                                      : kOOB;
-                        lds_load16(r, sB + q * 1024, voff);
+                            col < p.N ? lb0 + (uint32_t)(((mn_kr(u - LA) * 8 + k0) * p.ldw + col) * 2) : kOOB;
+                        lds_load16(r, sB + q * 1024, live ? voff : kOOB);
                     } else {
                         // weight [N][Kd], contraction contiguous; second segment from w1
                         const bool seg1 = p.two_seg && k0 >= p.Kd;
@@ -398,26 +400,24 @@ void gg_kernel(GemmParams p) {
                                                  (uint32_t)(min(BN, p.N - n0) * p.ldw * 2));
                         const uint32_t lt = LY::kc_period(q) ? lb1 : lb0;
                         const uint32_t voff = lt + (uint32_t)((q * LY::kRowsPerLoad * p.ldw + kk0) * 2);
-                        lds_load16(r, sB + q * 1024, voff);
+                        lds_load16(r, sB + q * 1024, live ? voff : kOOB);
                     }
                 }
             }
         };
-        // wait until at most `n` stages of this wave's loads are still in flight
-        auto wait_stages = [&](int n) {
-            if (n <= 0) wait_vmcnt<0>();
-            else if (n == 1) wait_vmcnt<LPW>();
-            else wait_vmcnt<(2 * LPW < 64 ? 2 * LPW : 63)>();
+        auto issue = [&](int kt, int slot, bool live) {
+#pragma unroll
+            for (int u = 0; u < LPW; ++u) load_one(kt, slot, u, live);
         };
 
         f32x16 acc[MTW][NTW];
 #pragma unroll
         for (int a = 0; a < MTW; ++a)
 #pragma unroll
-            for (int b = 0; b < NTW; ++b)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
+            for (int b = 0; b < NTW; ++b) acc[a][b] = f32x16{};
 
+        // Two fragment buffers: the fragments of k16 step s+1 are read while
+        // the MFMAs of step s run.
         bf16x8 af[2][MTW], bfv[2][NTW];
         auto load_frags = [&](int slot, int kk, int buf) {
             const uint8_t* sA = smem + slot * TL::kStage;
@@ -434,43 +434,68 @@ void gg_kernel(GemmParams p) {
                                                                      : LY::frag_mn(sB, cb, kk, lane);
             }
         };
+        // LDS reads one fragment set takes: a KC fragment is one 16-byte read,
+        // an MN fragment two transposing 8-byte reads
+        constexpr int kReadsA = SCHED == SCHED_ROWS ? MTW : 2 * MTW;
+        constexpr int kReadsB = (SCHED == SCHED_ROWS && LB == LAY_KC) ? NTW : 2 * NTW;
+        constexpr int kReads = kReadsA + kReadsB;
+        constexpr int kMfma = MTW * NTW;
+        static_assert(KK == 2, "two k16 steps per stage");
+        constexpr int LPS = LPW / KK;  // LDS-direct loads per k16 step
+        static_assert(LPW % KK == 0, "loads split over the steps of a stage");
 
-        // Pipeline over a ring of S stages.  Loads run S-1 stages ahead.  At the
-        // end of k-step kt the stage two ahead is waited for and a barrier makes
-        // it visible, so the first fragments of stage kt+1 can be read while the
-        // last MFMAs of stage kt run; the same barrier frees stage kt's slot,
-        // which the loads issued at k-step kt+1 refill.
+        // Pipeline over a ring of S LDS stages, loads S-1 stages ahead.  The k16
+        // steps of stage kt issue the loads of stage kt+S-1 (one every few
+        // MFMAs) and read the next step's fragments (one LDS read per MFMA), so
+        // LDS-direct writes, fragment reads and MFMAs overlap instead of coming
+        // in bursts.  Every stage issues the same number of loads (past the end
+        // they are zero loads), so "stages up to kt+2 have landed" is a fixed
+        // vmcnt of S-3 stages at the end of stage kt.  The barrier after it
+        // publishes stage kt+2 (first read in the last step of stage kt+1) and
+        // frees the slot of stage kt, which stage kt+1's loads refill.
+        constexpr int kWaitLoads = (S - 3) * LPW;
         if (KT > 0) {
-            const int pre = min(S - 1, KT);
-            for (int t = 0; t < pre; ++t) issue(t, t);
-            wait_stages(pre - min(2, KT));
+#pragma unroll
+            for (int t = 0; t < S - 1; ++t) issue(t, t, t < KT);
+            wait_vmcnt<kWaitLoads>();
             __syncthreads();
             load_frags(0, 0, 0);
         }
         for (int kt = 0; kt < KT; ++kt) {
-            const int slot = kt % S;
-            if (kt + S - 1 < KT) issue(kt + S - 1, (kt + S - 1) % S);
+            const int kn = kt + S - 1;
+            const bool live = kn < KT;
+            const int nslot = kn % S;
+            const int slot1 = (kt + 1) % S;
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) {
-                const int cur = kk & 1;  // KK is even, so the parity restarts each stage
-                // next fragments; on the last k-step this reads a stale slot that
-                // no load is writing (harmless, never used) so that no branch
-                // makes the compiler's LDS wait counts pessimistic
-                if (kk + 1 < KK) load_frags(slot, kk + 1, cur ^ 1);
-                else load_frags((kt + 1) % S, 0, cur ^ 1);
-                __builtin_amdgcn_sched_barrier(0);
+                // next step: (kt, 1) or (kt+1, 0)
+                if (kk + 1 < KK) load_frags(kt % S, kk + 1, (kk + 1) & 1);
+                else load_frags(slot1, 0, (kk + 1) & 1);
 #pragma unroll
-                for (int mt = 0; mt < MTW; ++mt)
+                for (int mt = 0; mt < MTW; ++mt) {
 #pragma unroll
                     for (int nt = 0; nt < NTW; ++nt)
-                        acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfv[cur][nt], af[cur][mt],
+                        acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfv[kk & 1][nt], af[kk & 1][mt],
                                                                               acc[mt][nt], 0, 0, 0);
+#pragma unroll
+                    for (int u = 0; u < LPS; ++u)
+                        if (u * MTW / LPS == mt) load_one(kn, nslot, kk * LPS + u, live);
+                }
+                // each MFMA followed by its share of the LDS reads (at most one
+                // per MFMA when there are more MFMAs than reads)
+                constexpr int kPer = (kReads + kMfma - 1) / kMfma;
+#pragma unroll
+                for (int t = 0; t < kMfma; ++t) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                    if (t * kPer < kReads) __builtin_amdgcn_sched_group_barrier(0x100, kPer, 0);  // LDS reads
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
-            // stages issued beyond kt+2: those up to min(kt+S-1, KT-1)
-            wait_stages(min(kt + S - 1, KT - 1) - (kt + 2));
+            wait_vmcnt<kWaitLoads>();
             __syncthreads();
         }
+        wait_vmcnt<0>();  // zero loads of the stages past the end
+        __syncthreads();  // the next tile's first loads overwrite the ring
 
         // ---- epilogue: lane holds row (l%32) and columns 8*j4 + 4*(l/32) + 0..3 ----
         const int cq = 4 * (lane >> 5);
@@ -554,21 +579,28 @@ void gg_kernel(GemmParams p) {
     }
 }
 
-// Tile configurations: big (256x256, four 128x128 waves) and small (128x128, four 64x64 waves).
+// Tile configurations.
+//   big    256x256, four 128x128 waves, 4-stage ring (128 KiB LDS, one workgroup
+//          per CU).  A 128x128 wave tile is the largest the 256 accumulator
+//          registers allow and moves the fewest LDS bytes per MFMA, which is what
+//          bounds this kernel.
+//   small  128x128, four 64x64 waves (kept for comparisons: MOE_GEMM_TILE=128)
 enum : int { CFG_BIG = 0, CFG_SMALL = 1 };
+
+static int env_int(const char* name, int dflt) {
+    const char* e = getenv(name);
+    return e ? atoi(e) : dflt;
+}
 
 static int tile_config() {
     static int cfg = -1;
-    if (cfg < 0) {
-        const char* e = getenv("MOE_GEMM_TILE");
-        cfg = (e && atoi(e) == 128) ? CFG_SMALL : CFG_BIG;
-    }
+    if (cfg < 0) cfg = env_int("MOE_GEMM_TILE", 256) == 128 ? CFG_SMALL : CFG_BIG;
     return cfg;
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int LB, int EPI, int SCHED>
+template <int BM, int BN, int BK, int WM, int WN, int LB, int EPI, int SCHED, int LDSB>
 static int launch_cfg(const GemmParams& p, hipStream_t s) {
-    using TL = Tile<BM, BN, BK, WM, WN>;
+    using TL = Tile<BM, BN, BK, WM, WN, LDSB>;
     int64_t total_upper;
     if (SCHED == SCHED_ROWS) {
         const int tn = EPI == EPI_SWIGLU ? (p.N + BN / 2 - 1) / (BN / 2) : (p.N + BN - 1) / BN;
@@ -576,18 +608,18 @@ static int launch_cfg(const GemmParams& p, hipStream_t s) {
     } else {
         total_upper = (int64_t)p.e_local * ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
     }
-    const int per_cu = TL::kStage * TL::kStages > 80 * 1024 ? 1 : 2;
+    const int per_cu = (TL::kStage * TL::kStages > 80 * 1024 || TL::kMTW * TL::kNTW >= 8) ? 1 : 2;
     int64_t g = std::min<int64_t>(total_upper, (int64_t)moe_host::num_cus() * per_cu);
     const int grid = (int)((g + 7) / 8 * 8);
     if (grid == 0) return MOE_OK;
-    gg_kernel<BM, BN, BK, WM, WN, LB, EPI, SCHED><<<grid, TL::kThreads, 0, s>>>(p);
+    gg_kernel<BM, BN, BK, WM, WN, LB, EPI, SCHED, LDSB><<<grid, TL::kThreads, 0, s>>>(p);
     return moe_host::launch_status();
 }
 
 template <int LB, int EPI, int SCHED>
 static int launch(const GemmParams& p, hipStream_t s) {
-    if (tile_config() == CFG_SMALL) return launch_cfg<128, 128, 32, 2, 2, LB, EPI, SCHED>(p, s);
-    return launch_cfg<256, 256, 32, 2, 2, LB, EPI, SCHED>(p, s);
+    if (tile_config() == CFG_SMALL) return launch_cfg<128, 128, 32, 2, 2, LB, EPI, SCHED, kLdsBudget>(p, s);
+    return launch_cfg<256, 256, 32, 2, 2, LB, EPI, SCHED, kLdsBudget>(p, s);
 }
 
 }  // namespace moe
