@@ -187,16 +187,15 @@ struct Tile {
     static_assert(kLoadsPerWave * (kStages - 1) < 64, "vmcnt range");
 };
 
+// The GEMM of one workgroup for one tile shape.  smem is the stage ring;
+// s_off holds the clamped row offsets (already loaded); s_start and s_wave are
+// scratch for the schedule.
 template <int BM, int BN, int BK, int WM, int WN, int LB, int EPI, int SCHED, int LDSB>
-__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(1, 2)))
-void gg_kernel(GemmParams p) {
+__device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, const int* s_off, int* s_start,
+                                        int* s_wave) {
     using TL = Tile<BM, BN, BK, WM, WN, LDSB>;
     using LY = Lay<BK>;
     constexpr int MTW = TL::kMTW, NTW = TL::kNTW, LPW = TL::kLoadsPerWave, S = TL::kStages, KK = TL::kKK;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[S * TL::kStage];
-    __shared__ int s_off[kMaxGroups + 1];    // clamped row offsets
-    __shared__ int s_start[kMaxGroups + 1];  // ROWS: first m-tile of each expert; WGRAD: sorted order
-    __shared__ int s_wave[16];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
@@ -204,11 +203,6 @@ void gg_kernel(GemmParams p) {
     const int EL = p.e_local;
 
     // ---- per-workgroup schedule setup (device-resident row counts) ----
-    for (int j = tid; j <= EL; j += TL::kThreads) {
-        int64_t o = p.offsets[j];
-        s_off[j] = (int)(o < p.cap ? o : p.cap);
-    }
-    __syncthreads();
     int n_tiles_total;
     int tiles_n;  // tiles along N (ROWS) ; tiles per group (WGRAD)
     int tiles_mw = 0;
@@ -441,8 +435,6 @@ void gg_kernel(GemmParams p) {
         constexpr int kReads = kReadsA + kReadsB;
         constexpr int kMfma = MTW * NTW;
         static_assert(KK == 2, "two k16 steps per stage");
-        constexpr int LPS = LPW / KK;  // LDS-direct loads per k16 step
-        static_assert(LPW % KK == 0, "loads split over the steps of a stage");
 
         // Pipeline over a ring of S LDS stages, loads S-1 stages ahead.  The k16
         // steps of stage kt issue the loads of stage kt+S-1 (one every few
@@ -477,9 +469,11 @@ void gg_kernel(GemmParams p) {
                     for (int nt = 0; nt < NTW; ++nt)
                         acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfv[kk & 1][nt], af[kk & 1][mt],
                                                                               acc[mt][nt], 0, 0, 0);
+                    // this step's share of the stage's loads, spread over its MFMA rows
+                    const int lo = kk * LPW / KK, n = (kk + 1) * LPW / KK - lo;
 #pragma unroll
-                    for (int u = 0; u < LPS; ++u)
-                        if (u * MTW / LPS == mt) load_one(kn, nslot, kk * LPS + u, live);
+                    for (int i = 0; i < LPW; ++i)
+                        if (i < n && i * MTW / n == mt) load_one(kn, nslot, lo + i, live);
                 }
                 // each MFMA followed by its share of the LDS reads (at most one
                 // per MFMA when there are more MFMAs than reads)
@@ -579,13 +573,81 @@ void gg_kernel(GemmParams p) {
     }
 }
 
+// Whether tiles of ALT rows beat tiles of BM rows on this call's row counts:
+// every workgroup evaluates the same device-resident counts, so all agree.
+// Cost model: rounds of tiles over the grid times the tile's rows, with 10%
+// added for the smaller tile, whose MFMAs run a little less efficiently.
+template <int BM, int ALT, int BN, int EPI, int THREADS>
+__device__ __forceinline__ bool prefer_alt(const GemmParams& p, const int* s_off, int* s_wave) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int mb = 0, ma = 0;
+    for (int j = tid; j < p.e_local; j += THREADS) {
+        const int c = s_off[j + 1] - s_off[j];
+        mb += (c + BM - 1) / BM;
+        ma += (c + ALT - 1) / ALT;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        mb += __shfl_xor(mb, o, 64);
+        ma += __shfl_xor(ma, o, 64);
+    }
+    if (lane == 0) {
+        s_wave[2 * wave] = mb;
+        s_wave[2 * wave + 1] = ma;
+    }
+    __syncthreads();
+    mb = ma = 0;
+    for (int w = 0; w < THREADS / 64; ++w) {
+        mb += s_wave[2 * w];
+        ma += s_wave[2 * w + 1];
+    }
+    __syncthreads();  // s_wave is reused by the schedule
+    const int64_t tn = EPI == EPI_SWIGLU ? (p.N + BN / 2 - 1) / (BN / 2) : (p.N + BN - 1) / BN;
+    const int64_t G = gridDim.x;
+    const int64_t rb = (mb * tn + G - 1) / G, ra = (ma * tn + G - 1) / G;
+    return ra * ALT * 11 < rb * BM * 10;
+}
+
+// One launch: loads the row offsets, then runs the BM-row body, or the
+// ALT-row body when ALT != 0 and prefer_alt says so.
+template <int BM, int BN, int BK, int WM, int WN, int LB, int EPI, int SCHED, int LDSB, int ALT>
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(1, 2)))
+void gg_kernel(GemmParams p) {
+    using TL = Tile<BM, BN, BK, WM, WN, LDSB>;
+    using TA = Tile<ALT ? ALT : BM, BN, BK, WM, WN, LDSB>;
+    constexpr int kRing = TL::kStages * TL::kStage;
+    constexpr int kRingA = TA::kStages * TA::kStage;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[kRing > kRingA ? kRing : kRingA];
+    __shared__ int s_off[kMaxGroups + 1];    // clamped row offsets
+    __shared__ int s_start[kMaxGroups + 1];  // ROWS: first m-tile of each expert; WGRAD: sorted order
+    __shared__ int s_wave[16];
+    for (int j = threadIdx.x; j <= p.e_local; j += TL::kThreads) {
+        int64_t o = p.offsets[j];
+        s_off[j] = (int)(o < p.cap ? o : p.cap);
+    }
+    __syncthreads();
+    if constexpr (ALT != 0) {
+        if (prefer_alt<BM, ALT, BN, EPI, TL::kThreads>(p, s_off, s_wave)) {
+            gg_body<ALT, BN, BK, WM, WN, LB, EPI, SCHED, LDSB>(p, smem, s_off, s_start, s_wave);
+            return;
+        }
+    }
+    gg_body<BM, BN, BK, WM, WN, LB, EPI, SCHED, LDSB>(p, smem, s_off, s_start, s_wave);
+}
+
 // Tile configurations.
 //   big    256x256, four 128x128 waves, 4-stage ring (128 KiB LDS, one workgroup
 //          per CU).  A 128x128 wave tile is the largest the 256 accumulator
 //          registers allow and moves the fewest LDS bytes per MFMA, which is what
 //          bounds this kernel.
-//   small  128x128, four 64x64 waves (kept for comparisons: MOE_GEMM_TILE=128)
-enum : int { CFG_BIG = 0, CFG_SMALL = 1 };
+//   mid    192x256, four 96x128 waves, 4-stage ring (112 KiB): for experts of
+//          about 100-190 rows, where a 256-row tile is mostly padding
+//   auto   (default) the row-tiled GEMMs carry both big and mid bodies and pick
+//          one per call on the device from the row counts; the weight-gradient
+//          GEMM uses big
+//   small  128x128, four 64x64 waves
+// MOE_GEMM_TILE=256, 192 or 128 pins one configuration (for comparisons).
+enum : int { CFG_AUTO = 0, CFG_BIG = 1, CFG_MID = 2, CFG_SMALL = 3 };
 
 static int env_int(const char* name, int dflt) {
     const char* e = getenv(name);
@@ -594,17 +656,21 @@ static int env_int(const char* name, int dflt) {
 
 static int tile_config() {
     static int cfg = -1;
-    if (cfg < 0) cfg = env_int("MOE_GEMM_TILE", 256) == 128 ? CFG_SMALL : CFG_BIG;
+    if (cfg < 0) {
+        const int t = env_int("MOE_GEMM_TILE", 0);
+        cfg = t == 128 ? CFG_SMALL : t == 192 ? CFG_MID : t == 256 ? CFG_BIG : CFG_AUTO;
+    }
     return cfg;
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int LB, int EPI, int SCHED, int LDSB>
+template <int BM, int BN, int BK, int WM, int WN, int LB, int EPI, int SCHED, int LDSB, int ALT = 0>
 static int launch_cfg(const GemmParams& p, hipStream_t s) {
     using TL = Tile<BM, BN, BK, WM, WN, LDSB>;
     int64_t total_upper;
     if (SCHED == SCHED_ROWS) {
         const int tn = EPI == EPI_SWIGLU ? (p.N + BN / 2 - 1) / (BN / 2) : (p.N + BN - 1) / BN;
-        total_upper = ((p.cap + BM - 1) / BM + p.e_local) * (int64_t)tn;
+        constexpr int bm = ALT && ALT < BM ? ALT : BM;
+        total_upper = ((p.cap + bm - 1) / bm + p.e_local) * (int64_t)tn;
     } else {
         total_upper = (int64_t)p.e_local * ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
     }
@@ -612,13 +678,17 @@ static int launch_cfg(const GemmParams& p, hipStream_t s) {
     int64_t g = std::min<int64_t>(total_upper, (int64_t)moe_host::num_cus() * per_cu);
     const int grid = (int)((g + 7) / 8 * 8);
     if (grid == 0) return MOE_OK;
-    gg_kernel<BM, BN, BK, WM, WN, LB, EPI, SCHED, LDSB><<<grid, TL::kThreads, 0, s>>>(p);
+    gg_kernel<BM, BN, BK, WM, WN, LB, EPI, SCHED, LDSB, ALT><<<grid, TL::kThreads, 0, s>>>(p);
     return moe_host::launch_status();
 }
 
 template <int LB, int EPI, int SCHED>
 static int launch(const GemmParams& p, hipStream_t s) {
     if (tile_config() == CFG_SMALL) return launch_cfg<128, 128, 32, 2, 2, LB, EPI, SCHED, kLdsBudget>(p, s);
+    if constexpr (SCHED == SCHED_ROWS) {
+        if (tile_config() == CFG_MID) return launch_cfg<192, 256, 32, 2, 2, LB, EPI, SCHED, kLdsBudget>(p, s);
+        if (tile_config() == CFG_AUTO) return launch_cfg<256, 256, 32, 2, 2, LB, EPI, SCHED, kLdsBudget, 192>(p, s);
+    }
     return launch_cfg<256, 256, 32, 2, 2, LB, EPI, SCHED, kLdsBudget>(p, s);
 }
 
