@@ -9,14 +9,60 @@
 // loads and no shared memory.  MoonEP page: the dispatch gradient sums each
 // token's K dispatched copies, i.e. the same combine without gates.
 //
-// One wave64 per token, lanes over 16-byte column vectors.  For every
-// column vector the K source rows are loaded together (K independent 16-byte
-// loads in flight per lane), then accumulated in k order.
+// One wave64 per token, lanes over 16-byte column vectors.  The token's
+// valid rows (pos >= 0) are compacted in k order; a body sized for that count
+// then keeps NV x U independent 16-byte loads in flight per lane (NV rows x U
+// column vectors, 8 to 16 in all) before accumulating each column vector over
+// the rows in k order.  A token with no local row gets zeros.
 #include "moe_common.hpp"
 
 namespace moe {
 
-template <bool GATED, int KMAX>
+template <bool GATED, int NV, int U>
+__device__ __forceinline__ void combine_rows(const u32x4* __restrict__ y, const int (&rows)[16], const float (&g)[16],
+                                             int nv_rows, int nv, int lane, u32x4* __restrict__ orow) {
+    for (int v0 = 0; v0 < nv; v0 += 64 * U) {
+        u32x4 buf[NV][U];
+#pragma unroll
+        for (int r = 0; r < NV; ++r) {
+            const u32x4* src = y + (int64_t)rows[r] * nv;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int v = v0 + u * 64 + lane;
+                if (r < nv_rows && v < nv) buf[r][u] = src[v];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int v = v0 + u * 64 + lane;
+            if (v >= nv) continue;
+            float acc[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+#pragma unroll
+            for (int r = 0; r < NV; ++r) {
+                if (r >= nv_rows) continue;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float lo = bf_lo(buf[r][u][i]), hi = bf_hi(buf[r][u][i]);
+                    if (GATED) {
+                        acc[2 * i] += g[r] * lo;
+                        acc[2 * i + 1] += g[r] * hi;
+                    } else {
+                        acc[2 * i] += lo;
+                        acc[2 * i + 1] += hi;
+                    }
+                }
+            }
+            u32x4 o;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = pack_bf2(acc[2 * i], acc[2 * i + 1]);
+            __builtin_nontemporal_store(o, orow + v);
+        }
+    }
+}
+
+template <bool GATED>
 __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ y, const int32_t* __restrict__ pos,
                                                       const float* __restrict__ gates, int T, int K, int H,
                                                       u32x4* __restrict__ out) {
@@ -26,42 +72,31 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ 
     const int my_pos = lane < K ? pos[t * K + lane] : -1;
     float my_g = 1.0f;
     if (GATED && lane < K) my_g = gates[t * K + lane];
-    int rows[KMAX];
-    float g[KMAX];
+    // compact the valid k in ascending order (uniform over the wave)
+    uint64_t m = __ballot(my_pos >= 0);
+    const int nv_rows = __popcll(m);
+    int rows[16];
+    float g[16];
 #pragma unroll
-    for (int k = 0; k < KMAX; ++k) {
-        rows[k] = k < K ? __shfl(my_pos, k, 64) : -1;
-        g[k] = GATED ? __shfl(my_g, k, 64) : 1.0f;
+    for (int r = 0; r < 16; ++r) {
+        const int k = m ? __builtin_ctzll(m) : 0;
+        rows[r] = __shfl(my_pos, k, 64);
+        g[r] = GATED ? __shfl(my_g, k, 64) : 1.0f;
+        m &= m - 1;
     }
     const int nv = H >> 3;
     u32x4* orow = out + t * nv;
-    for (int v = lane; v < nv; v += 64) {
-        u32x4 buf[KMAX];
-#pragma unroll
-        for (int k = 0; k < KMAX; ++k)
-            if (rows[k] >= 0) buf[k] = y[(int64_t)rows[k] * nv + v];
-        float acc[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-#pragma unroll
-        for (int k = 0; k < KMAX; ++k) {
-            if (rows[k] < 0) continue;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float lo = bf_lo(buf[k][i]), hi = bf_hi(buf[k][i]);
-                if (GATED) {
-                    acc[2 * i] += g[k] * lo;
-                    acc[2 * i + 1] += g[k] * hi;
-                } else {
-                    acc[2 * i] += lo;
-                    acc[2 * i + 1] += hi;
-                }
-            }
-        }
-        u32x4 o;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] = pack_bf2(acc[2 * i], acc[2 * i + 1]);
-        __builtin_nontemporal_store(o, orow + v);
+    if (nv_rows == 0) {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        for (int v = lane; v < nv; v += 64) __builtin_nontemporal_store(z, orow + v);
+    } else if (nv_rows <= 2) {
+        combine_rows<GATED, 2, 4>(y, rows, g, nv_rows, nv, lane, orow);
+    } else if (nv_rows <= 4) {
+        combine_rows<GATED, 4, 2>(y, rows, g, nv_rows, nv, lane, orow);
+    } else if (nv_rows <= 8) {
+        combine_rows<GATED, 8, 2>(y, rows, g, nv_rows, nv, lane, orow);
+    } else {
+        combine_rows<GATED, 16, 1>(y, rows, g, nv_rows, nv, lane, orow);
     }
 }
 
@@ -79,7 +114,7 @@ __global__ __launch_bounds__(256) void gather_kernel(const u32x4* __restrict__ d
     if (GATED && lane < K) my_g = gates[t * K + lane];
     const int nv = H >> 3;
     const u32x4* src = d_out + t * nv;
-    constexpr int U = 4;
+    constexpr int U = 8;
     for (int v0 = 0; v0 < nv; v0 += 64 * U) {
         u32x4 buf[U];
 #pragma unroll
@@ -127,11 +162,9 @@ extern "C" int moe_combine(const moe_bf16* y, const int32_t* pos, const float* g
     const u32x4* yy = (const u32x4*)y;
     u32x4* oo = (u32x4*)out;
     if (gates) {
-        if (K <= 8) combine_kernel<true, 8><<<grid, block, 0, s>>>(yy, pos, gates, T, K, H, oo);
-        else combine_kernel<true, 16><<<grid, block, 0, s>>>(yy, pos, gates, T, K, H, oo);
+        combine_kernel<true><<<grid, block, 0, s>>>(yy, pos, gates, T, K, H, oo);
     } else {
-        if (K <= 8) combine_kernel<false, 8><<<grid, block, 0, s>>>(yy, pos, gates, T, K, H, oo);
-        else combine_kernel<false, 16><<<grid, block, 0, s>>>(yy, pos, gates, T, K, H, oo);
+        combine_kernel<false><<<grid, block, 0, s>>>(yy, pos, gates, T, K, H, oo);
     }
     return moe_host::launch_status();
 }
