@@ -40,7 +40,8 @@
 
 namespace moe {
 
-constexpr int kGroupM = 4;
+constexpr int kGroupM = 4;  // row-tiled GEMMs: m-tiles per group of the tile order
+constexpr int kGroupN = 4;  // weight gradient: n-tiles per group of the tile order
 constexpr int kMaxGroups = 512;
 constexpr int kLdsBudget = 128 * 1024;  // LDS per workgroup for the stage ring
 
@@ -279,9 +280,11 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
         return wn * (BN / WN) + 32 * nt;
     };
 
-    const int G = gridDim.x;
-    for (int tile = xcd_remap(blockIdx.x, G); tile < n_tiles_total; tile += G) {
-        // ---- decode the tile ----
+    // ---- tile decode (identical in every lane) ----
+    struct TileDesc {
+        int j, row0, valid, ni, mi_w, KT;
+    };
+    auto decode = [&](int tile) {
         int j, row0 = 0, valid = 0, ni = 0, mi_w = 0, KT;
         if (SCHED == SCHED_ROWS) {
             const int MT = s_start[EL];
@@ -303,165 +306,219 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
             KT = (p.two_seg ? 2 * p.Kd : p.Kd) / BK;
         } else {
             j = s_start[tile / tiles_n];
+            // within a group: runs of kGroupN output-column tiles, rows fastest,
+            // so the tiles in flight on one XCD share few A and B column blocks
             const int r = tile % tiles_n;
-            mi_w = r % tiles_mw;
-            ni = r / tiles_mw;
+            const int tnn = tiles_n / tiles_mw;
+            const int g = r / (kGroupN * tiles_mw);
+            const int gw = min(kGroupN, tnn - g * kGroupN);
+            const int idx = r - g * kGroupN * tiles_mw;
+            ni = g * kGroupN + idx % gw;
+            mi_w = idx / gw;
             row0 = s_off[j];
             valid = s_off[j + 1] - row0;
             KT = (valid + BK - 1) / BK;
         }
-        // the decode is identical in every lane: tell the compiler so that the
-        // buffer descriptors below live in scalar registers
-        j = __builtin_amdgcn_readfirstlane(j);
-        row0 = __builtin_amdgcn_readfirstlane(row0);
-        valid = __builtin_amdgcn_readfirstlane(valid);
-        ni = __builtin_amdgcn_readfirstlane(ni);
-        mi_w = __builtin_amdgcn_readfirstlane(mi_w);
-        KT = __builtin_amdgcn_readfirstlane(KT);
+        // tell the compiler the decode is uniform, so that the buffer
+        // descriptors built from it live in scalar registers
+        TileDesc d;
+        d.j = __builtin_amdgcn_readfirstlane(j);
+        d.row0 = __builtin_amdgcn_readfirstlane(row0);
+        d.valid = __builtin_amdgcn_readfirstlane(valid);
+        d.ni = __builtin_amdgcn_readfirstlane(ni);
+        d.mi_w = __builtin_amdgcn_readfirstlane(mi_w);
+        d.KT = __builtin_amdgcn_readfirstlane(KT);
+        return d;
+    };
 
-        // ---- LDS-direct loader: load q fills 1 KiB of the stage ----
-        // Every bound that matters (ragged rows, matrix end) sits in the
-        // per-lane offset, which the buffer descriptor checks; out-of-range
-        // lanes read zero.
-        const i32x4 rsA = make_srd(p.a + (int64_t)row0 * p.lda,
-                                   SCHED == SCHED_ROWS ? (uint32_t)(valid * p.lda * 2) : 0u);
-        // Load u (0..LPW-1) of this wave for stage kt into LDS slot `slot`.  A
-        // stage past the end of the contraction (live == false) is loaded from
-        // the out-of-range offset: zeros, no memory traffic, and the same number
-        // of loads per stage, so the vmcnt bookkeeping stays fixed.
-        auto load_one = [&](int kt, int slot, int u, bool live) {
-            const uint32_t sA = lds_addr(smem) + slot * TL::kStage;
-            const uint32_t sB = sA + TL::kABytes;
-            const int k0 = kt * BK;
-            // re-materialise the lane terms each load (cheap adds) rather than
-            // keeping one hoisted offset per load alive across the loop
-            uint32_t la0 = lt_a0, la1 = lt_a1, lb0 = lt_b0, lb1 = lt_b1;
-            asm volatile("" : "+v"(la0), "+v"(la1), "+v"(lb0), "+v"(lb1));
-            {
-                // load u of wave w fills A block u*W + w (u < LA) or B block
-                // (u - LA)*W + w: A/B and the sub-tile follow from u at compile
-                // time, so the stream of loads has no branches
-                constexpr int LA = TL::kALoads / TL::kWaves;
-                constexpr bool kSubPerLoad = LY::kLoadsPerSub == TL::kWaves;
-                // MN blocks: sub-tile (64 columns) and 8-k-row group of block v*W + w
-                auto mn_sub = [&](int v) { return kSubPerLoad ? v : (v * TL::kWaves + wave) / LY::kLoadsPerSub; };
-                auto mn_kr = [&](int v) { return kSubPerLoad ? wave : (v * TL::kWaves + wave) % LY::kLoadsPerSub; };
-                if (u < LA) {
-                    const int q = u * TL::kWaves + wave;
-                    if (SCHED == SCHED_ROWS) {
-                        const uint32_t lt = LY::kc_period(q) ? la1 : la0;
-                        const uint32_t voff = lt + (uint32_t)((q * LY::kRowsPerLoad * p.lda + k0) * 2);
-                        lds_load16(rsA, sA + q * 1024, live ? voff : kOOB);
-                    } else {
-                        const i32x4 r = make_srd(p.a + (int64_t)(row0 + k0) * p.lda,
-                                                 (uint32_t)(max(0, min(BK, valid - k0)) * p.lda * 2));
-                        const int col = mi_w * BM + mn_sub(u) * 64;
-                        const uint32_t voff = col < p.M ? la0 + (uint32_t)((mn_kr(u) * 8 * p.lda + col) * 2) : kOOB;
-                        lds_load16(r, sA + q * 1024, live ? voff : kOOB);
-                    }
+    // ---- issue cursor: the tile and stage whose loads are issued next ----
+    // It walks this workgroup's tiles (tile0, tile0 + G, ...) S-1 stages ahead
+    // of the MFMAs, skipping tiles without stages, so the LDS ring runs on
+    // across tile boundaries: a tile's first stages load during the previous
+    // tile's last stages and its epilogue.
+    const int G = gridDim.x;
+    const int tile0 = xcd_remap(blockIdx.x, G);
+    int itile = tile0, ik = 0;
+    TileDesc ic = {0, 0, 0, 0, 0, 0};
+    // buffer descriptors of the issue cursor's tile (row-tiled GEMMs), built
+    // once per tile: the A rows, and the B weight of each half / segment
+    i32x4 c_srdA = {0, 0, 0, 0}, c_srdB0 = {0, 0, 0, 0}, c_srdB1 = {0, 0, 0, 0};
+    // weight gradient: the group's first A and B rows
+    uint64_t c_rowA = 0, c_rowB = 0;
+    auto seek = [&]() {
+        for (; itile < n_tiles_total; itile += G) {
+            ic = decode(itile);
+            if (ic.KT > 0) break;
+        }
+        if (SCHED == SCHED_ROWS && itile < n_tiles_total) {
+            c_srdA = make_srd(p.a + (int64_t)ic.row0 * p.lda, (uint32_t)(ic.valid * p.lda * 2));
+            if (LB == LAY_MN) {
+                const uint32_t range = (uint32_t)(p.Kd * p.ldw * 2);
+                c_srdB0 = make_srd(p.w0 + (int64_t)ic.j * p.w_stride, range);
+                if (EPI == EPI_SWIGLU) c_srdB1 = make_srd(p.w1 + (int64_t)ic.j * p.w_stride, range);
+            } else {
+                const int n0 = ic.ni * BN;
+                const uint32_t range = (uint32_t)(min(BN, p.N - n0) * p.ldw * 2);
+                c_srdB0 = make_srd(p.w0 + (int64_t)ic.j * p.w_stride + (int64_t)n0 * p.ldw, range);
+                if (p.two_seg) c_srdB1 = make_srd(p.w1 + (int64_t)ic.j * p.w_stride + (int64_t)n0 * p.ldw, range);
+            }
+            // opaque from here on: kept in SGPRs rather than rebuilt from the
+            // tile indices in every stage
+            asm volatile("" : "+s"(c_srdA), "+s"(c_srdB0), "+s"(c_srdB1));
+        }
+        if (SCHED == SCHED_WGRAD && itile < n_tiles_total) {
+            c_rowA = (uint64_t)(p.a + (int64_t)ic.row0 * p.lda);
+            c_rowB = (uint64_t)(p.b + (int64_t)ic.row0 * p.ldb);
+            asm volatile("" : "+s"(c_rowA), "+s"(c_rowB));
+        }
+    };
+    auto advance = [&]() {
+        if (itile < n_tiles_total && ++ik >= ic.KT) {
+            ik = 0;
+            itile += G;
+            seek();
+        }
+    };
+    seek();
+
+    // Load u (0..LPW-1) of this wave for stage kt of the issue cursor's tile
+    // into LDS slot `slot`.  With live == false (no tile left) it loads from
+    // the out-of-range offset: zeros, no memory traffic, and the same number
+    // of loads per stage, so the vmcnt bookkeeping stays fixed.
+    auto load_one = [&](int kt, int slot, int u, bool live) {
+        const uint32_t sA = lds_addr(smem) + slot * TL::kStage;
+        const uint32_t sB = sA + TL::kABytes;
+        const int k0 = kt * BK;
+        // re-materialise the lane terms each load (cheap adds) rather than
+        // keeping one hoisted offset per load alive across the loop
+        uint32_t la0 = lt_a0, la1 = lt_a1, lb0 = lt_b0, lb1 = lt_b1;
+        asm volatile("" : "+v"(la0), "+v"(la1), "+v"(lb0), "+v"(lb1));
+        {
+            // load u of wave w fills A block u*W + w (u < LA) or B block
+            // (u - LA)*W + w: A/B and the sub-tile follow from u at compile
+            // time, so the stream of loads has no branches
+            constexpr int LA = TL::kALoads / TL::kWaves;
+            constexpr bool kSubPerLoad = LY::kLoadsPerSub == TL::kWaves;
+            // MN blocks: sub-tile (64 columns) and 8-k-row group of block v*W + w
+            auto mn_sub = [&](int v) { return kSubPerLoad ? v : (v * TL::kWaves + wave) / LY::kLoadsPerSub; };
+            auto mn_kr = [&](int v) { return kSubPerLoad ? wave : (v * TL::kWaves + wave) % LY::kLoadsPerSub; };
+            if (u < LA) {
+                const int q = u * TL::kWaves + wave;
+                if (SCHED == SCHED_ROWS) {
+                    const uint32_t lt = LY::kc_period(q) ? la1 : la0;
+                    const uint32_t voff = lt + (uint32_t)((q * LY::kRowsPerLoad * p.lda + k0) * 2);
+                    lds_load16(c_srdA, sA + q * 1024, live ? voff : kOOB);
                 } else {
-                    const int q = (u - LA) * TL::kWaves + wave;
-                    if (SCHED == SCHED_WGRAD) {
-                        const i32x4 r = make_srd(p.b + (int64_t)(row0 + k0) * p.ldb,
-                                                 (uint32_t)(max(0, min(BK, valid - k0)) * p.ldb * 2));
-                        const int col = ni * BN + mn_sub(u - LA) * 64;
-                        const uint32_t voff = col < p.N ? lb0 + (uint32_t)((mn_kr(u - LA) * 8 * p.ldb + col) * 2) : kOOB;
-                        lds_load16(r, sB + q * 1024, live ? voff : kOOB);
-                    } else if (LB == LAY_MN) {
-                        // weight [Kd][ldw], N contiguous: [BK][64] sub-tiles
-                        const int sub = mn_sub(u - LA);
-                        const uint16_t* w;
-                        int col;
-                        if (EPI == EPI_SWIGLU) {
-                            constexpr int HS = BN / 128;  // sub-tiles per half
-                            w = sub < HS ? p.w0 : p.w1;
-                            col = ni * (BN / 2) + (sub % HS) * 64;
-                        } else {
-                            w = p.w0;
-                            col = ni * BN + sub * 64;
-                        }
-                        const i32x4 r = make_srd(w + (int64_t)j * p.w_stride, (uint32_t)(p.Kd * p.ldw * 2));
-                        const uint32_t voff =
-                            col < p.N ? lb0 + (uint32_t)(((mn_kr(u - LA) * 8 + k0) * p.ldw + col) * 2) : kOOB;
-                        lds_load16(r, sB + q * 1024, live ? voff : kOOB);
+                    const i32x4 r = make_srd((const uint16_t*)c_rowA + (int64_t)k0 * p.lda,
+                                             (uint32_t)(max(0, min(BK, ic.valid - k0)) * p.lda * 2));
+                    const int col = ic.mi_w * BM + mn_sub(u) * 64;
+                    const uint32_t voff = col < p.M ? la0 + (uint32_t)((mn_kr(u) * 8 * p.lda + col) * 2) : kOOB;
+                    lds_load16(r, sA + q * 1024, live ? voff : kOOB);
+                }
+            } else {
+                const int q = (u - LA) * TL::kWaves + wave;
+                if (SCHED == SCHED_WGRAD) {
+                    const i32x4 r = make_srd((const uint16_t*)c_rowB + (int64_t)k0 * p.ldb,
+                                             (uint32_t)(max(0, min(BK, ic.valid - k0)) * p.ldb * 2));
+                    const int col = ic.ni * BN + mn_sub(u - LA) * 64;
+                    const uint32_t voff = col < p.N ? lb0 + (uint32_t)((mn_kr(u - LA) * 8 * p.ldb + col) * 2) : kOOB;
+                    lds_load16(r, sB + q * 1024, live ? voff : kOOB);
+                } else if (LB == LAY_MN) {
+                    // weight [Kd][ldw], N contiguous: [BK][64] sub-tiles
+                    const int sub = mn_sub(u - LA);
+                    i32x4 r;
+                    int col;
+                    if (EPI == EPI_SWIGLU) {
+                        constexpr int HS = BN / 128;  // sub-tiles per half
+                        r = sub < HS ? c_srdB0 : c_srdB1;
+                        col = ic.ni * (BN / 2) + (sub % HS) * 64;
                     } else {
-                        // weight [N][Kd], contraction contiguous; second segment from w1
-                        const bool seg1 = p.two_seg && k0 >= p.Kd;
-                        const uint16_t* w = seg1 ? p.w1 : p.w0;
-                        const int kk0 = seg1 ? k0 - p.Kd : k0;
-                        const int n0 = ni * BN;
-                        const i32x4 r = make_srd(w + (int64_t)j * p.w_stride + (int64_t)n0 * p.ldw,
-                                                 (uint32_t)(min(BN, p.N - n0) * p.ldw * 2));
-                        const uint32_t lt = LY::kc_period(q) ? lb1 : lb0;
-                        const uint32_t voff = lt + (uint32_t)((q * LY::kRowsPerLoad * p.ldw + kk0) * 2);
-                        lds_load16(r, sB + q * 1024, live ? voff : kOOB);
+                        r = c_srdB0;
+                        col = ic.ni * BN + sub * 64;
                     }
+                    const uint32_t voff =
+                        col < p.N ? lb0 + (uint32_t)(((mn_kr(u - LA) * 8 + k0) * p.ldw + col) * 2) : kOOB;
+                    lds_load16(r, sB + q * 1024, live ? voff : kOOB);
+                } else {
+                    // weight [N][Kd], contraction contiguous; second segment from w1
+                    const bool seg1 = p.two_seg && k0 >= p.Kd;
+                    const i32x4 r = seg1 ? c_srdB1 : c_srdB0;
+                    const int kk0 = seg1 ? k0 - p.Kd : k0;
+                    const uint32_t lt = LY::kc_period(q) ? lb1 : lb0;
+                    const uint32_t voff = lt + (uint32_t)((q * LY::kRowsPerLoad * p.ldw + kk0) * 2);
+                    lds_load16(r, sB + q * 1024, live ? voff : kOOB);
                 }
             }
-        };
-        auto issue = [&](int kt, int slot, bool live) {
+        }
+    };
+    auto issue = [&](int kt, int slot, bool live) {
 #pragma unroll
-            for (int u = 0; u < LPW; ++u) load_one(kt, slot, u, live);
-        };
+        for (int u = 0; u < LPW; ++u) load_one(kt, slot, u, live);
+    };
 
-        f32x16 acc[MTW][NTW];
+    f32x16 acc[MTW][NTW];
+    // Two fragment buffers: the fragments of k16 step s+1 are read while
+    // the MFMAs of step s run.
+    bf16x8 af[2][MTW], bfv[2][NTW];
+    auto load_frags = [&](int slot, int kk, int buf) {
+        const uint8_t* sA = smem + slot * TL::kStage;
+        const uint8_t* sB = sA + TL::kABytes;
+#pragma unroll
+        for (int mt = 0; mt < MTW; ++mt) {
+            const int rb = wm * (BM / WM) + mt * 32;
+            af[buf][mt] = SCHED == SCHED_ROWS ? LY::frag_kc(sA, rb, kk, lane) : LY::frag_mn(sA, rb, kk, lane);
+        }
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) {
+            const int cb = col_of(nt);
+            bfv[buf][nt] = (SCHED == SCHED_ROWS && LB == LAY_KC) ? LY::frag_kc(sB, cb, kk, lane)
+                                                                 : LY::frag_mn(sB, cb, kk, lane);
+        }
+    };
+    // LDS reads one fragment set takes: a KC fragment is one 16-byte read,
+    // an MN fragment two transposing 8-byte reads
+    constexpr int kReadsA = SCHED == SCHED_ROWS ? MTW : 2 * MTW;
+    constexpr int kReadsB = (SCHED == SCHED_ROWS && LB == LAY_KC) ? NTW : 2 * NTW;
+    constexpr int kReads = kReadsA + kReadsB;
+    constexpr int kMfma = MTW * NTW;
+    static_assert(KK == 2, "two k16 steps per stage");
+
+    // Pipeline over a ring of S LDS stages, loads S-1 stages ahead.  The k16
+    // steps of a stage issue the loads of the issue cursor's stage (one every
+    // few MFMAs) and read the next step's fragments (one LDS read per MFMA), so
+    // LDS-direct writes, fragment reads and MFMAs overlap instead of coming in
+    // bursts.  Every stage issues the same number of loads (zero loads once no
+    // tile is left), so "stages up to gs+2 have landed" is a fixed vmcnt of S-3
+    // stages at the end of stage gs.  The barrier after it publishes stage gs+2
+    // (first read in the last step of stage gs+1) and frees the slot of stage
+    // gs, which stage gs+1's loads refill.
+    constexpr int kWaitLoads = (S - 3) * LPW;
+#pragma unroll
+    for (int t = 0; t < S - 1; ++t) {
+        issue(ik, t, itile < n_tiles_total);
+        advance();
+    }
+    wait_vmcnt<kWaitLoads>();
+    __syncthreads();
+
+    unsigned gs = 0;  // global stage index of this workgroup; its LDS slot is gs % S
+    for (int tile = tile0; tile < n_tiles_total; tile += G) {
+        const TileDesc cd = decode(tile);
+        const int j = cd.j, row0 = cd.row0, valid = cd.valid, ni = cd.ni, mi_w = cd.mi_w, KT = cd.KT;
 #pragma unroll
         for (int a = 0; a < MTW; ++a)
 #pragma unroll
             for (int b = 0; b < NTW; ++b) acc[a][b] = f32x16{};
-
-        // Two fragment buffers: the fragments of k16 step s+1 are read while
-        // the MFMAs of step s run.
-        bf16x8 af[2][MTW], bfv[2][NTW];
-        auto load_frags = [&](int slot, int kk, int buf) {
-            const uint8_t* sA = smem + slot * TL::kStage;
-            const uint8_t* sB = sA + TL::kABytes;
-#pragma unroll
-            for (int mt = 0; mt < MTW; ++mt) {
-                const int rb = wm * (BM / WM) + mt * 32;
-                af[buf][mt] = SCHED == SCHED_ROWS ? LY::frag_kc(sA, rb, kk, lane) : LY::frag_mn(sA, rb, kk, lane);
-            }
-#pragma unroll
-            for (int nt = 0; nt < NTW; ++nt) {
-                const int cb = col_of(nt);
-                bfv[buf][nt] = (SCHED == SCHED_ROWS && LB == LAY_KC) ? LY::frag_kc(sB, cb, kk, lane)
-                                                                     : LY::frag_mn(sB, cb, kk, lane);
-            }
-        };
-        // LDS reads one fragment set takes: a KC fragment is one 16-byte read,
-        // an MN fragment two transposing 8-byte reads
-        constexpr int kReadsA = SCHED == SCHED_ROWS ? MTW : 2 * MTW;
-        constexpr int kReadsB = (SCHED == SCHED_ROWS && LB == LAY_KC) ? NTW : 2 * NTW;
-        constexpr int kReads = kReadsA + kReadsB;
-        constexpr int kMfma = MTW * NTW;
-        static_assert(KK == 2, "two k16 steps per stage");
-
-        // Pipeline over a ring of S LDS stages, loads S-1 stages ahead.  The k16
-        // steps of stage kt issue the loads of stage kt+S-1 (one every few
-        // MFMAs) and read the next step's fragments (one LDS read per MFMA), so
-        // LDS-direct writes, fragment reads and MFMAs overlap instead of coming
-        // in bursts.  Every stage issues the same number of loads (past the end
-        // they are zero loads), so "stages up to kt+2 have landed" is a fixed
-        // vmcnt of S-3 stages at the end of stage kt.  The barrier after it
-        // publishes stage kt+2 (first read in the last step of stage kt+1) and
-        // frees the slot of stage kt, which stage kt+1's loads refill.
-        constexpr int kWaitLoads = (S - 3) * LPW;
-        if (KT > 0) {
-#pragma unroll
-            for (int t = 0; t < S - 1; ++t) issue(t, t, t < KT);
-            wait_vmcnt<kWaitLoads>();
-            __syncthreads();
-            load_frags(0, 0, 0);
-        }
-        for (int kt = 0; kt < KT; ++kt) {
-            const int kn = kt + S - 1;
-            const bool live = kn < KT;
-            const int nslot = kn % S;
-            const int slot1 = (kt + 1) % S;
+        if (KT > 0) load_frags((int)(gs % S), 0, 0);
+        for (int kt = 0; kt < KT; ++kt, ++gs) {
+            const bool live = itile < n_tiles_total;
+            const int kn = ik;  // the issue cursor's stage, loaded into the slot of gs-1
+            const int nslot = (int)((gs + S - 1) % S);
+            const int slot = (int)(gs % S), slot1 = (int)((gs + 1) % S);
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) {
-                // next step: (kt, 1) or (kt+1, 0)
-                if (kk + 1 < KK) load_frags(kt % S, kk + 1, (kk + 1) & 1);
+                // next step: (gs, 1) or (gs+1, 0)
+                if (kk + 1 < KK) load_frags(slot, kk + 1, (kk + 1) & 1);
                 else load_frags(slot1, 0, (kk + 1) & 1);
 #pragma unroll
                 for (int mt = 0; mt < MTW; ++mt) {
@@ -485,11 +542,10 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
+            advance();
             wait_vmcnt<kWaitLoads>();
             __syncthreads();
         }
-        wait_vmcnt<0>();  // zero loads of the stages past the end
-        __syncthreads();  // the next tile's first loads overwrite the ring
 
         // ---- epilogue: lane holds row (l%32) and columns 8*j4 + 4*(l/32) + 0..3 ----
         const int cq = 4 * (lane >> 5);
@@ -508,7 +564,10 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
                         if (n < p.N) {
                             f32x4 v = {acc[mt][nt][4 * j4], acc[mt][nt][4 * j4 + 1], acc[mt][nt][4 * j4 + 2],
                                        acc[mt][nt][4 * j4 + 3]};
-                            __builtin_nontemporal_store(v, (f32x4*)(orow + n));
+                            // a plain store: L2 merges the 32-byte pieces of a row
+                            // into whole lines (a non-temporal store doubled the
+                            // HBM write traffic)
+                            *(f32x4*)(orow + n) = v;
                         }
                     }
                 continue;
@@ -571,6 +630,7 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
             }
         }
     }
+    wait_vmcnt<0>();  // the zero loads issued past the last tile
 }
 
 // Whether tiles of ALT rows beat tiles of BM rows on this call's row counts:
