@@ -59,9 +59,11 @@ def lib():
         L.oracle_bwd_down.argtypes = [_p, _p, _p, _p, _i, _i, _i, _l, _p, _l, _p]
         L.oracle_bwd_up.argtypes = [_p, _p, _p, _p, _i, _i, _i, _l, _p, _l, _p]
         L.oracle_wgrad.argtypes = [_p, _l, _p, _l, _p, _i, _i, _i, _l, _p, _i, _p, _i, _p]
+        L.oracle_gate_grad.argtypes = [_p, _p, _p, _i, _i, _i, _p]
+        L.oracle_route_backward.argtypes = [_p, _p, _p, _i, _i, _i, _p]
         for name in ("oracle_route", "oracle_permute", "oracle_expert_up", "oracle_expert_down",
                      "oracle_combine", "oracle_bwd_gather", "oracle_bwd_down", "oracle_bwd_up",
-                     "oracle_wgrad"):
+                     "oracle_wgrad", "oracle_gate_grad", "oracle_route_backward"):
             getattr(L, name).restype = None
     return _lib
 
@@ -197,6 +199,25 @@ def wgrad(A, lda, B, ldb, offsets, M, N, cap, groups=None, cols=None, out=None):
     return dw
 
 
+def gate_grad(d_out, y, pos):
+    """dgates f32[T,K] = <d_out[t], y[pos[t,k]]> for local pairs, 0 for pos < 0."""
+    d_out, y, pos = _c(d_out, np.uint16), _c(y, np.uint16), _c(pos, np.int32)
+    T, K = pos.shape
+    H = d_out.shape[1]
+    dg = np.empty((T, K), np.float32)
+    lib().oracle_gate_grad(_ptr(d_out), _ptr(y), _ptr(pos), T, K, H, _ptr(dg))
+    return dg
+
+
+def route_backward(topk_idx, gates, dgates, E):
+    """dlogits f32[T,E]: the gradient of the scores through the renormalised top-K gates."""
+    topk_idx, gates, dgates = _c(topk_idx, np.int32), _c(gates, np.float32), _c(dgates, np.float32)
+    T, K = topk_idx.shape
+    dl = np.empty((T, E), np.float32)
+    lib().oracle_route_backward(_ptr(topk_idx), _ptr(gates), _ptr(dgates), T, E, K, _ptr(dl))
+    return dl
+
+
 def forward(inp: dict, e_begin: int, e_local: int, K: int, cap: int):
     """The whole oracle forward chain on one set of inputs (small sizes)."""
     idx, g = route(inp["logits"], K)
@@ -219,4 +240,7 @@ def backward(inp: dict, fwd: dict, cap: int):
     dwg = wgrad(fwd["x_perm"], H, dab, 2 * F, fwd["offsets"], H, F, cap)
     dwu = wgrad(fwd["x_perm"], H, dab[:, F:].copy(), F, fwd["offsets"], H, F, cap)
     dwd = wgrad(fwd["h"], F, dy, H, fwd["offsets"], F, H, cap)
-    return dict(dy_perm=dy, dab=dab, dx_perm=dxp, dx=dx, dw_gate=dwg, dw_up=dwu, dw_down=dwd)
+    dg = gate_grad(inp["d_out"], fwd["y"], fwd["pos"])
+    dl = route_backward(fwd["topk_idx"], fwd["gates"], dg, inp["logits"].shape[1])
+    return dict(dy_perm=dy, dab=dab, dx_perm=dxp, dx=dx, dw_gate=dwg, dw_up=dwu, dw_down=dwd, dgates=dg,
+                dlogits=dl)

@@ -375,3 +375,49 @@ void oracle_wgrad(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb
         }
     }
 }
+
+/* ---- R1: gate gradient --------------------------------------------------
+ * The combine is out[t] = sum_k gate[t,k] * y[pos[t,k]], so the gradient of
+ * a gate is the dot product of the output gradient with the expert output it
+ * weighted: dgates[t,k] = sum_{c<H} dOut[t,c] * y[pos[t,k],c] (c ascending,
+ * fp32 running sum from +0).  A non-local pair gets 0: its expert and y row
+ * are on another GPU, and the gate's full gradient is the sum of the per-GPU
+ * parts, exactly one of which is non-zero.
+ */
+void oracle_gate_grad(const uint16_t* d_out, const uint16_t* y, const int32_t* pos, int T, int K, int H,
+                      float* dgates) {
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; ++t) {
+        for (int k = 0; k < K; ++k) {
+            int32_t r = pos[(int64_t)t * K + k];
+            float acc = 0.0f;
+            if (r >= 0)
+                for (int c = 0; c < H; ++c) acc += bf(d_out[(int64_t)t * H + c]) * bf(y[(int64_t)r * H + c]);
+            dgates[(int64_t)t * K + k] = acc;
+        }
+    }
+}
+
+/* ---- R2: router backward --------------------------------------------------
+ * The gates are the chosen experts' softmax probabilities renormalised over
+ * the K choices, which equals the softmax of the chosen scores alone (the
+ * full normaliser cancels); the choice itself is piecewise constant in the
+ * scores and contributes nothing.  So, with g = gates[t,:], dg = dgates[t,:]:
+ *   sum = sum_j g_j * dg_j                      (j ascending, fp32)
+ *   dlogits[t, idx[t,k]] = g_k * (dg_k - sum)
+ * and dlogits[t,e] = 0 for every expert e not chosen.  The map is linear in
+ * dg, so per-GPU partial gate gradients give per-GPU partial dlogits.
+ */
+void oracle_route_backward(const int32_t* topk_idx, const float* gates, const float* dgates, int T, int E,
+                           int K, float* dlogits) {
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; ++t) {
+        const float* g = gates + (int64_t)t * K;
+        const float* dg = dgates + (int64_t)t * K;
+        float sum = 0.0f;
+        for (int j = 0; j < K; ++j) sum += g[j] * dg[j];
+        float* row = dlogits + (int64_t)t * E;
+        for (int e = 0; e < E; ++e) row[e] = 0.0f;
+        for (int k = 0; k < K; ++k) row[topk_idx[(int64_t)t * K + k]] = g[k] * (dg[k] - sum);
+    }
+}

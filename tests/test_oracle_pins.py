@@ -436,3 +436,81 @@ def test_backward_finite_difference_direction():
     fd = (np.sum(dO * layer(X0 + eps * v)) - np.sum(dO * layer(X0 - eps * v))) / (2 * eps)
     ad = np.sum(f(bwd["dx"]) * v)
     assert abs(ad - fd) <= 2 ** -5 * abs(fd)
+
+
+# ---------------------------------------------------------------- router backward
+
+def test_gate_grad_vs_fp64_dot():
+    """dgates[t,k] = <dOut[t], y[pos[t,k]]> within the fp32 running-sum bound; pos < 0 gives exactly 0."""
+    rng = np.random.default_rng(81)
+    T, K, H, R = 24, 3, 200, 40
+    d_out = rand_bf16(rng, (T, H))
+    y = rand_bf16(rng, (R, H), std=0.5)
+    pos = rng.integers(0, R, (T, K)).astype(np.int32)
+    pos[rng.random((T, K)) < 0.3] = -1
+    got = oracle.gate_grad(d_out, y, pos).astype(np.float64)
+    D, Y = f(d_out), f(y)
+    for t in range(T):
+        for k in range(K):
+            r = pos[t, k]
+            if r < 0:
+                assert got[t, k] == 0.0
+                continue
+            exact = float(np.dot(D[t], Y[r]))
+            assert abs(got[t, k] - exact) <= gamma(H) * float(np.sum(np.abs(D[t] * Y[r]))) + 1e-30
+
+
+def _fp64_gates(s, K):
+    """Router forward in fp64 from its definition: softmax over all E, top-K, renormalise."""
+    p = scipy.special.softmax(s)
+    idx = np.lexsort((np.arange(len(s)), -s))[:K]
+    return idx, p[idx] / np.sum(p[idx])
+
+
+def test_route_backward_vs_finite_differences():
+    """dlogits matches a central difference of sum_k dg_k * g_k(s) of the fp64 router forward."""
+    rng = np.random.default_rng(82)
+    T, E, K = 12, 9, 3
+    # scores at least 0.05 apart, so a 1e-6 step never changes the top-K choice
+    s = np.stack([rng.permutation(E) * 0.05 + rng.standard_normal() for _ in range(T)]).astype(np.float32)
+    dg = rng.standard_normal((T, K)).astype(np.float32)
+    idx, g = oracle.route(s, K)
+    dl = oracle.route_backward(idx, g, dg, E).astype(np.float64)
+    h = 1e-6
+    for t in range(T):
+        st = s[t].astype(np.float64)
+        i0, _ = _fp64_gates(st, K)
+        assert np.array_equal(i0, idx[t])
+
+        def loss(v):
+            i, gg = _fp64_gates(v, K)
+            assert np.array_equal(i, i0)
+            return float(np.dot(dg[t].astype(np.float64), gg))
+
+        for e in range(E):
+            d = np.zeros(E)
+            d[e] = h
+            fd = (loss(st + d) - loss(st - d)) / (2 * h)
+            assert abs(dl[t, e] - fd) <= 1e-5 + 1e-4 * abs(fd), (t, e, dl[t, e], fd)
+
+
+def test_route_backward_invariants():
+    """Rows sum to 0; experts not chosen get exactly 0; K=1 gives exactly 0; a constant added to
+    every dg_k changes nothing (the gates sum to 1); dlogits is linear in dgates."""
+    rng = np.random.default_rng(83)
+    T, E, K = 30, 16, 4
+    s = rng.standard_normal((T, E)).astype(np.float32)
+    idx, g = oracle.route(s, K)
+    dg = rng.standard_normal((T, K)).astype(np.float32)
+    dl = oracle.route_backward(idx, g, dg, E)
+    chosen = np.zeros((T, E), bool)
+    np.put_along_axis(chosen, idx, True, axis=1)
+    assert np.all(dl[~chosen] == 0.0)
+    scale = np.sum(np.abs(dl), axis=1) + np.sum(np.abs(g * dg), axis=1)
+    assert np.all(np.abs(np.sum(dl.astype(np.float64), axis=1)) <= 1e-6 * scale)
+    dl_shift = oracle.route_backward(idx, g, dg + np.float32(3.0), E)
+    assert np.allclose(dl_shift, dl, atol=1e-5)
+    dl2 = oracle.route_backward(idx, g, dg * np.float32(2.0), E)
+    assert np.allclose(dl2, 2 * dl, rtol=1e-6, atol=1e-7)
+    i1, g1 = oracle.route(s, 1)
+    assert np.all(oracle.route_backward(i1, g1, dg[:, :1], E) == 0.0)
