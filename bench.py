@@ -57,7 +57,10 @@ def algorithmic_work(shape, R, T_act, n_active):
     w["expert_down"] = dict(bytes=2 * n_active * F * H + 2 * R * F + 2 * R * H, flops=2 * R * F * H)
     w["combine"] = dict(bytes=2 * H * R + 8 * T * K + 2 * H * T, flops=0)
     if shape.backward:
-        w["bwd_gather"] = dict(bytes=2 * H * T_act + 2 * H * R + 8 * T * K, flops=0)
+        # gather + gate gradient: d_out rows read once, dy_perm written, y rows read, pos/gates in, dgates out
+        w["bwd_gather"] = dict(bytes=2 * H * T_act + 2 * H * R + 2 * H * R + 12 * T * K, flops=2 * R * H)
+        # router backward: topk_idx, gates, dgates in, dense dlogits out
+        w["route_bwd"] = dict(bytes=12 * T * K + 4 * T * E, flops=0)
         w["bwd_down_dgrad"] = dict(bytes=2 * n_active * F * H + 2 * R * H + 4 * R * 2 * F,
                                    flops=2 * R * H * F)
         w["bwd_up_dgrad"] = dict(bytes=2 * n_active * 2 * H * F + 2 * R * 2 * F + 2 * R * H,
@@ -165,7 +168,10 @@ def main():
     if shape.backward:
         H, F, EL, cap = shape.H, shape.F, shape.EL, buf.cap
         steps += [
-            ("bwd_gather", lambda: _lib.moe_gather(dev["d_out"], buf.pos, buf.gates, buf.dy_perm)),
+            ("bwd_gather", lambda: _lib.moe_gather_gate_grad(dev["d_out"], buf.pos, buf.gates, buf.y, buf.dy_perm,
+                                                             buf.dgates)),
+            ("route_bwd", lambda: _lib.moe_route_backward(buf.topk_idx, buf.gates, buf.dgates, shape.E,
+                                                          buf.dlogits)),
             ("bwd_down_dgrad", lambda: _lib.moe_grouped_gemm(buf.dy_perm, dev["w_down"], None, 1, buf.offsets, H,
                                                              F, cap, buf.dab, epilogue=_lib.MOE_EPI_SWIGLU_BWD,
                                                              ab=buf.ab)),

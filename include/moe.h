@@ -81,6 +81,22 @@ int moe_abi_version(void);
 int moe_route(const float* logits, int T, int E, int K,
               int32_t* topk_idx, float* gates, moe_stream stream);
 
+/*
+ * Router backward (second half): the gradient of the routing scores through
+ * the renormalised top-K gates of moe_route.  The gates are the softmax of the
+ * chosen scores alone (the full softmax normaliser cancels in the
+ * renormalisation) and the top-K choice is piecewise constant, so for the
+ * chosen expert e = topk_idx[t,k]:
+ *   dlogits[t,e] = gates[t,k] * (dgates[t,k] - sum_j gates[t,j]*dgates[t,j])
+ * (sum over j ascending, fp32) and dlogits[t,e] = 0 for the other experts.
+ * Linear in dgates, so per-GPU partial gate gradients give per-GPU partial
+ * score gradients that sum to the full one.
+ *   topk_idx int32 [T,K], gates fp32 [T,K] (from moe_route);
+ *   dgates fp32 [T,K] (from moe_gather_gate_grad);  dlogits fp32 [T,E] out.
+ */
+int moe_route_backward(const int32_t* topk_idx, const float* gates, const float* dgates,
+                       int T, int E, int K, float* dlogits, moe_stream stream);
+
 /* Bytes of workspace moe_permute needs for these sizes. */
 size_t moe_permute_workspace_size(int T, int K, int e_local);
 
@@ -120,6 +136,23 @@ int moe_permute(const int32_t* topk_idx, int T, int K, int e_begin, int e_local,
  */
 int moe_gather(const moe_bf16* d_out, const int32_t* pos, const float* gates,
                int T, int K, int H, moe_bf16* dy_perm, moe_stream stream);
+
+/*
+ * moe_gather plus the gradient of the gates (router backward, first half).
+ * UniEP "MoE workflow": the combine weights each expert output by its gating
+ * score, so the gradient of a gate is the dot product of the token's output
+ * gradient with the expert output it weighted.  For k < K, r = pos[t,k]:
+ *   dy_perm[r]  = bf16(gates[t,k] * d_out[t])       (as moe_gather)
+ *   dgates[t,k] = sum_c d_out[t,c] * y[r,c]          (fp32, fixed order)
+ * and dgates[t,k] = 0 when pos[t,k] < 0: that expert is on another GPU, and
+ * the full gradient of a gate is the sum of the per-GPU values.
+ *   d_out bf16 [T,H];  pos int32 [T,K];  gates fp32 [T,K] (required);
+ *   y bf16 [cap_rows,H], the forward's down-projection output;
+ *   dy_perm bf16 [cap_rows,H] out;  dgates fp32 [T,K] out.
+ */
+int moe_gather_gate_grad(const moe_bf16* d_out, const int32_t* pos, const float* gates,
+                         const moe_bf16* y, int T, int K, int H, moe_bf16* dy_perm,
+                         float* dgates, moe_stream stream);
 
 /*
  * Padding-free gate/up GroupGEMM with fused SwiGLU (UniEP "MoE workflow":

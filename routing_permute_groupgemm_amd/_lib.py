@@ -23,9 +23,11 @@ SIGNATURES = {
     "moe_strerror": ([_i], ctypes.c_char_p),
     "moe_abi_version": ([], _i),
     "moe_route": ([_p, _i, _i, _i, _p, _p, _p], _i),
+    "moe_route_backward": ([_p, _p, _p, _i, _i, _i, _p, _p], _i),
     "moe_permute_workspace_size": ([_i, _i, _i], _z),
     "moe_permute": ([_p, _i, _i, _i, _i, _p, _i, _i, _p, _p, _p, _p, _p, _p, _p, _z, _p], _i),
     "moe_gather": ([_p, _p, _p, _i, _i, _i, _p, _p], _i),
+    "moe_gather_gate_grad": ([_p, _p, _p, _p, _i, _i, _i, _p, _p, _p], _i),
     "moe_grouped_gemm_swiglu": ([_p, _p, _p, _p, _i, _i, _i, _i, _p, _p, _p], _i),
     "moe_grouped_gemm": ([_p, _i, _p, _p, _i, _p, _i, _i, _i, _i, _i, _p, _p, _i, _p], _i),
     "moe_combine": ([_p, _p, _p, _i, _i, _i, _p, _p], _i),
@@ -88,6 +90,19 @@ def moe_route(logits, K, topk_idx=None, gates=None, stream=None):
     return topk_idx, gates
 
 
+def moe_route_backward(topk_idx, gates, dgates, E, dlogits=None, stream=None):
+    _need(topk_idx, torch.int32, "topk_idx")
+    _need(gates, torch.float32, "gates")
+    _need(dgates, torch.float32, "dgates")
+    T, K = topk_idx.shape
+    if dlogits is None:
+        dlogits = torch.empty((T, E), dtype=torch.float32, device=gates.device)
+    _need(dlogits, torch.float32, "dlogits")
+    _check(load().moe_route_backward(_ptr(topk_idx), _ptr(gates), _ptr(dgates), T, E, K, _ptr(dlogits),
+                                     _stream(stream)))
+    return dlogits
+
+
 def moe_permute_workspace_size(T, K, e_local) -> int:
     return int(load().moe_permute_workspace_size(T, K, e_local))
 
@@ -138,6 +153,22 @@ def moe_gather(d_out, pos, gates, dy_perm, stream=None):
     _check(load().moe_gather(_ptr(d_out), _ptr(pos), _ptr(gates), T, K, d_out.shape[1], _ptr(dy_perm),
                              _stream(stream)))
     return dy_perm
+
+
+def moe_gather_gate_grad(d_out, pos, gates, y, dy_perm, dgates=None, stream=None):
+    """dy_perm as moe_gather, and dgates[t,k] = <d_out[t], y[pos[t,k]]> (0 for non-local pairs)."""
+    _need(d_out, torch.bfloat16, "d_out")
+    _need(pos, torch.int32, "pos")
+    _need(gates, torch.float32, "gates")
+    _need(y, torch.bfloat16, "y")
+    _need(dy_perm, torch.bfloat16, "dy_perm")
+    T, K = pos.shape
+    if dgates is None:
+        dgates = torch.empty((T, K), dtype=torch.float32, device=d_out.device)
+    _need(dgates, torch.float32, "dgates")
+    _check(load().moe_gather_gate_grad(_ptr(d_out), _ptr(pos), _ptr(gates), _ptr(y), T, K, d_out.shape[1],
+                                       _ptr(dy_perm), _ptr(dgates), _stream(stream)))
+    return dy_perm, dgates
 
 
 def moe_grouped_gemm_swiglu(x_perm, w_gate, w_up, offsets, cap_rows, h=None, ab_save=None, stream=None):

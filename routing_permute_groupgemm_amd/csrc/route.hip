@@ -79,6 +79,39 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
     }
 }
 
+// Router backward: one wave per token.  The gates are the softmax of the
+// chosen scores, so with g, dg the token's gates and gate gradients the
+// score gradient is g_k * (dg_k - sum_j g_j dg_j) at the chosen experts and 0
+// elsewhere.  The sum runs over j ascending; each lane then writes its
+// experts lane, lane + 64, ... so the row is written once, coalesced.
+__global__ __launch_bounds__(256) void route_backward_kernel(const int32_t* __restrict__ topk_idx,
+                                                             const float* __restrict__ gates,
+                                                             const float* __restrict__ dgates, int T, int E, int K,
+                                                             float* __restrict__ dlogits) {
+    const int lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    const int my_idx = lane < K ? topk_idx[t * K + lane] : -1;
+    const float my_g = lane < K ? gates[t * K + lane] : 0.0f;
+    const float my_dg = lane < K ? dgates[t * K + lane] : 0.0f;
+    float sum = 0.0f;
+    for (int j = 0; j < K; ++j) sum += __shfl(my_g, j, 64) * __shfl(my_dg, j, 64);
+    const float my_val = my_g * (my_dg - sum);
+    float* row = dlogits + t * E;
+    for (int e0 = 0; e0 < E; e0 += 64) {
+        const int e = e0 + lane;
+        float v = 0.0f;
+        for (int k = 0; k < K; ++k) {
+            // both shuffles run on the whole wave (a shuffle under a lane-varying
+            // condition would read from inactive source lanes)
+            const int ik = __shfl(my_idx, k, 64);
+            const float vk = __shfl(my_val, k, 64);
+            if (ik == e) v = vk;
+        }
+        if (e < E) row[e] = v;
+    }
+}
+
 }  // namespace moe
 
 extern "C" int moe_route(const float* logits, int T, int E, int K, int32_t* topk_idx, float* gates,
@@ -104,6 +137,22 @@ extern "C" int moe_route(const float* logits, int T, int E, int K, int32_t* topk
         case 7: route_kernel<7><<<grid, block, 0, s>>>(logits, T, E, K, topk_idx, gates); break;
         default: route_kernel<8><<<grid, block, 0, s>>>(logits, T, E, K, topk_idx, gates); break;
     }
+    return moe_host::launch_status();
+}
+
+extern "C" int moe_route_backward(const int32_t* topk_idx, const float* gates, const float* dgates, int T, int E,
+                                  int K, float* dlogits, moe_stream stream) {
+    using namespace moe;
+    if (T < 0 || E < 1 || E > 512 || K < 1 || K > 16) return MOE_EINVAL;
+    if (K > E) return MOE_ESHAPE;
+    if ((int64_t)T * K >= (1ll << 31) || (int64_t)T * E >= (1ll << 40)) return MOE_EINVAL;
+    if (T == 0) return MOE_OK;
+    if (!topk_idx || !gates || !dgates || !dlogits) return MOE_EINVAL;
+    if (moe_host::misaligned(topk_idx) || moe_host::misaligned(gates) || moe_host::misaligned(dgates) ||
+        moe_host::misaligned(dlogits))
+        return MOE_EALIGN;
+    route_backward_kernel<<<(T + 3) / 4, 256, 0, (hipStream_t)stream>>>(topk_idx, gates, dgates, T, E, K,
+                                                                         dlogits);
     return moe_host::launch_status();
 }
 

@@ -38,6 +38,8 @@ class MoeBuffers:
     dw_gate: torch.Tensor | None = None
     dw_up: torch.Tensor | None = None
     dw_down: torch.Tensor | None = None
+    dgates: torch.Tensor | None = None
+    dlogits: torch.Tensor | None = None
 
     @classmethod
     def allocate(cls, shape: MoeShape, cap: int | None = None, device="cuda", backward=None):
@@ -61,6 +63,8 @@ class MoeBuffers:
             b.dw_gate = e((EL, H, F), dt=torch.float32)
             b.dw_up = e((EL, H, F), dt=torch.float32)
             b.dw_down = e((EL, F, H), dt=torch.float32)
+            b.dgates = e((T, K), dt=torch.float32)
+            b.dlogits = e((T, shape.E), dt=torch.float32)
         return b
 
 
@@ -102,7 +106,8 @@ def backward(buf: MoeBuffers, inp: dict):
     """inp additionally holds d_out. Needs the forward's ab_save."""
     s = buf.shape
     H, F, EL, cap = s.H, s.F, s.EL, buf.cap
-    _lib.moe_gather(inp["d_out"], buf.pos, buf.gates, buf.dy_perm)
+    _lib.moe_gather_gate_grad(inp["d_out"], buf.pos, buf.gates, buf.y, buf.dy_perm, buf.dgates)
+    _lib.moe_route_backward(buf.topk_idx, buf.gates, buf.dgates, s.E, buf.dlogits)
     _lib.moe_grouped_gemm(buf.dy_perm, inp["w_down"], None, 1, buf.offsets, H, F, cap, buf.dab,
                           epilogue=_lib.MOE_EPI_SWIGLU_BWD, ab=buf.ab)
     _lib.moe_grouped_gemm(buf.dab, inp["w_gate"], inp["w_up"], 1, buf.offsets, F, H, cap, buf.dx_perm)

@@ -22,7 +22,7 @@ def declared_symbols():
 def test_header_declares_the_entry_points():
     names = declared_symbols()
     for need in ("moe_route", "moe_permute", "moe_grouped_gemm_swiglu", "moe_grouped_gemm", "moe_combine",
-                 "moe_wgrad", "moe_gather"):
+                 "moe_wgrad", "moe_gather", "moe_gather_gate_grad", "moe_route_backward"):
         assert need in names
 
 
@@ -114,3 +114,21 @@ def test_gemm_rejects():
     assert lib.moe_combine(FAKE, FAKE, None, 8, 2, 100, FAKE, None) == -2
     assert lib.moe_combine(FAKE, None, None, 8, 2, 64, FAKE, None) == -1
     assert lib.moe_gather(FAKE, FAKE, None, 8, 0, 64, FAKE, None) == -1
+
+
+def test_router_backward_rejects():
+    lib = _lib.load()
+    g = lib.moe_gather_gate_grad
+    assert g(FAKE, FAKE, None, FAKE, 8, 2, 64, FAKE, FAKE, None) == -1     # gates required
+    assert g(FAKE, FAKE, FAKE, None, 8, 2, 64, FAKE, FAKE, None) == -1     # y required
+    assert g(FAKE, FAKE, FAKE, FAKE, 8, 2, 64, FAKE, None, None) == -1     # dgates required
+    assert g(FAKE, FAKE, FAKE, FAKE, 8, 17, 64, FAKE, FAKE, None) == -1    # K > 16
+    assert g(FAKE, FAKE, FAKE, FAKE, 8, 2, 100, FAKE, FAKE, None) == -2    # H % 64
+    assert g(FAKE, FAKE, FAKE, MIS, 8, 2, 64, FAKE, FAKE, None) == -3
+    assert g(None, None, None, None, 0, 2, 64, None, None, None) == 0      # no tokens: nothing to do
+    r = lib.moe_route_backward
+    assert r(FAKE, FAKE, FAKE, 8, 4, 5, FAKE, None) == -2                  # K > E
+    assert r(FAKE, FAKE, FAKE, 8, 600, 2, FAKE, None) == -1                # E > 512
+    assert r(FAKE, None, FAKE, 8, 8, 2, FAKE, None) == -1
+    assert r(FAKE, FAKE, FAKE, 8, 8, 2, MIS, None) == -3
+    assert r(None, None, None, 0, 8, 2, None, None) == 0

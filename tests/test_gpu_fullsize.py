@@ -196,6 +196,30 @@ def test_wgrad_sampled(case, which):
         assert_close(f"dw[{j}]", got[j][:, cols], ref[j][:, cols])
 
 
+def test_gate_grad_and_route_backward_full(case):
+    """Router backward at full size: dgates for every token from the same seeded d_out and y on both
+    sides, the fused kernel's dy_perm equal to moe_gather's, and dlogits for every token from the same
+    seeded dgates."""
+    c = case
+    s = c.shape
+    d_out = c.inp["d_out"] if "d_out" in c.inp else synth.operand_bf16((s.T, s.H), seed=0, tag=10)
+    yin = synth.operand_bf16((s.cap, s.H), seed=0, tag=11, std=0.05)
+    d = pipeline.to_device(dict(d_out=d_out, y=yin))
+    dy = torch.empty((s.cap, s.H), dtype=torch.bfloat16, device="cuda")
+    dy2 = torch.empty_like(dy)
+    _, dg = _lib.moe_gather_gate_grad(d["d_out"], c.buf.pos, c.buf.gates, d["y"], dy)
+    _lib.moe_gather(d["d_out"], c.buf.pos, c.buf.gates, dy2)
+    dgin = synth.operand_bf16((s.T, s.K), seed=0, tag=12)
+    dgin = synth.bf16_bits_to_f32(dgin)
+    dl = _lib.moe_route_backward(c.buf.topk_idx, c.buf.gates, torch.from_numpy(dgin).cuda(), s.E)
+    torch.cuda.synchronize()
+    R = c.R
+    assert torch.equal(dy[:R].view(torch.int16), dy2[:R].view(torch.int16)), "fused gather differs"
+    assert_close("dgates", bits(dg), oracle.gate_grad(d_out, yin, c.ref_pm["pos"]))
+    # gates: the oracle's own (indices are bit-exact; gate values within tolerance)
+    assert_close("dlogits", bits(dl), oracle.route_backward(c.ref_idx, c.ref_g, dgin, s.E))
+
+
 def test_full_layer_rerun_bitwise(case):
     c = case
     s = c.shape
@@ -204,7 +228,8 @@ def test_full_layer_rerun_bitwise(case):
     if s.backward:
         pipeline.backward(b2, c.dev)
     torch.cuda.synchronize()
-    fields = ["topk_idx", "gates", "pos", "out"] + (["dx", "dw_gate", "dw_up", "dw_down"] if s.backward else [])
+    fields = ["topk_idx", "gates", "pos", "out"] + (["dx", "dw_gate", "dw_up", "dw_down", "dgates", "dlogits"]
+                                                      if s.backward else [])
     for f in fields:
         assert torch.equal(getattr(c.buf, f).view(torch.uint8), getattr(b2, f).view(torch.uint8)), f
     R = c.R

@@ -65,6 +65,8 @@ def check_layer(shape, inp, buf, cap):
     assert_close("dw_gate", bits(buf.dw_gate), refb["dw_gate"])
     assert_close("dw_up", bits(buf.dw_up), refb["dw_up"])
     assert_close("dw_down", bits(buf.dw_down), refb["dw_down"])
+    assert_close("dgates", bits(buf.dgates), refb["dgates"])
+    assert_close("dlogits", bits(buf.dlogits), refb["dlogits"])
     return ref
 
 
@@ -87,7 +89,7 @@ def test_layer_reruns_are_bitwise_identical(name):
         pipeline.backward(b2, dev)
         torch.cuda.synchronize()
         R = int(bits(b1.offsets)[-1])
-        for f in ("topk_idx", "gates", "pos", "out", "dx", "dw_gate", "dw_up", "dw_down"):
+        for f in ("topk_idx", "gates", "pos", "out", "dx", "dw_gate", "dw_up", "dw_down", "dgates", "dlogits"):
             assert torch.equal(getattr(b1, f).view(torch.uint8), getattr(b2, f).view(torch.uint8)), f
         for f in ("src", "x_perm", "h", "ab", "y", "dy_perm", "dab", "dx_perm"):
             a, b = getattr(b1, f)[:R], getattr(b2, f)[:R]
