@@ -8,34 +8,49 @@
 // chosen probabilities renormalised over the K choices; the softmax
 // normaliser cancels, so g_k = exp(s_k - s_max) / sum_k' exp(s_k' - s_max).
 //
-// One wave64 per token.  Each lane holds E/64 scores as 64-bit keys
-// (order-preserving score bits << 32 | ~expert id), so the K rounds of a
-// wave-wide max give the total order directly; the winner's key is cleared.
-// Loads of a row are coalesced (lane-strided), the kernel is HBM-bound.
+// One wave64 per token.  Lane l holds the scores of experts l, l+64, ... as
+// order-preserving 32-bit keys.  Each of the K rounds takes the lane's best
+// remaining key (the lowest slot wins a tie inside the lane: lowest expert
+// id), reduces the lane bests to the wave maximum with DPP row operations
+// (no LDS round trips), and, if several lanes hold that score, takes the
+// lowest expert id among them; the winner clears its key.  Row loads are
+// lane-strided and coalesced.
 #include "moe_common.hpp"
 
 namespace moe {
 
-__device__ __forceinline__ uint64_t score_key(float s, int e) {
+__device__ __forceinline__ uint32_t score_key(float s) {
     if (s == 0.0f) s = 0.0f;  // -0 and +0 compare equal: canonicalise to +0
     uint32_t u = __float_as_uint(s);
-    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return ((uint64_t)u << 32) | (uint32_t)(0xffffffffu - (uint32_t)e);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);  // > 0 for every non-NaN score
 }
 
-__device__ __forceinline__ float key_score(uint64_t k) {
-    uint32_t u = (uint32_t)(k >> 32);
-    u = (u & 0x80000000u) ? (u & 0x7fffffffu) : ~u;
-    return __uint_as_float(u);
+__device__ __forceinline__ float key_score(uint32_t u) {
+    return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        uint64_t o = __shfl_xor(v, off, 64);
-        v = o > v ? o : v;
-    }
-    return v;
+// max / min over the 64 lanes: butterflies within each row of 16 (quad
+// permutes, half-row and row mirrors), then row broadcasts bring every row
+// into lane 63.  Lanes without a DPP source take the identity.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xf, 0xf, false));   // quad [1,0,3,2]
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xf, 0xf, false));   // quad [2,3,0,1]
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xf, 0xf, false));  // row_half_mirror
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xf, 0xf, false));  // row_mirror
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false));  // row_bcast:15
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false));  // row_bcast:31
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+    const int id = -1;  // all ones: the identity of an unsigned min
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0xB1, 0xf, 0xf, false));
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x4E, 0xf, 0xf, false));
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x141, 0xf, 0xf, false));
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x140, 0xf, 0xf, false));
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x142, 0xa, 0xf, false));
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x143, 0xc, 0xf, false));
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 template <int EPL>
@@ -46,26 +61,44 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
     const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
     const float* row = logits + t * E;
-    uint64_t key[EPL];
+    uint32_t key[EPL];  // 0 = absent or taken (below every score's key)
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
-        int e = i * 64 + lane;
-        key[i] = e < E ? score_key(__builtin_nontemporal_load(row + e), e) : 0ull;
+        const int e = i * 64 + lane;
+        key[i] = e < E ? score_key(__builtin_nontemporal_load(row + e)) : 0u;
     }
     int my_idx = 0;
     float my_score = 0.0f, s_max = 0.0f;
     for (int k = 0; k < K; ++k) {
-        uint64_t best = key[0];
+        // the lane's best remaining key; strict > keeps the lowest slot on a tie
+        uint32_t best = key[0];
+        int bj = 0;
 #pragma unroll
-        for (int i = 1; i < EPL; ++i) best = key[i] > best ? key[i] : best;
-        best = wave_max_u64(best);
+        for (int i = 1; i < EPL; ++i)
+            if (key[i] > best) {
+                best = key[i];
+                bj = i;
+            }
+        const uint32_t m = wave_max_u32(best);
+        const uint64_t tied = __ballot(best == m);
+        int e_win;
+        if (__popcll(tied) == 1) {
+            const int wl = __builtin_ctzll(tied);
+            e_win = __builtin_amdgcn_readlane(bj, wl) * 64 + wl;
+        } else {
+            // several lanes hold this score: the lowest expert id among them
+            e_win = (int)wave_min_u32(best == m ? (uint32_t)(bj * 64 + lane) : 0xffffffffu);
+        }
+        e_win = __builtin_amdgcn_readfirstlane(e_win);
+        if (lane == (e_win & 63)) {
 #pragma unroll
-        for (int i = 0; i < EPL; ++i)
-            if (key[i] == best) key[i] = 0ull;
-        float s = key_score(best);
+            for (int i = 0; i < EPL; ++i)
+                if (i == (e_win >> 6)) key[i] = 0u;
+        }
+        const float s = key_score(m);
         if (k == 0) s_max = s;
         if (lane == k) {
-            my_idx = (int)(0xffffffffu - (uint32_t)best);
+            my_idx = e_win;
             my_score = s;
         }
     }

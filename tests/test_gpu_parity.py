@@ -170,3 +170,18 @@ def test_wgrad_empty_expert_writes_zeros_and_grid_independence():
     assert_close("dw", dw.cpu().numpy(), ref)
     assert torch.equal(dw.view(torch.int32), dw2.view(torch.int32))
     assert np.all(dw[0].cpu().numpy() == 0) and np.all(dw[4].cpu().numpy() == 0)
+
+
+@pytest.mark.parametrize("E,K", [(8, 2), (64, 8), (100, 8), (256, 8), (320, 16)])
+def test_route_ties_and_signed_zeros(E, K):
+    """Scores drawn from a handful of values (exact ties everywhere, -0.0 next to +0.0): the GPU's
+    choice must follow (score desc, id asc) exactly."""
+    rng = np.random.default_rng(E * 31 + K)
+    T = 777
+    logits = rng.integers(-2, 3, (T, E)).astype(np.float32)
+    logits[rng.random((T, E)) < 0.2] = -0.0
+    idx, g = _lib.moe_route(torch.from_numpy(logits).cuda(), K)
+    torch.cuda.synchronize()
+    ref_idx, ref_g = oracle.route(logits, K)
+    assert_equal("topk_idx", bits(idx), ref_idx)
+    assert_close("gates", bits(g), ref_g)
