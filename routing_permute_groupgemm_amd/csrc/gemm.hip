@@ -548,6 +548,59 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
         }
 
         // ---- epilogue: lane holds row (l%32) and columns 8*j4 + 4*(l/32) + 0..3 ----
+        if constexpr (EPI == EPI_BF16 || EPI == EPI_F32) {
+            // Plain results go out through LDS so that every store writes whole
+            // 128-byte row lines (stored straight from the MFMA layout, each
+            // store touches 32 rows).  The stage slot of the last stage (gs-1)
+            // is free until the next stage issues its loads; each wave stages
+            // 32 rows x 128 bytes at a time in its own 4 KiB of that slot, with
+            // 16-byte chunks XOR-swizzled by row.
+            static_assert(TL::kStage / TL::kWaves >= 4096, "staging space per wave");
+            uint8_t* stg = smem + ((gs + S - 1) % S) * TL::kStage + wave * 4096;
+            const int r = lane & 31, h = lane >> 5;
+            auto stage_addr = [&](int row, int chunk) {
+                return (MOE_LDS uint8_t*)(stg + row * 128 + ((chunk ^ (row & 7)) << 4));
+            };
+            // column groups per round: 64 bf16 (two MFMA tiles) or 32 fp32 (one)
+            constexpr int kTilesPerRound = EPI == EPI_BF16 ? 2 : 1;
+#pragma unroll
+            for (int mt = 0; mt < MTW; ++mt) {
+#pragma unroll
+                for (int np = 0; np < NTW / kTilesPerRound; ++np) {
+#pragma unroll
+                    for (int q = 0; q < kTilesPerRound; ++q) {
+                        const f32x16& a = acc[mt][np * kTilesPerRound + q];
+#pragma unroll
+                        for (int j4 = 0; j4 < 4; ++j4) {
+                            if (EPI == EPI_BF16) {
+                                u32x2 w = {pack_bf2(a[4 * j4], a[4 * j4 + 1]), pack_bf2(a[4 * j4 + 2], a[4 * j4 + 3])};
+                                *(MOE_LDS u32x2*)(stage_addr(r, 4 * q + j4) + 8 * h) = w;
+                            } else {
+                                f32x4 w = {a[4 * j4], a[4 * j4 + 1], a[4 * j4 + 2], a[4 * j4 + 3]};
+                                *(MOE_LDS f32x4*)stage_addr(r, 2 * j4 + h) = w;
+                            }
+                        }
+                    }
+                    // read back 8 rows x 128 bytes per instruction and store whole lines
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int rr = 8 * i + (lane >> 3), c = lane & 7;
+                        const u32x4 v = *(const MOE_LDS u32x4*)stage_addr(rr, c);
+                        const int mloc = wm * (BM / WM) + mt * 32 + rr;
+                        if (EPI == EPI_BF16) {
+                            const int n = ni * BN + wn * (BN / WN) + 64 * np + 8 * c;
+                            if (mloc < valid && n < p.N) *(u32x4*)(p.c + (int64_t)(row0 + mloc) * p.ldc + n) = v;
+                        } else {
+                            const int m = mi_w * BM + mloc;
+                            const int n = ni * BN + wn * (BN / WN) + 32 * np + 4 * c;
+                            if (m < p.M && n < p.N) *(u32x4*)(p.cf + ((int64_t)j * p.M + m) * p.N + n) = v;
+                        }
+                    }
+                }
+            }
+            __syncthreads();  // every wave is done with the slot before the next stage refills it
+            continue;
+        }
         const int cq = 4 * (lane >> 5);
 #pragma unroll
         for (int mt = 0; mt < MTW; ++mt) {
