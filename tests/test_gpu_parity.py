@@ -185,3 +185,26 @@ def test_route_ties_and_signed_zeros(E, K):
     ref_idx, ref_g = oracle.route(logits, K)
     assert_equal("topk_idx", bits(idx), ref_idx)
     assert_close("gates", bits(g), ref_g)
+
+
+@pytest.mark.parametrize("T,K", [(8192, 8), (8193, 8), (20000, 4)])
+def test_permute_local_share_and_capacity(T, K):
+    """A local share (experts 8..47 of 64) at several thousand tokens: counts, offsets, pos, src and
+    x_perm exactly as the oracle's, with the expected capacity and with half of it (rows dropped)."""
+    shape = synth.MoeShape(f"paths_T{T}_K{K}", 93, T=T, H=64, F=64, E=64, K=K, e_begin=8, e_local=40)
+    inp = synth.make_inputs(shape, seed=5)
+    dev = pipeline.to_device(inp)
+    for cap in (shape.cap, shape.T * shape.K * 40 // 64 // 2):
+        buf = pipeline.MoeBuffers.allocate(shape, cap=cap, backward=False)
+        pipeline.route(buf, dev["logits"])
+        pipeline.permute(buf, dev["x"])
+        torch.cuda.synchronize()
+        idx, _ = oracle.route(inp["logits"], K)
+        ref = oracle.permute(idx, shape.e_begin, shape.EL, inp["x"], cap)
+        R = min(int(ref["offsets"][-1]), cap)
+        assert_equal("counts", bits(buf.counts)[:shape.EL], ref["counts"])
+        assert_equal("offsets", bits(buf.offsets), ref["offsets"])
+        assert_equal("pos", bits(buf.pos), ref["pos"])
+        assert_equal("src", bits(buf.src)[:R], ref["src"][:R])
+        assert_equal("status", bits(buf.status)[0], ref["status"])
+        assert_equal("x_perm", bits(buf.x_perm)[:R], ref["x_perm"][:R])
