@@ -767,13 +767,10 @@ static int env_int(const char* name, int dflt) {
     return e ? atoi(e) : dflt;
 }
 
+// read on every call, so a process can compare configurations
 static int tile_config() {
-    static int cfg = -1;
-    if (cfg < 0) {
-        const int t = env_int("MOE_GEMM_TILE", 0);
-        cfg = t == 128 ? CFG_SMALL : t == 192 ? CFG_MID : t == 256 ? CFG_BIG : CFG_AUTO;
-    }
-    return cfg;
+    const int t = env_int("MOE_GEMM_TILE", 0);
+    return t == 128 ? CFG_SMALL : t == 192 ? CFG_MID : t == 256 ? CFG_BIG : CFG_AUTO;
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int LB, int EPI, int SCHED, int LDSB, int ALT = 0>

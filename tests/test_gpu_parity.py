@@ -208,3 +208,15 @@ def test_permute_local_share_and_capacity(T, K):
         assert_equal("src", bits(buf.src)[:R], ref["src"][:R])
         assert_equal("status", bits(buf.status)[0], ref["status"])
         assert_equal("x_perm", bits(buf.x_perm)[:R], ref["x_perm"][:R])
+
+
+@pytest.mark.parametrize("tile", ["256", "192", "128"])
+@pytest.mark.parametrize("name", ["ep_share_small", "fwdbwd_small"])
+def test_layer_matches_oracle_in_every_tile_configuration(name, tile, monkeypatch):
+    """The automatic choice takes the 192-row body at these sizes; pin each GroupGEMM configuration
+    (MOE_GEMM_TILE, read on every call) and check the whole layer element by element."""
+    monkeypatch.setenv("MOE_GEMM_TILE", tile)
+    shape = SMALL[name]
+    inp = synth.make_inputs(shape, seed=4, d_out=True)
+    buf, _ = run_gpu(shape, inp)
+    check_layer(shape, inp, buf, shape.cap)
