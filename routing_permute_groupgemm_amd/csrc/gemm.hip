@@ -5,18 +5,20 @@
 // dgrad GEMMs and, for the weights, a transposed GroupGEMM reducing over the
 // token dimension), "Scoreboard-based Synchronization" (a padding-free
 // GroupGEMM with dynamic pointer arithmetic over irregular per-expert tiles),
-// "Computation Worker" (a 128x256x64 tile; here 128x128x64 for 64-wide
-// waves).  The blog restatement of the performance model notes that SwiGLU
-// is purely memory-bound, so it is fused into the GEMM epilogue.
+// "Computation Worker" (a 128x256x64 tile on Hopper; here 256x256 or 192x256
+// blocks of 64-wide waves, BK = 32).  The blog restatement of the
+// performance model notes that SwiGLU is purely memory-bound, so it is fused
+// into the GEMM epilogue.
 //
 // One kernel template covers every GEMM of the layer:
 //   ROWS schedule  C[r, :] = A[r, :] . B_j for the rows r of expert j
 //     A (x_perm, h, dy_perm, dab) is contraction-contiguous ("KC");
 //     B is the expert weight, either [Kd][N] (N contiguous, "MN") or [N][Kd]
-//     (contraction contiguous, "KC").  Tiles: 128 rows x 128 B-columns; the
-//     per-expert row counts stay on the device: every workgroup rebuilds the
-//     tile prefix of the experts from `offsets` and finds a tile's expert by
-//     binary search over it.
+//     (contraction contiguous, "KC").  The per-expert row counts stay on the
+//     device: every workgroup rebuilds the tile prefix of the experts from
+//     `offsets` and finds a tile's expert by binary search over it.  The
+//     kernel carries a 256-row and a 192-row body and every workgroup picks
+//     the same one from the row counts (prefer_alt).
 //   WGRAD schedule dW_j = A_j^T . B_j over the rows of expert j, A and B both
 //     "MN" (their rows are the contraction).  The contraction over rows is one
 //     fixed-order loop per output tile (no split, no atomics); experts are
@@ -24,14 +26,15 @@
 //
 // Data path: global -> LDS by buffer_load ... lds (16 bytes per lane, no
 // VGPR staging; loads past the resource bound return zero, which masks
-// ragged row tails), two LDS stages; LDS rows are 128 bytes, 16-byte chunks
-// XOR-swizzled by row; contraction-contiguous fragments are read with
-// ds_read_b128, the others with the transposing ds_read_b64_tr_b16.  The
-// MFMA is v_mfma_f32_32x32x16_bf16 with the weight fragment as its first
-// operand, so each lane ends with 4 consecutive output columns of one row.
-// Workgroups are persistent, and block ids are remapped so each XCD (own L2)
-// walks a contiguous run of tiles; tiles are visited in groups of 4 row
-// blocks so neighbouring tiles share A rows and B columns.
+// ragged row tails) into a four-stage ring that runs on across a workgroup's
+// tiles; LDS rows are XOR-swizzled by 16-byte chunk; contraction-contiguous
+// fragments are read with ds_read_b128, the others with the transposing
+// ds_read_b64_tr_b16.  Inside a stage every MFMA is followed by an LDS read
+// of the next k-step's fragments, and the stage's loads are spread among the
+// MFMAs.  The MFMA is v_mfma_f32_32x32x16_bf16 with the weight fragment as
+// its first operand, so each lane ends with 4 consecutive output columns of
+// one row.  Workgroups are persistent, and block ids are remapped so each XCD
+// (own L2) walks a contiguous run of tiles.
 #include <stdlib.h>
 
 #include <algorithm>
@@ -74,8 +77,8 @@ struct GemmParams {
 
 typedef __attribute__((ext_vector_type(4))) int i32x4;
 
-// Buffer resource (raw, stride 0): loads at or past `bytes` return zero.
-// Buffer descriptor (gfx9 layout: base, stride 0, byte range, format dword).
+// Buffer descriptor (gfx9 layout: base, stride 0, byte range, format dword);
+// loads at or past `bytes` return zero.
 // Callers pass wave-uniform values; readfirstlane states that to the compiler
 // (a no-op on values it already holds in scalar registers) so the descriptor
 // can always live in SGPRs as the buffer instructions require.
