@@ -41,17 +41,22 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-rows", action="store_true",
+                    help="forward-only workloads: permute with the row copy instead of zero-copy dispatch")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration under rocprofv3)")
     return ap.parse_args()
 
 
-def algorithmic_work(shape, R, T_act, n_active):
-    """Per-launch algorithmic bytes and flops of every step (real rows only, no padding)."""
+def algorithmic_work(shape, R, T_act, n_active, zero_copy=False):
+    """Per-launch algorithmic bytes and flops of every step (real rows only, no padding).
+    With zero-copy dispatch the permutation moves indices only and the gate/up
+    GroupGEMM reads the routed rows from x (the same 2*R*H bytes as from x_perm)."""
     T, H, F, E, K, EL = shape.T, shape.H, shape.F, shape.E, shape.K, shape.EL
     w = {}
     w["route"] = dict(bytes=4 * T * E + 8 * T * K, flops=0)
-    w["permute"] = dict(bytes=4 * T * K * 3 + 4 * R + 2 * H * T_act + 2 * H * R + 8 * EL, flops=0)
+    rows = 0 if zero_copy else 2 * H * T_act + 2 * H * R
+    w["permute"] = dict(bytes=4 * T * K * 3 + 4 * R + rows + 8 * EL, flops=0)
     ab = 2 * R * 2 * F if shape.backward else 0
     w["expert_up"] = dict(bytes=2 * n_active * H * 2 * F + 2 * R * H + 2 * R * F + ab, flops=4 * R * H * F)
     w["expert_down"] = dict(bytes=2 * n_active * F * H + 2 * R * F + 2 * R * H, flops=2 * R * F * H)
@@ -157,12 +162,13 @@ def main():
     print(f"[bench] {shape.name}: generating inputs", file=sys.stderr, flush=True)
     inp = synth.make_inputs(shape, seed=args.seed)
     dev = pipeline.to_device(inp)
-    buf = pipeline.MoeBuffers.allocate(shape)
+    zero_copy = not shape.backward and not args.copy_rows
+    buf = pipeline.MoeBuffers.allocate(shape, zero_copy=zero_copy)
     stream = torch.cuda.current_stream()
 
     steps = [("route", lambda: pipeline.route(buf, dev["logits"])),
              ("permute", lambda: pipeline.permute(buf, dev["x"])),
-             ("expert_up", lambda: pipeline.expert_up(buf, dev["w_gate"], dev["w_up"])),
+             ("expert_up", lambda: pipeline.expert_up(buf, dev["w_gate"], dev["w_up"], dev["x"])),
              ("expert_down", lambda: pipeline.expert_down(buf, dev["w_down"])),
              ("combine", lambda: pipeline.combine(buf))]
     if shape.backward:
@@ -219,7 +225,7 @@ def main():
     pos = buf.pos.cpu().numpy()
     T_act = int(np.sum(np.any(pos >= 0, axis=1)))
     n_active = int(np.sum(counts > 0))
-    work = algorithmic_work(shape, R, T_act, n_active)
+    work = algorithmic_work(shape, R, T_act, n_active, zero_copy)
     dom = max(per, key=per.get)
     rl = roofline(work[dom], per[dom])
     rl["kernel"] = dom
@@ -242,6 +248,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": shape.name, "T": shape.T, "H": shape.H, "F": shape.F, "E": shape.E, "K": shape.K,
                    "e_local": shape.EL, "cap_rows": buf.cap, "pass": "fwd+bwd" if shape.backward else "fwd",
+                   "dispatch": "zero-copy" if zero_copy else "row copy",
                    "routed_rows": R, "maxvio": round(synth.maxvio(counts, shape.T, shape.K, shape.E), 3),
                    "seed": args.seed, "parallelism": "single GPU"},
         "roofline": rl,

@@ -113,6 +113,9 @@ size_t moe_permute_workspace_size(int T, int K, int e_local);
  *   pos      int32 [T,K] out: destination row of pair (t,k), or -1.
  *   src      int32 [cap_rows] out: src[pos[t,k]] = t*K+k.
  *   x_perm   bf16 [cap_rows,H] out: x_perm[pos[t,k]] = x[t] (bit copy).
+ *            x and x_perm both NULL: the index-only permutation, no row
+ *            copy (for moe_grouped_gemm_swiglu_gather); one of them NULL is
+ *            MOE_EINVAL.
  *   status   int32 [1] out: 0, or 1 if R > cap_rows (rows >= cap_rows are
  *            dropped: their pos is -1 and nothing is written for them;
  *            counts/offsets still hold the true totals).
@@ -171,6 +174,29 @@ int moe_grouped_gemm_swiglu(const moe_bf16* x_perm, const moe_bf16* w_gate,
                             const moe_bf16* w_up, const int32_t* offsets,
                             int e_local, int H, int F, int cap_rows,
                             moe_bf16* h, moe_bf16* ab_save, moe_stream stream);
+
+/*
+ * moe_grouped_gemm_swiglu without the permuted copy of the tokens (MoonEP
+ * page, "How Redundant Expert Planning Achieves Perfect Balance": zero-copy
+ * dispatch puts tokens at their expert-grouped positions with no copy through
+ * an intermediate buffer; on one GPU the GEMM reads each token where it
+ * already is).  Row r of the expert-grouped
+ * order is read from x[src[r] / K], so the index-only moe_permute (x and
+ * x_perm NULL) replaces the row copy.  h and ab_save are bit-identical to
+ * moe_grouped_gemm_swiglu on the x_perm that moe_permute would have written.
+ *   x    bf16 [T,H], the tokens;  src int32 [cap_rows] from moe_permute
+ *        (src[r] = t*K + k);  K the top-k of src's encoding;
+ *   other arguments as moe_grouped_gemm_swiglu.
+ * Errors: T*H*2 must be below 2^31 and cap_rows <= T*K (MOE_EINVAL).  A src
+ * value outside [0, T*K) reads a zero row (no access outside x).
+ * The weight gradient needs x_perm, so a forward that is followed by the
+ * backward keeps the row copy.
+ */
+int moe_grouped_gemm_swiglu_gather(const moe_bf16* x, int T, const int32_t* src, int K,
+                                   const moe_bf16* w_gate, const moe_bf16* w_up,
+                                   const int32_t* offsets, int e_local, int H, int F,
+                                   int cap_rows, moe_bf16* h, moe_bf16* ab_save,
+                                   moe_stream stream);
 
 /*
  * Generic padding-free GroupGEMM over expert row groups (UniEP "MoE

@@ -29,6 +29,7 @@ SIGNATURES = {
     "moe_gather": ([_p, _p, _p, _i, _i, _i, _p, _p], _i),
     "moe_gather_gate_grad": ([_p, _p, _p, _p, _i, _i, _i, _p, _p, _p], _i),
     "moe_grouped_gemm_swiglu": ([_p, _p, _p, _p, _i, _i, _i, _i, _p, _p, _p], _i),
+    "moe_grouped_gemm_swiglu_gather": ([_p, _i, _p, _i, _p, _p, _p, _i, _i, _i, _i, _p, _p, _p], _i),
     "moe_grouped_gemm": ([_p, _i, _p, _p, _i, _p, _i, _i, _i, _i, _i, _p, _p, _i, _p], _i),
     "moe_combine": ([_p, _p, _p, _i, _i, _i, _p, _p], _i),
     "moe_wgrad": ([_p, _i, _p, _i, _p, _i, _i, _i, _i, _p, _p], _i),
@@ -107,8 +108,11 @@ def moe_permute_workspace_size(T, K, e_local) -> int:
     return int(load().moe_permute_workspace_size(T, K, e_local))
 
 
-def moe_permute(topk_idx, e_begin, e_local, x, cap_rows, out=None, ws=None, stream=None):
-    """-> dict(counts, offsets, pos, src, x_perm, status) (all device tensors)."""
+def moe_permute(topk_idx, e_begin, e_local, x, cap_rows, out=None, ws=None, stream=None, copy_rows=True):
+    """-> dict(counts, offsets, pos, src, x_perm, status) (all device tensors).
+
+    copy_rows=False: the index-only permutation (x_perm is None), for the
+    gate/up GroupGEMM that reads x through src."""
     _need(topk_idx, torch.int32, "topk_idx")
     _need(x, torch.bfloat16, "x")
     T, K = topk_idx.shape
@@ -128,15 +132,17 @@ def moe_permute(topk_idx, e_begin, e_local, x, cap_rows, out=None, ws=None, stre
     if src is None:
         src = torch.empty(max(cap_rows, 1), dtype=torch.int32, device=dev)
     x_perm = o.get("x_perm")
-    if x_perm is None:
+    if x_perm is None and copy_rows:
         x_perm = torch.empty((max(cap_rows, 1), H), dtype=torch.bfloat16, device=dev)
+    if not copy_rows:
+        x_perm = None
     status = o.get("status")
     if status is None:
         status = torch.empty(4, dtype=torch.int32, device=dev)
     need = moe_permute_workspace_size(T, K, e_local)
     if ws is None or ws.numel() < need:
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
-    _check(load().moe_permute(_ptr(topk_idx), T, K, e_begin, e_local, _ptr(x), H, cap_rows,
+    _check(load().moe_permute(_ptr(topk_idx), T, K, e_begin, e_local, _ptr(x) if copy_rows else None, H, cap_rows,
                               _ptr(counts), _ptr(offsets), _ptr(pos), _ptr(src), _ptr(x_perm),
                               _ptr(status), _ptr(ws), ws.numel(), _stream(stream)))
     return dict(counts=counts[:e_local], offsets=offsets, pos=pos, src=src, x_perm=x_perm,
@@ -181,6 +187,25 @@ def moe_grouped_gemm_swiglu(x_perm, w_gate, w_up, offsets, cap_rows, h=None, ab_
         h = torch.empty((x_perm.shape[0], F), dtype=torch.bfloat16, device=x_perm.device)
     _check(load().moe_grouped_gemm_swiglu(_ptr(x_perm), _ptr(w_gate), _ptr(w_up), _ptr(offsets), EL, H, F,
                                           cap_rows, _ptr(h), _ptr(ab_save), _stream(stream)))
+    return h
+
+
+def moe_grouped_gemm_swiglu_gather(x, src, K, w_gate, w_up, offsets, cap_rows, h=None, ab_save=None,
+                                   stream=None):
+    """Gate/up GroupGEMM + SwiGLU reading row r of the expert-grouped order
+    straight from x[src[r] // K] (no x_perm)."""
+    _need(x, torch.bfloat16, "x")
+    _need(src, torch.int32, "src")
+    _need(w_gate, torch.bfloat16, "w_gate")
+    _need(w_up, torch.bfloat16, "w_up")
+    _need(offsets, torch.int32, "offsets")
+    EL, H, F = w_gate.shape
+    T = x.shape[0]
+    if h is None:
+        h = torch.empty((max(cap_rows, 1), F), dtype=torch.bfloat16, device=x.device)
+    _check(load().moe_grouped_gemm_swiglu_gather(_ptr(x), T, _ptr(src), int(K), _ptr(w_gate), _ptr(w_up),
+                                                 _ptr(offsets), EL, H, F, cap_rows, _ptr(h), _ptr(ab_save),
+                                                 _stream(stream)))
     return h
 
 

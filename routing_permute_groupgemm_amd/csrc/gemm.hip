@@ -24,6 +24,12 @@
 //     fixed-order loop per output tile (no split, no atomics); experts are
 //     visited longest first.
 //
+// Zero-copy variant (GATHER, gate/up only): the A rows are read from the
+// tokens x[src[r] / K] instead of the permuted copy (MoonEP page, "How
+// Redundant Expert Planning Achieves Perfect Balance": zero-copy dispatch);
+// each lane's row offsets are set once per tile from indices fetched a tile
+// ahead.
+//
 // Data path: global -> LDS by buffer_load ... lds (16 bytes per lane, no
 // VGPR staging; loads past the resource bound return zero, which masks
 // ragged row tails) into a four-stage ring that runs on across a workgroup's
@@ -73,6 +79,10 @@ struct GemmParams {
     uint16_t* c2;         // SWIGLU: ab_save [rows, 2F]
     const uint16_t* ab;   // SWIGLU_BWD: saved [a | b], row stride 2N
     float* cf;            // WGRAD: fp32 out [e_local, M, N]
+    const int32_t* src;   // ROWS gather: row r of the tile reads a[src[r] / topk]
+    int topk;
+    uint32_t topk_rcp;    // floor((2^32 - 1) / topk): src / topk without a divide
+    int64_t a_rows;       // ROWS gather: rows of a (bounds every A load)
 };
 
 typedef __attribute__((ext_vector_type(4))) int i32x4;
@@ -107,11 +117,27 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const MOE_LDS void*)p;
 }
 
+// 4 bytes per lane into LDS at lds + 4*lane (same contract as lds_load16).
+__device__ __forceinline__ void lds_load4(i32x4 srd, uint32_t lds, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds), "v"(voff), "s"(srd)
+                 : "memory");
+}
+
 // s_waitcnt vmcnt(n) for a compile-time n (lgkmcnt and expcnt left alone).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// The same wait, also a compiler barrier for memory: LDS written by
+// LDS-direct loads is read after it.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_mem() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
 // ---- LDS tile layouts -------------------------------------------------------
@@ -193,13 +219,16 @@ struct Tile {
 
 // The GEMM of one workgroup for one tile shape.  smem is the stage ring;
 // s_off holds the clamped row offsets (already loaded); s_start and s_wave are
-// scratch for the schedule.
-template <int BM, int BN, int BK, int WM, int WN, int LB, int EPI, int SCHED, int LDSB>
+// scratch for the schedule; s_idx (GATHER only) holds the prefetched source
+// indices of the A rows.
+template <int BM, int BN, int BK, int WM, int WN, int LB, int EPI, int SCHED, int LDSB, bool GATHER>
 __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, const int* s_off, int* s_start,
-                                        int* s_wave) {
+                                        int* s_wave, int* s_idx) {
     using TL = Tile<BM, BN, BK, WM, WN, LDSB>;
     using LY = Lay<BK>;
     constexpr int MTW = TL::kMTW, NTW = TL::kNTW, LPW = TL::kLoadsPerWave, S = TL::kStages, KK = TL::kKK;
+    constexpr int LA = TL::kALoads / TL::kWaves;  // A loads per wave and stage
+    static_assert(!GATHER || (SCHED == SCHED_ROWS && EPI == EPI_SWIGLU), "gathered A rows: gate/up GEMM only");
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
@@ -260,8 +289,9 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
     // per-lane parts of the LDS-direct load offsets
     uint32_t lt_a0, lt_a1 = 0, lt_b0, lt_b1 = 0;
     if (SCHED == SCHED_ROWS) {
-        lt_a0 = LY::lane_kc(lane, 0, p.lda);
-        lt_a1 = LY::lane_kc(lane, 1, p.lda);
+        // gathered rows: the row term comes from the row's own offset
+        lt_a0 = LY::lane_kc(lane, 0, GATHER ? 0 : p.lda);
+        lt_a1 = LY::lane_kc(lane, 1, GATHER ? 0 : p.lda);
         if (LB == LAY_KC) {
             lt_b0 = LY::lane_kc(lane, 0, p.ldw);
             lt_b1 = LY::lane_kc(lane, 1, p.ldw);
@@ -348,13 +378,75 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
     i32x4 c_srdA = {0, 0, 0, 0}, c_srdB0 = {0, 0, 0, 0}, c_srdB1 = {0, 0, 0, 0};
     // weight gradient: the group's first A and B rows
     uint64_t c_rowA = 0, c_rowB = 0;
+
+    // Gathered A rows (GATHER): one descriptor over all of a; per lane, the
+    // byte offset of the row behind each of its LA loads (kOOB past the
+    // expert's rows).  The source indices of a tile's rows are fetched one
+    // tile ahead, by LDS-direct loads into this wave's half of a two-buffer
+    // area, so the switch to the next tile never waits for loads in flight:
+    // when the cursor reaches a tile, the KT >= 2 stages issued since its
+    // prefetch put it behind the (S-2)*LPW newest loads, which a free vmcnt
+    // wait then covers.
+    uint32_t c_rowoff[LA];
+#pragma unroll
+    for (int u = 0; u < LA; ++u) c_rowoff[u] = kOOB;
+    int idx_buf = 0;
+    bool pf_issued = false;  // the last advance() issued a prefetch (LA more loads)
+    i32x4 srd_src = {0, 0, 0, 0};
+    if (GATHER) {
+        c_srdA = make_srd(p.a, (uint32_t)(p.a_rows * p.lda * 2));
+        srd_src = make_srd(p.src, (uint32_t)(p.cap * 4));
+    }
+    // lane's row in A load u of this wave: rows q*16 + l/4 of the tile, the
+    // uniform part q*16 and the lane part l/4
+    // (per-tile code takes the lane part through an opaque copy so that
+    // nothing derived from it is hoisted out of the loop and kept live)
+    auto a_row0 = [&](int u) { return (u * TL::kWaves + wave) * LY::kRowsPerLoad; };
+    const int a_rowl_v = lane / LY::kChunks;
+    auto opaque = [](int v) {
+        asm volatile("" : "+v"(v));
+        return v;
+    };
+    auto prefetch_rows = [&](int tile, int buf) {
+        const TileDesc d = decode(tile);
+        const uint32_t base = lds_addr(s_idx) + (uint32_t)(((buf * TL::kWaves + wave) * LA) * 256);
+        const int a_rowl = opaque(a_rowl_v);
+#pragma unroll
+        for (int u = 0; u < LA; ++u) {
+            const uint32_t voff = (uint32_t)(d.row0 + a_row0(u)) * 4u + (uint32_t)a_rowl * 4u;
+            lds_load4(srd_src, base + u * 256, a_rowl < d.valid - a_row0(u) ? voff : kOOB);
+        }
+    };
+
     auto seek = [&]() {
         for (; itile < n_tiles_total; itile += G) {
             ic = decode(itile);
             if (ic.KT > 0) break;
         }
         if (SCHED == SCHED_ROWS && itile < n_tiles_total) {
-            c_srdA = make_srd(p.a + (int64_t)ic.row0 * p.lda, (uint32_t)(ic.valid * p.lda * 2));
+            if (GATHER) {
+                wait_vmcnt_mem<(S - 2) * LPW>();
+                const int a_rowl = opaque(a_rowl_v);
+                const int* si = s_idx + ((idx_buf * TL::kWaves + wave) * LA) * 64 + opaque(lane);
+#pragma unroll
+                for (int u = 0; u < LA; ++u) {
+                    // src = t*K + k; the quotient estimate is t or t - 1
+                    const uint32_t v = (uint32_t)si[u * 64];
+                    uint32_t tok = __umulhi(v, p.topk_rcp);
+                    if (v - tok * (uint32_t)p.topk >= (uint32_t)p.topk) ++tok;
+                    // the lane's 16-byte column chunk is folded in here
+                    c_rowoff[u] = a_rowl < ic.valid - a_row0(u) && tok < (uint32_t)p.a_rows
+                                      ? tok * (uint32_t)(p.lda * 2) + lt_a0
+                                      : kOOB;
+                }
+                idx_buf ^= 1;
+                if (itile + G < n_tiles_total) {
+                    prefetch_rows(itile + G, idx_buf);
+                    pf_issued = true;
+                }
+            } else {
+                c_srdA = make_srd(p.a + (int64_t)ic.row0 * p.lda, (uint32_t)(ic.valid * p.lda * 2));
+            }
             if (LB == LAY_MN) {
                 const uint32_t range = (uint32_t)(p.Kd * p.ldw * 2);
                 c_srdB0 = make_srd(p.w0 + (int64_t)ic.j * p.w_stride, range);
@@ -382,6 +474,11 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
             seek();
         }
     };
+    if (GATHER && tile0 < n_tiles_total) {
+        // the first tile's indices (row-tiled schedules skip no tile)
+        prefetch_rows(tile0, 0);
+        wait_vmcnt_mem<0>();
+    }
     seek();
 
     // Load u (0..LPW-1) of this wave for stage kt of the issue cursor's tile
@@ -409,7 +506,8 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
                 const int q = u * TL::kWaves + wave;
                 if (SCHED == SCHED_ROWS) {
                     const uint32_t lt = LY::kc_period(q) ? la1 : la0;
-                    const uint32_t voff = lt + (uint32_t)((q * LY::kRowsPerLoad * p.lda + k0) * 2);
+                    const uint32_t voff = GATHER ? c_rowoff[u] + (uint32_t)(k0 * 2)
+                                                 : lt + (uint32_t)((q * LY::kRowsPerLoad * p.lda + k0) * 2);
                     lds_load16(c_srdA, sA + q * 1024, live ? voff : kOOB);
                 } else {
                     const i32x4 r = make_srd((const uint16_t*)c_rowA + (int64_t)k0 * p.lda,
@@ -503,6 +601,7 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
     }
     wait_vmcnt<kWaitLoads>();
     __syncthreads();
+    pf_issued = false;  // the prologue's wait covered any prefetch
 
     unsigned gs = 0;  // global stage index of this workgroup; its LDS slot is gs % S
     for (int tile = tile0; tile < n_tiles_total; tile += G) {
@@ -546,7 +645,13 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
                 __builtin_amdgcn_sched_barrier(0);
             }
             advance();
-            wait_vmcnt<kWaitLoads>();
+            if (GATHER && pf_issued) {
+                // the LA index loads advance() just issued are the newest
+                pf_issued = false;
+                wait_vmcnt<kWaitLoads + LA>();
+            } else {
+                wait_vmcnt<kWaitLoads>();
+            }
             __syncthreads();
         }
 
@@ -726,7 +831,7 @@ __device__ __forceinline__ bool prefer_alt(const GemmParams& p, const int* s_off
 
 // One launch: loads the row offsets, then runs the BM-row body, or the
 // ALT-row body when ALT != 0 and prefer_alt says so.
-template <int BM, int BN, int BK, int WM, int WN, int LB, int EPI, int SCHED, int LDSB, int ALT>
+template <int BM, int BN, int BK, int WM, int WN, int LB, int EPI, int SCHED, int LDSB, int ALT, bool GATHER>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void gg_kernel(GemmParams p) {
     using TL = Tile<BM, BN, BK, WM, WN, LDSB>;
@@ -737,6 +842,9 @@ void gg_kernel(GemmParams p) {
     __shared__ int s_off[kMaxGroups + 1];    // clamped row offsets
     __shared__ int s_start[kMaxGroups + 1];  // ROWS: first m-tile of each expert; WGRAD: sorted order
     __shared__ int s_wave[16];
+    // GATHER: two buffers of 64 source indices per A load of each wave, and
+    // 1 KiB of slack behind them
+    __shared__ int s_idx[GATHER ? 2 * TL::kALoads * 64 + 256 : 1];
     for (int j = threadIdx.x; j <= p.e_local; j += TL::kThreads) {
         int64_t o = p.offsets[j];
         s_off[j] = (int)(o < p.cap ? o : p.cap);
@@ -744,11 +852,11 @@ void gg_kernel(GemmParams p) {
     __syncthreads();
     if constexpr (ALT != 0) {
         if (prefer_alt<BM, ALT, BN, EPI, TL::kThreads>(p, s_off, s_wave)) {
-            gg_body<ALT, BN, BK, WM, WN, LB, EPI, SCHED, LDSB>(p, smem, s_off, s_start, s_wave);
+            gg_body<ALT, BN, BK, WM, WN, LB, EPI, SCHED, LDSB, GATHER>(p, smem, s_off, s_start, s_wave, s_idx);
             return;
         }
     }
-    gg_body<BM, BN, BK, WM, WN, LB, EPI, SCHED, LDSB>(p, smem, s_off, s_start, s_wave);
+    gg_body<BM, BN, BK, WM, WN, LB, EPI, SCHED, LDSB, GATHER>(p, smem, s_off, s_start, s_wave, s_idx);
 }
 
 // Tile configurations.
@@ -776,7 +884,8 @@ static int tile_config() {
     return t == 128 ? CFG_SMALL : t == 192 ? CFG_MID : t == 256 ? CFG_BIG : CFG_AUTO;
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int LB, int EPI, int SCHED, int LDSB, int ALT = 0>
+template <int BM, int BN, int BK, int WM, int WN, int LB, int EPI, int SCHED, int LDSB, int ALT = 0,
+          bool GATHER = false>
 static int launch_cfg(const GemmParams& p, hipStream_t s) {
     using TL = Tile<BM, BN, BK, WM, WN, LDSB>;
     int64_t total_upper;
@@ -791,18 +900,21 @@ static int launch_cfg(const GemmParams& p, hipStream_t s) {
     int64_t g = std::min<int64_t>(total_upper, (int64_t)moe_host::num_cus() * per_cu);
     const int grid = (int)((g + 7) / 8 * 8);
     if (grid == 0) return MOE_OK;
-    gg_kernel<BM, BN, BK, WM, WN, LB, EPI, SCHED, LDSB, ALT><<<grid, TL::kThreads, 0, s>>>(p);
+    gg_kernel<BM, BN, BK, WM, WN, LB, EPI, SCHED, LDSB, ALT, GATHER><<<grid, TL::kThreads, 0, s>>>(p);
     return moe_host::launch_status();
 }
 
-template <int LB, int EPI, int SCHED>
+template <int LB, int EPI, int SCHED, bool GATHER = false>
 static int launch(const GemmParams& p, hipStream_t s) {
-    if (tile_config() == CFG_SMALL) return launch_cfg<128, 128, 32, 2, 2, LB, EPI, SCHED, kLdsBudget>(p, s);
+    if (tile_config() == CFG_SMALL)
+        return launch_cfg<128, 128, 32, 2, 2, LB, EPI, SCHED, kLdsBudget, 0, GATHER>(p, s);
     if constexpr (SCHED == SCHED_ROWS) {
-        if (tile_config() == CFG_MID) return launch_cfg<192, 256, 32, 2, 2, LB, EPI, SCHED, kLdsBudget>(p, s);
-        if (tile_config() == CFG_AUTO) return launch_cfg<256, 256, 32, 2, 2, LB, EPI, SCHED, kLdsBudget, 192>(p, s);
+        if (tile_config() == CFG_MID)
+            return launch_cfg<192, 256, 32, 2, 2, LB, EPI, SCHED, kLdsBudget, 0, GATHER>(p, s);
+        if (tile_config() == CFG_AUTO)
+            return launch_cfg<256, 256, 32, 2, 2, LB, EPI, SCHED, kLdsBudget, 192, GATHER>(p, s);
     }
-    return launch_cfg<256, 256, 32, 2, 2, LB, EPI, SCHED, kLdsBudget>(p, s);
+    return launch_cfg<256, 256, 32, 2, 2, LB, EPI, SCHED, kLdsBudget, 0, GATHER>(p, s);
 }
 
 }  // namespace moe
@@ -839,6 +951,46 @@ extern "C" int moe_grouped_gemm_swiglu(const moe_bf16* x_perm, const moe_bf16* w
     p.c2 = ab_save;
     if (H == 0) return MOE_EINVAL;
     return launch<LAY_MN, EPI_SWIGLU, SCHED_ROWS>(p, (hipStream_t)stream);
+}
+
+extern "C" int moe_grouped_gemm_swiglu_gather(const moe_bf16* x, int T, const int32_t* src, int K,
+                                              const moe_bf16* w_gate, const moe_bf16* w_up, const int32_t* offsets,
+                                              int e_local, int H, int F, int cap_rows, moe_bf16* h,
+                                              moe_bf16* ab_save, moe_stream stream) {
+    using namespace moe;
+    if (e_local < 0 || e_local > kMaxGroups || H <= 0 || F < 0 || cap_rows < 0 || T < 0 || K < 1 || K > 16)
+        return MOE_EINVAL;
+    if (H % 64 || F % 64) return MOE_ESHAPE;
+    // every A load offset (row * H * 2 + column bytes) must stay below the
+    // out-of-range offset that masks rows past an expert's end
+    if ((int64_t)T * H * 2 >= (1ll << 31) || (int64_t)64 * F * 2 >= (1ll << 31)) return MOE_EINVAL;
+    if ((int64_t)cap_rows > (int64_t)T * K) return MOE_EINVAL;
+    if (!offsets) return MOE_EINVAL;
+    if (e_local == 0 || cap_rows == 0 || F == 0) return MOE_OK;
+    if (!x || !src || !w_gate || !w_up || !h) return MOE_EINVAL;
+    if (misaligned(x) || misaligned(src) || misaligned(w_gate) || misaligned(w_up) || misaligned(offsets) ||
+        misaligned(h) || misaligned(ab_save))
+        return MOE_EALIGN;
+    GemmParams p{};
+    p.a = x;
+    p.lda = H;
+    p.src = src;
+    p.topk = K;
+    p.topk_rcp = 0xffffffffu / (uint32_t)K;
+    p.a_rows = T;
+    p.w0 = w_gate;
+    p.w1 = w_up;
+    p.w_stride = (int64_t)H * F;
+    p.ldw = F;
+    p.offsets = offsets;
+    p.e_local = e_local;
+    p.cap = cap_rows;
+    p.N = F;
+    p.Kd = H;
+    p.c = h;
+    p.ldc = F;
+    p.c2 = ab_save;
+    return launch<LAY_MN, EPI_SWIGLU, SCHED_ROWS, true>(p, (hipStream_t)stream);
 }
 
 extern "C" int moe_grouped_gemm(const moe_bf16* a, int lda, const moe_bf16* w0, const moe_bf16* w1, int trans_w,

@@ -256,7 +256,9 @@ extern "C" int moe_permute(const int32_t* topk_idx, int T, int K, int e_begin, i
     if (!offsets || !status) return MOE_EINVAL;
     if (e_local > 0 && !counts) return MOE_EINVAL;
     if (T > 0 && (!topk_idx || !pos)) return MOE_EINVAL;
-    if (cap_rows > 0 && (!src || (H > 0 && (!x || !x_perm)))) return MOE_EINVAL;
+    // x and x_perm both NULL: the index-only permutation (no row copy)
+    if ((x == nullptr) != (x_perm == nullptr)) return MOE_EINVAL;
+    if (cap_rows > 0 && !src) return MOE_EINVAL;
     if (misaligned(topk_idx) || misaligned(x) || misaligned(counts) || misaligned(offsets) ||
         misaligned(pos) || misaligned(src) || misaligned(x_perm) || misaligned(status) || misaligned(ws))
         return MOE_EALIGN;
@@ -277,7 +279,7 @@ extern "C" int moe_permute(const int32_t* topk_idx, int T, int K, int e_begin, i
         else
             perm_rank_kernel<16><<<nblk, 256, 0, s>>>(topk_idx, T, K, e_begin, e_local, nbits, nblk, w,
                                                      cap_rows, pos, src);
-        if (H > 0)
+        if (H > 0 && x_perm)
             perm_copy_kernel<4><<<(T + 3) / 4, 256, 0, s>>>((const u32x4*)x, T, K, H, pos, (u32x4*)x_perm);
     }
     return moe_host::launch_status();

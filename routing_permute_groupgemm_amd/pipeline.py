@@ -23,7 +23,7 @@ class MoeBuffers:
     offsets: torch.Tensor
     pos: torch.Tensor
     src: torch.Tensor
-    x_perm: torch.Tensor
+    x_perm: torch.Tensor | None  # None with zero_copy
     status: torch.Tensor
     ws: torch.Tensor
     h: torch.Tensor
@@ -40,10 +40,15 @@ class MoeBuffers:
     dw_down: torch.Tensor | None = None
     dgates: torch.Tensor | None = None
     dlogits: torch.Tensor | None = None
+    # zero-copy dispatch: the permutation is index-only and the gate/up
+    # GroupGEMM reads x[src[r] // K]; forward only (the weight gradient reads x_perm)
+    zero_copy: bool = False
 
     @classmethod
-    def allocate(cls, shape: MoeShape, cap: int | None = None, device="cuda", backward=None):
+    def allocate(cls, shape: MoeShape, cap: int | None = None, device="cuda", backward=None, zero_copy=False):
         backward = shape.backward if backward is None else backward
+        if zero_copy and backward:
+            raise ValueError("zero_copy is forward-only: the weight gradient reads x_perm")
         T, H, F, K, EL = shape.T, shape.H, shape.F, shape.K, shape.EL
         cap = shape.cap if cap is None else cap
         capn = max(cap, 1)
@@ -52,9 +57,10 @@ class MoeBuffers:
         b = cls(shape=shape, cap=cap,
                 topk_idx=e((T, K), dt=torch.int32), gates=e((T, K), dt=torch.float32),
                 counts=e(max(EL, 1), dt=torch.int32), offsets=e(EL + 1, dt=torch.int32),
-                pos=e((T, K), dt=torch.int32), src=e(capn, dt=torch.int32), x_perm=e((capn, H)),
+                pos=e((T, K), dt=torch.int32), src=e(capn, dt=torch.int32),
+                x_perm=None if zero_copy else e((capn, H)),
                 status=e(4, dt=torch.int32), ws=e(ws_bytes, dt=torch.uint8), h=e((capn, F)),
-                ab=e((capn, 2 * F)) if backward else None, y=e((capn, H)), out=e((T, H)))
+                ab=e((capn, 2 * F)) if backward else None, y=e((capn, H)), out=e((T, H)), zero_copy=zero_copy)
         if backward:
             b.dy_perm = e((capn, H))
             b.dab = e((capn, 2 * F))
@@ -76,11 +82,16 @@ def permute(buf: MoeBuffers, x):
     s = buf.shape
     _lib.moe_permute(buf.topk_idx, s.e_begin, s.EL, x, buf.cap,
                      out=dict(counts=buf.counts, offsets=buf.offsets, pos=buf.pos, src=buf.src,
-                              x_perm=buf.x_perm, status=buf.status), ws=buf.ws)
+                              x_perm=buf.x_perm, status=buf.status), ws=buf.ws, copy_rows=not buf.zero_copy)
 
 
-def expert_up(buf: MoeBuffers, w_gate, w_up):
-    _lib.moe_grouped_gemm_swiglu(buf.x_perm, w_gate, w_up, buf.offsets, buf.cap, h=buf.h, ab_save=buf.ab)
+def expert_up(buf: MoeBuffers, w_gate, w_up, x=None):
+    """x (the token rows) is needed with zero_copy only."""
+    if buf.zero_copy:
+        _lib.moe_grouped_gemm_swiglu_gather(x, buf.src, buf.shape.K, w_gate, w_up, buf.offsets, buf.cap,
+                                            h=buf.h, ab_save=buf.ab)
+    else:
+        _lib.moe_grouped_gemm_swiglu(buf.x_perm, w_gate, w_up, buf.offsets, buf.cap, h=buf.h, ab_save=buf.ab)
 
 
 def expert_down(buf: MoeBuffers, w_down):
@@ -96,7 +107,7 @@ def forward(buf: MoeBuffers, inp: dict):
     """inp: device tensors logits, x, w_gate, w_up, w_down."""
     route(buf, inp["logits"])
     permute(buf, inp["x"])
-    expert_up(buf, inp["w_gate"], inp["w_up"])
+    expert_up(buf, inp["w_gate"], inp["w_up"], inp["x"])
     expert_down(buf, inp["w_down"])
     combine(buf)
     return buf.out

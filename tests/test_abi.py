@@ -96,6 +96,22 @@ def test_permute_rejects():
     assert call(cap=33) == -1          # cap > T*K
     assert call(el=513) == -1
     assert call(offsets=None) == -1
+    assert call(xp=None) == -1         # x without x_perm
+    assert call(x=None) == -1          # x_perm without x
+
+
+def test_gather_gemm_rejects():
+    lib = _lib.load()
+    g = lib.moe_grouped_gemm_swiglu_gather
+    # (x, T, src, K, w_gate, w_up, offsets, e_local, H, F, cap, h, ab, stream)
+    assert g(FAKE, 64, FAKE, 2, FAKE, FAKE, FAKE, 4, 96, 64, 16, FAKE, None, None) == -2   # H % 64
+    assert g(FAKE, 64, FAKE, 2, FAKE, FAKE, None, 4, 64, 64, 16, FAKE, None, None) == -1   # no offsets
+    assert g(FAKE, 64, FAKE, 0, FAKE, FAKE, FAKE, 4, 64, 64, 16, FAKE, None, None) == -1   # K < 1
+    assert g(FAKE, 64, FAKE, 17, FAKE, FAKE, FAKE, 4, 64, 64, 16, FAKE, None, None) == -1  # K > 16
+    assert g(FAKE, 8, FAKE, 1, FAKE, FAKE, FAKE, 4, 64, 64, 16, FAKE, None, None) == -1    # cap > T*K
+    assert g(FAKE, 1 << 20, FAKE, 8, FAKE, FAKE, FAKE, 4, 1024, 64, 16, FAKE, None, None) == -1  # T*H*2 = 2^31
+    assert g(FAKE, 64, None, 2, FAKE, FAKE, FAKE, 4, 64, 64, 16, FAKE, None, None) == -1   # no src
+    assert g(FAKE, 64, MIS, 2, FAKE, FAKE, FAKE, 4, 64, 64, 16, FAKE, None, None) == -3    # misaligned
 
 
 def test_gemm_rejects():

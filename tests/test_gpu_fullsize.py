@@ -94,6 +94,22 @@ def test_expert_up_sampled_rows(case):
         assert_close("ab_save", bits(c.buf.ab)[rows], ab[rows])
 
 
+def test_zero_copy_gate_up_full(case):
+    """The zero-copy gate/up GroupGEMM (rows read from x through src) at full size, in the bench's
+    launch configuration: bit-identical to the copy path's h (and ab_save) for every row."""
+    c = case
+    s = c.shape
+    h = torch.zeros_like(c.buf.h)
+    ab = torch.zeros_like(c.buf.ab) if c.buf.ab is not None else None
+    _lib.moe_grouped_gemm_swiglu_gather(c.dev["x"], c.buf.src, s.K, c.dev["w_gate"], c.dev["w_up"], c.buf.offsets,
+                                        c.buf.cap, h=h, ab_save=ab)
+    torch.cuda.synchronize()
+    assert torch.equal(h[:c.R].view(torch.int16), c.buf.h[:c.R].view(torch.int16))
+    if ab is not None:
+        assert torch.equal(ab[:c.R].view(torch.int16), c.buf.ab[:c.R].view(torch.int16))
+    del h, ab
+
+
 def test_expert_down_sampled_rows(case):
     c = case
     s = c.shape
