@@ -113,9 +113,8 @@ size_t moe_permute_workspace_size(int T, int K, int e_local);
  *   pos      int32 [T,K] out: destination row of pair (t,k), or -1.
  *   src      int32 [cap_rows] out: src[pos[t,k]] = t*K+k.
  *   x_perm   bf16 [cap_rows,H] out: x_perm[pos[t,k]] = x[t] (bit copy).
- *            x and x_perm both NULL: the index-only permutation, no row
- *            copy (for moe_grouped_gemm_swiglu_gather); one of them NULL is
- *            MOE_EINVAL.
+ *            x_perm NULL: the index-only permutation, no row copy and x
+ *            not read (for moe_grouped_gemm_swiglu_gather).
  *   status   int32 [1] out: 0, or 1 if R > cap_rows (rows >= cap_rows are
  *            dropped: their pos is -1 and nothing is written for them;
  *            counts/offsets still hold the true totals).
@@ -181,8 +180,8 @@ int moe_grouped_gemm_swiglu(const moe_bf16* x_perm, const moe_bf16* w_gate,
  * dispatch puts tokens at their expert-grouped positions with no copy through
  * an intermediate buffer; on one GPU the GEMM reads each token where it
  * already is).  Row r of the expert-grouped
- * order is read from x[src[r] / K], so the index-only moe_permute (x and
- * x_perm NULL) replaces the row copy.  h and ab_save are bit-identical to
+ * order is read from x[src[r] / K], so the index-only moe_permute (x_perm
+ * NULL) replaces the row copy.  h and ab_save are bit-identical to
  * moe_grouped_gemm_swiglu on the x_perm that moe_permute would have written.
  *   x    bf16 [T,H], the tokens;  src int32 [cap_rows] from moe_permute
  *        (src[r] = t*K + k);  K the top-k of src's encoding;

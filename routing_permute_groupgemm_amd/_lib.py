@@ -142,7 +142,7 @@ def moe_permute(topk_idx, e_begin, e_local, x, cap_rows, out=None, ws=None, stre
     need = moe_permute_workspace_size(T, K, e_local)
     if ws is None or ws.numel() < need:
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
-    _check(load().moe_permute(_ptr(topk_idx), T, K, e_begin, e_local, _ptr(x) if copy_rows else None, H, cap_rows,
+    _check(load().moe_permute(_ptr(topk_idx), T, K, e_begin, e_local, _ptr(x), H, cap_rows,
                               _ptr(counts), _ptr(offsets), _ptr(pos), _ptr(src), _ptr(x_perm),
                               _ptr(status), _ptr(ws), ws.numel(), _stream(stream)))
     return dict(counts=counts[:e_local], offsets=offsets, pos=pos, src=src, x_perm=x_perm,

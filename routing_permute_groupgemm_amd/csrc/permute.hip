@@ -256,9 +256,9 @@ extern "C" int moe_permute(const int32_t* topk_idx, int T, int K, int e_begin, i
     if (!offsets || !status) return MOE_EINVAL;
     if (e_local > 0 && !counts) return MOE_EINVAL;
     if (T > 0 && (!topk_idx || !pos)) return MOE_EINVAL;
-    // x and x_perm both NULL: the index-only permutation (no row copy)
-    if ((x == nullptr) != (x_perm == nullptr)) return MOE_EINVAL;
+    // x_perm NULL: the index-only permutation (no row copy, x not read)
     if (cap_rows > 0 && !src) return MOE_EINVAL;
+    if (x_perm && T > 0 && cap_rows > 0 && H > 0 && !x) return MOE_EINVAL;
     if (misaligned(topk_idx) || misaligned(x) || misaligned(counts) || misaligned(offsets) ||
         misaligned(pos) || misaligned(src) || misaligned(x_perm) || misaligned(status) || misaligned(ws))
         return MOE_EALIGN;

@@ -96,8 +96,7 @@ def test_permute_rejects():
     assert call(cap=33) == -1          # cap > T*K
     assert call(el=513) == -1
     assert call(offsets=None) == -1
-    assert call(xp=None) == -1         # x without x_perm
-    assert call(x=None) == -1          # x_perm without x
+    assert call(x=None) == -1          # rows to copy but no x
 
 
 def test_gather_gemm_rejects():
