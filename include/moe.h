@@ -251,6 +251,40 @@ int moe_wgrad(const moe_bf16* a, int lda, const moe_bf16* b, int ldb,
               const int32_t* offsets, int e_local, int M, int N, int cap_rows,
               float* dw, moe_stream stream);
 
+/*
+ * Router projection (UniEP "MoE workflow": the router network produces each
+ * token's scores over the experts, from which routing takes the top-k):
+ *   logits[t,e] = sum_i x[t,i] * w_r[i,e]  (+ bias[e])      fp32 accumulate
+ *   x bf16 [T,H];  w_r bf16 [H,E];  bias fp32 [E] or NULL;  logits fp32 [T,E].
+ * When the tiles are too few to fill the GPU the contraction over H is cut
+ * into chunks whose fp32 partials are added in chunk order (then the bias):
+ * repeated calls on one device give identical bits.  H and E must be
+ * multiples of 64 (MOE_ESHAPE), E <= 4096.  ws: device workspace of at least
+ * moe_router_workspace_size(T, H, E) bytes (may be NULL when that is 0 for
+ * the forward; the backward always needs it).
+ * The routing step consumes logits; whether they come from here or from the
+ * caller, moe_route selects exactly on the fp32 values it is given.
+ */
+size_t moe_router_workspace_size(int T, int H, int E);
+int moe_router_logits(const moe_bf16* x, int T, int H, const moe_bf16* w_r, int E,
+                      const float* bias, float* logits, void* ws, size_t ws_bytes,
+                      moe_stream stream);
+
+/*
+ * Backward of the router projection, from the score gradient dlogits fp32
+ * [T,E] (moe_route_backward's output), rounded to bf16 like the other
+ * activation gradients of the path:
+ *   dx[t,i]   = bf16( sum_e bf16(dlogits[t,e]) * w_r[i,e] )   bf16 [T,H]
+ *   dw_r[i,e] = sum_t x[t,i] * bf16(dlogits[t,e])             fp32 [H,E]
+ * dx is the router's share of the input gradient only (the caller adds the
+ * experts' dX).  dw_r sums the tokens in fixed chunks added in chunk order
+ * (the non-bitwise-serial variant of the weight gradient: run-to-run
+ * identical, not the serial order).  Shapes and ws as moe_router_logits.
+ */
+int moe_router_backward(const moe_bf16* x, int T, int H, const moe_bf16* w_r, int E,
+                        const float* dlogits, moe_bf16* dx, float* dw_r, void* ws,
+                        size_t ws_bytes, moe_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

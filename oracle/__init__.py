@@ -61,9 +61,13 @@ def lib():
         L.oracle_wgrad.argtypes = [_p, _l, _p, _l, _p, _i, _i, _i, _l, _p, _i, _p, _i, _p]
         L.oracle_gate_grad.argtypes = [_p, _p, _p, _i, _i, _i, _p]
         L.oracle_route_backward.argtypes = [_p, _p, _p, _i, _i, _i, _p]
+        L.oracle_router_logits.argtypes = [_p, _p, _p, _i, _i, _i, _p, _i, _p]
+        L.oracle_round_bf16.argtypes = [_p, _l, _p]
+        L.oracle_router_dx.argtypes = [_p, _p, _i, _i, _i, _p, _i, _p]
         for name in ("oracle_route", "oracle_permute", "oracle_expert_up", "oracle_expert_down",
                      "oracle_combine", "oracle_bwd_gather", "oracle_bwd_down", "oracle_bwd_up",
-                     "oracle_wgrad", "oracle_gate_grad", "oracle_route_backward"):
+                     "oracle_wgrad", "oracle_gate_grad", "oracle_route_backward", "oracle_router_logits",
+                     "oracle_round_bf16", "oracle_router_dx"):
             getattr(L, name).restype = None
     return _lib
 
@@ -216,6 +220,41 @@ def route_backward(topk_idx, gates, dgates, E):
     dl = np.empty((T, E), np.float32)
     lib().oracle_route_backward(_ptr(topk_idx), _ptr(gates), _ptr(dgates), T, E, K, _ptr(dl))
     return dl
+
+
+def router_logits(x, w_r, bias=None, rows=None):
+    """logits f32[T,E] = fp32(x . w_r in fp64) + bias; only `rows` are filled if given (others 0)."""
+    x, w_r = _c(x, np.uint16), _c(w_r, np.uint16)
+    T, H = x.shape
+    E = w_r.shape[1]
+    b = None if bias is None else _c(bias, np.float32)
+    out = np.zeros((T, E), np.float32)
+    r = _rows(rows)
+    lib().oracle_router_logits(_ptr(x), _ptr(w_r), _ptr(b), T, H, E, _ptr(r), 0 if r is None else len(r),
+                               _ptr(out))
+    return out
+
+
+def round_bf16(a):
+    """fp32 array -> bf16 bit patterns, nearest even."""
+    a = _c(a, np.float32)
+    out = np.empty(a.shape, np.uint16)
+    lib().oracle_round_bf16(_ptr(a), a.size, _ptr(out))
+    return out
+
+
+def router_backward(x, w_r, dlogits, rows=None, cols=None):
+    """-> (dx u16[T,H] (only `rows` filled if given), dw_r f32[H,E] (only `cols` if given)) of the
+    router projection, from bf16(dlogits)."""
+    x, w_r = _c(x, np.uint16), _c(w_r, np.uint16)
+    T, H = x.shape
+    E = w_r.shape[1]
+    dl = round_bf16(dlogits)
+    dx = np.zeros((T, H), np.uint16)
+    r = _rows(rows)
+    lib().oracle_router_dx(_ptr(dl), _ptr(w_r), T, H, E, _ptr(r), 0 if r is None else len(r), _ptr(dx))
+    dw = wgrad(x, H, dl, E, np.array([0, T], np.int32), H, E, T, cols=cols)[0]
+    return dx, dw
 
 
 def forward(inp: dict, e_begin: int, e_local: int, K: int, cap: int):

@@ -421,3 +421,55 @@ void oracle_route_backward(const int32_t* topk_idx, const float* gates, const fl
         for (int k = 0; k < K; ++k) row[topk_idx[(int64_t)t * K + k]] = g[k] * (dg[k] - sum);
     }
 }
+
+/* ---- R3: router projection ----------------------------------------------
+ * UniEP "MoE workflow": the router network scores every token against every
+ * expert.  The scores are the token times the router weight, plus the
+ * per-expert bias of the synthetic routing recipe:
+ *   logits[t,e] = fp32( sum_i x[t,i] * W_r[i,e] ) + bias[e]
+ * with the sum in fp64, i ascending (the definition the scores handed to the
+ * routing step are made by; the fp64 sum is exact enough that its rounding
+ * to fp32 is the correctly rounded dot product but for ties), then one fp32
+ * add of the bias.  Only `rows` (if given) are filled.
+ */
+void oracle_router_logits(const uint16_t* x, const uint16_t* w_r, const float* bias, int T, int H, int E,
+                          const int64_t* rows, int n_rows, float* logits) {
+    int n = rows ? n_rows : T;
+#pragma omp parallel for schedule(static)
+    for (int ri = 0; ri < n; ++ri) {
+        int64_t t = rows ? rows[ri] : ri;
+        for (int e = 0; e < E; ++e) {
+            double acc = 0.0;
+            for (int i = 0; i < H; ++i) acc += (double)bf(x[t * H + i]) * (double)bf(w_r[(int64_t)i * E + e]);
+            float v = (float)acc;
+            if (bias) v = v + bias[e];
+            logits[t * E + e] = v;
+        }
+    }
+}
+
+/* ---- R4: router projection backward --------------------------------------
+ * The gradient of logits = x . W_r with respect to x, from the score
+ * gradient rounded to bf16 (as every stored activation gradient of the path):
+ *   dx[t,i] = bf16( sum_e dl[t,e] * W_r[i,e] ),   e ascending, fp32
+ * (the weight gradient, sum_t x[t,i] * dl[t,e], is oracle_wgrad over the one
+ * group of all T rows).  oracle_round_bf16 gives dl = bf16(dlogits).
+ */
+void oracle_round_bf16(const float* in, int64_t n, uint16_t* out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) out[i] = rne(in[i]);
+}
+
+void oracle_router_dx(const uint16_t* dl, const uint16_t* w_r, int T, int H, int E, const int64_t* rows,
+                      int n_rows, uint16_t* dx) {
+    int n = rows ? n_rows : T;
+#pragma omp parallel for schedule(static)
+    for (int ri = 0; ri < n; ++ri) {
+        int64_t t = rows ? rows[ri] : ri;
+        for (int i = 0; i < H; ++i) {
+            float acc = 0.0f;
+            for (int e = 0; e < E; ++e) acc += bf(dl[t * E + e]) * bf(w_r[(int64_t)i * E + e]);
+            dx[t * H + i] = rne(acc);
+        }
+    }
+}

@@ -33,6 +33,9 @@ SIGNATURES = {
     "moe_grouped_gemm": ([_p, _i, _p, _p, _i, _p, _i, _i, _i, _i, _i, _p, _p, _i, _p], _i),
     "moe_combine": ([_p, _p, _p, _i, _i, _i, _p, _p], _i),
     "moe_wgrad": ([_p, _i, _p, _i, _p, _i, _i, _i, _i, _p, _p], _i),
+    "moe_router_workspace_size": ([_i, _i, _i], _z),
+    "moe_router_logits": ([_p, _i, _i, _p, _i, _p, _p, _p, _z, _p], _i),
+    "moe_router_backward": ([_p, _i, _i, _p, _i, _p, _p, _p, _p, _z, _p], _i),
 }
 
 MOE_EPI_NONE = 0
@@ -253,3 +256,47 @@ def moe_wgrad(a, lda, b, ldb, offsets, e_local, M, N, cap_rows, dw=None, a_col0=
     _check(load().moe_wgrad(pa, lda, pb, ldb, _ptr(offsets), e_local, M, N, cap_rows, _ptr(dw),
                             _stream(stream)))
     return dw
+
+
+def moe_router_workspace_size(T, H, E) -> int:
+    return int(load().moe_router_workspace_size(T, H, E))
+
+
+def _router_ws(T, H, E, ws, dev):
+    need = moe_router_workspace_size(T, H, E)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    return ws
+
+
+def moe_router_logits(x, w_r, bias=None, logits=None, ws=None, stream=None):
+    """logits fp32 [T,E] = x . w_r (+ bias)."""
+    _need(x, torch.bfloat16, "x")
+    _need(w_r, torch.bfloat16, "w_r")
+    if bias is not None:
+        _need(bias, torch.float32, "bias")
+    T, H = x.shape
+    E = w_r.shape[1]
+    if logits is None:
+        logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    ws = _router_ws(T, H, E, ws, x.device)
+    _check(load().moe_router_logits(_ptr(x), T, H, _ptr(w_r), E, _ptr(bias), _ptr(logits), _ptr(ws), ws.numel(),
+                                    _stream(stream)))
+    return logits
+
+
+def moe_router_backward(x, w_r, dlogits, dx=None, dw_r=None, ws=None, stream=None):
+    """-> (dx bf16 [T,H], dw_r fp32 [H,E]) of the router projection."""
+    _need(x, torch.bfloat16, "x")
+    _need(w_r, torch.bfloat16, "w_r")
+    _need(dlogits, torch.float32, "dlogits")
+    T, H = x.shape
+    E = w_r.shape[1]
+    if dx is None:
+        dx = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    if dw_r is None:
+        dw_r = torch.empty((H, E), dtype=torch.float32, device=x.device)
+    ws = _router_ws(T, H, E, ws, x.device)
+    _check(load().moe_router_backward(_ptr(x), T, H, _ptr(w_r), E, _ptr(dlogits), _ptr(dx), _ptr(dw_r), _ptr(ws),
+                                      ws.numel(), _stream(stream)))
+    return dx, dw_r

@@ -83,6 +83,16 @@ struct GemmParams {
     int topk;
     uint32_t topk_rcp;    // floor((2^32 - 1) / topk): src / topk without a divide
     int64_t a_rows;       // ROWS gather: rows of a (bounds every A load)
+    // Dense operands, no offsets array: offsets[j] = min(j * row_chunk, dense_rows)
+    // (ROWS: one group of all rows; WGRAD: the rows in chunks, one partial each)
+    int dense_rows;
+    int row_chunk;
+    // ROWS: the contraction in ksplit chunks of kchunk elements (a multiple of
+    // BK); with EPI_F32, chunk ks writes its partial result at cf + ks*part_stride
+    int ksplit;
+    int kchunk;
+    int64_t part_stride;
+    const float* bias;    // ROWS EPI_F32: added to every row, [N]
 };
 
 typedef __attribute__((ext_vector_type(4))) int i32x4;
@@ -269,7 +279,7 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
         }
         if (tid == TL::kThreads - 1) s_start[EL] = run;
         __syncthreads();
-        n_tiles_total = s_start[EL] * tiles_n;
+        n_tiles_total = s_start[EL] * tiles_n * max(p.ksplit, 1);
     } else {
         tiles_mw = (p.M + BM - 1) / BM;
         tiles_n = tiles_mw * ((p.N + BN - 1) / BN);
@@ -315,12 +325,18 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
 
     // ---- tile decode (identical in every lane) ----
     struct TileDesc {
-        int j, row0, valid, ni, mi_w, KT;
+        int j, row0, valid, ni, mi_w, KT, ks;
     };
     auto decode = [&](int tile) {
-        int j, row0 = 0, valid = 0, ni = 0, mi_w = 0, KT;
+        int j, row0 = 0, valid = 0, ni = 0, mi_w = 0, KT, ks = 0;
         if (SCHED == SCHED_ROWS) {
             const int MT = s_start[EL];
+            // contraction chunks outermost: the tiles in flight share the
+            // chunk's columns of A and rows of B
+            if (p.ksplit > 1) {
+                ks = tile / (MT * tiles_n);
+                tile -= ks * MT * tiles_n;
+            }
             const int grp = tile / (kGroupM * tiles_n);
             const int first = grp * kGroupM;
             const int gsz = min(kGroupM, MT - first);
@@ -336,7 +352,8 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
             j = lo;
             row0 = s_off[j] + (mi - s_start[j]) * BM;
             valid = min(BM, s_off[j + 1] - row0);
-            KT = (p.two_seg ? 2 * p.Kd : p.Kd) / BK;
+            const int kd = p.two_seg ? 2 * p.Kd : p.Kd;
+            KT = (p.ksplit > 1 ? min(p.kchunk, kd - ks * p.kchunk) : kd) / BK;
         } else {
             j = s_start[tile / tiles_n];
             // within a group: runs of kGroupN output-column tiles, rows fastest,
@@ -361,6 +378,7 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
         d.ni = __builtin_amdgcn_readfirstlane(ni);
         d.mi_w = __builtin_amdgcn_readfirstlane(mi_w);
         d.KT = __builtin_amdgcn_readfirstlane(KT);
+        d.ks = __builtin_amdgcn_readfirstlane(ks);
         return d;
     };
 
@@ -372,7 +390,7 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
     const int G = gridDim.x;
     const int tile0 = xcd_remap(blockIdx.x, G);
     int itile = tile0, ik = 0;
-    TileDesc ic = {0, 0, 0, 0, 0, 0};
+    TileDesc ic = {0, 0, 0, 0, 0, 0, 0};
     // buffer descriptors of the issue cursor's tile (row-tiled GEMMs), built
     // once per tile: the A rows, and the B weight of each half / segment
     i32x4 c_srdA = {0, 0, 0, 0}, c_srdB0 = {0, 0, 0, 0}, c_srdB1 = {0, 0, 0, 0};
@@ -444,17 +462,21 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
                     prefetch_rows(itile + G, idx_buf);
                     pf_issued = true;
                 }
-            } else {
-                c_srdA = make_srd(p.a + (int64_t)ic.row0 * p.lda, (uint32_t)(ic.valid * p.lda * 2));
             }
+            // first contraction index of the tile's chunk (0 without a split):
+            // the descriptors start there, and their ranges still end where the
+            // rows end, since kofs + chunk <= Kd <= the row stride
+            const int64_t kofs = (int64_t)ic.ks * p.kchunk;
+            if (!GATHER)
+                c_srdA = make_srd(p.a + (int64_t)ic.row0 * p.lda + kofs, (uint32_t)((ic.valid * p.lda - kofs) * 2));
             if (LB == LAY_MN) {
-                const uint32_t range = (uint32_t)(p.Kd * p.ldw * 2);
-                c_srdB0 = make_srd(p.w0 + (int64_t)ic.j * p.w_stride, range);
-                if (EPI == EPI_SWIGLU) c_srdB1 = make_srd(p.w1 + (int64_t)ic.j * p.w_stride, range);
+                const uint32_t range = (uint32_t)((p.Kd - kofs) * p.ldw * 2);
+                c_srdB0 = make_srd(p.w0 + (int64_t)ic.j * p.w_stride + kofs * p.ldw, range);
+                if (EPI == EPI_SWIGLU) c_srdB1 = make_srd(p.w1 + (int64_t)ic.j * p.w_stride + kofs * p.ldw, range);
             } else {
                 const int n0 = ic.ni * BN;
-                const uint32_t range = (uint32_t)(min(BN, p.N - n0) * p.ldw * 2);
-                c_srdB0 = make_srd(p.w0 + (int64_t)ic.j * p.w_stride + (int64_t)n0 * p.ldw, range);
+                const uint32_t range = (uint32_t)((min(BN, p.N - n0) * p.ldw - kofs) * 2);
+                c_srdB0 = make_srd(p.w0 + (int64_t)ic.j * p.w_stride + (int64_t)n0 * p.ldw + kofs, range);
                 if (p.two_seg) c_srdB1 = make_srd(p.w1 + (int64_t)ic.j * p.w_stride + (int64_t)n0 * p.ldw, range);
             }
             // opaque from here on: kept in SGPRs rather than rebuilt from the
@@ -606,7 +628,7 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
     unsigned gs = 0;  // global stage index of this workgroup; its LDS slot is gs % S
     for (int tile = tile0; tile < n_tiles_total; tile += G) {
         const TileDesc cd = decode(tile);
-        const int j = cd.j, row0 = cd.row0, valid = cd.valid, ni = cd.ni, mi_w = cd.mi_w, KT = cd.KT;
+        const int j = cd.j, row0 = cd.row0, valid = cd.valid, ni = cd.ni, mi_w = cd.mi_w, KT = cd.KT, ks = cd.ks;
 #pragma unroll
         for (int a = 0; a < MTW; ++a)
 #pragma unroll
@@ -698,10 +720,22 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
                         if (EPI == EPI_BF16) {
                             const int n = ni * BN + wn * (BN / WN) + 64 * np + 8 * c;
                             if (mloc < valid && n < p.N) *(u32x4*)(p.c + (int64_t)(row0 + mloc) * p.ldc + n) = v;
-                        } else {
+                        } else if (SCHED == SCHED_WGRAD) {
                             const int m = mi_w * BM + mloc;
                             const int n = ni * BN + wn * (BN / WN) + 32 * np + 4 * c;
                             if (m < p.M && n < p.N) *(u32x4*)(p.cf + ((int64_t)j * p.M + m) * p.N + n) = v;
+                        } else {
+                            // row-tiled fp32 output: one partial per contraction chunk
+                            const int n = ni * BN + wn * (BN / WN) + 32 * np + 4 * c;
+                            if (mloc < valid && n < p.N) {
+                                u32x4 w = v;
+                                if (p.bias) {
+                                    f32x4 f = __builtin_bit_cast(f32x4, v);
+                                    f += *(const f32x4*)(p.bias + n);
+                                    w = __builtin_bit_cast(u32x4, f);
+                                }
+                                *(u32x4*)(p.cf + ks * p.part_stride + (int64_t)(row0 + mloc) * p.ldc + n) = w;
+                            }
                         }
                     }
                 }
@@ -846,7 +880,7 @@ void gg_kernel(GemmParams p) {
     // 1 KiB of slack behind them
     __shared__ int s_idx[GATHER ? 2 * TL::kALoads * 64 + 256 : 1];
     for (int j = threadIdx.x; j <= p.e_local; j += TL::kThreads) {
-        int64_t o = p.offsets[j];
+        const int64_t o = p.offsets ? (int64_t)p.offsets[j] : min((int64_t)j * p.row_chunk, (int64_t)p.dense_rows);
         s_off[j] = (int)(o < p.cap ? o : p.cap);
     }
     __syncthreads();
@@ -892,7 +926,7 @@ static int launch_cfg(const GemmParams& p, hipStream_t s) {
     if (SCHED == SCHED_ROWS) {
         const int tn = EPI == EPI_SWIGLU ? (p.N + BN / 2 - 1) / (BN / 2) : (p.N + BN - 1) / BN;
         constexpr int bm = ALT && ALT < BM ? ALT : BM;
-        total_upper = ((p.cap + bm - 1) / bm + p.e_local) * (int64_t)tn;
+        total_upper = ((p.cap + bm - 1) / bm + p.e_local) * (int64_t)tn * std::max(p.ksplit, 1);
     } else {
         total_upper = (int64_t)p.e_local * ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
     }
@@ -1062,4 +1096,152 @@ extern "C" int moe_wgrad(const moe_bf16* a, int lda, const moe_bf16* b, int ldb,
     p.N = N;
     p.cf = dw;
     return launch<LAY_MN, EPI_F32, SCHED_WGRAD>(p, (hipStream_t)stream);
+}
+
+// ---- router projection -------------------------------------------------------
+// Dense GEMMs on the same kernel: one group of all T rows (no offsets array).
+// Few output tiles (E columns) would leave most of the chip idle, so the
+// contraction is cut into chunks, each leaving an fp32 partial that a second
+// pass adds in chunk order: the result is fixed for a given device, whatever
+// the scheduling.
+
+namespace moe {
+
+// Chunks of a contraction of kt_total steps so that `tiles` output tiles
+// become about one workgroup per compute unit, each chunk at least 8 steps.
+static void split_steps(int64_t tiles, int64_t kt_total, int* n_chunks, int* steps) {
+    kt_total = std::max<int64_t>(kt_total, 1);  // no tokens: one (empty) chunk
+    const int64_t cus = moe_host::num_cus();
+    int64_t s = std::min<int64_t>((cus + tiles - 1) / std::max<int64_t>(tiles, 1), std::max<int64_t>(kt_total / 8, 1));
+    s = std::max<int64_t>(s, 1);
+    const int64_t st = (kt_total + s - 1) / s;
+    *steps = (int)st;
+    *n_chunks = (int)((kt_total + st - 1) / st);
+}
+
+struct RouterPlan {
+    int fwd_chunks, fwd_steps;    // forward: contraction over H in chunks of fwd_steps * 32
+    int bwd_chunks, bwd_rows;     // weight gradient: token rows in chunks of bwd_rows
+    size_t fwd_bytes, bwd_bytes;  // workspace
+};
+
+static size_t round256(size_t b) { return (b + 255) / 256 * 256; }
+
+static RouterPlan router_plan(int T, int H, int E) {
+    RouterPlan r{};
+    split_steps((int64_t)((T + 255) / 256) * ((E + 255) / 256), H / 32, &r.fwd_chunks, &r.fwd_steps);
+    int steps;
+    split_steps((int64_t)((H + 255) / 256) * ((E + 255) / 256), (T + 31) / 32, &r.bwd_chunks, &steps);
+    r.bwd_rows = steps * 32;
+    r.bwd_chunks = std::max(1, (T + r.bwd_rows - 1) / r.bwd_rows);
+    r.fwd_bytes = r.fwd_chunks > 1 ? (size_t)r.fwd_chunks * T * E * 4 : 0;
+    r.bwd_bytes = round256((size_t)T * E * 2) + (r.bwd_chunks > 1 ? (size_t)r.bwd_chunks * H * E * 4 : 0);
+    return r;
+}
+
+static int router_check(int T, int H, int E) {
+    if (T < 0 || H <= 0 || E <= 0 || E > 4096) return MOE_EINVAL;
+    if (H % 64 || E % 64) return MOE_ESHAPE;
+    // every buffer descriptor spans at most 256 rows of x or all of W_r
+    if ((int64_t)T * E >= (1ll << 31) || (int64_t)T * H >= (1ll << 40) || (int64_t)256 * H * 2 >= (1ll << 31) ||
+        (int64_t)H * E * 2 >= (1ll << 31))
+        return MOE_EINVAL;
+    return MOE_OK;
+}
+
+}  // namespace moe
+
+extern "C" size_t moe_router_workspace_size(int T, int H, int E) {
+    using namespace moe;
+    if (router_check(T, H, E) != MOE_OK) return 0;
+    const RouterPlan r = router_plan(T, H, E);
+    return std::max(r.fwd_bytes, r.bwd_bytes) + 256;
+}
+
+extern "C" int moe_router_logits(const moe_bf16* x, int T, int H, const moe_bf16* w_r, int E, const float* bias,
+                                 float* logits, void* ws, size_t ws_bytes, moe_stream stream) {
+    using namespace moe;
+    const int st = router_check(T, H, E);
+    if (st != MOE_OK) return st;
+    if (T == 0) return MOE_OK;
+    if (!x || !w_r || !logits) return MOE_EINVAL;
+    if (misaligned(x) || misaligned(w_r) || misaligned(bias) || misaligned(logits) || misaligned(ws))
+        return MOE_EALIGN;
+    const RouterPlan r = router_plan(T, H, E);
+    if (r.fwd_bytes && (!ws || ws_bytes < r.fwd_bytes)) return MOE_EWORKSPACE;
+    const bool split = r.fwd_chunks > 1;
+    GemmParams p{};
+    p.a = x;
+    p.lda = H;
+    p.w0 = w_r;
+    p.ldw = E;
+    p.dense_rows = T;
+    p.row_chunk = T;
+    p.e_local = 1;
+    p.cap = T;
+    p.N = E;
+    p.Kd = H;
+    p.cf = split ? (float*)ws : logits;
+    p.ldc = E;
+    p.ksplit = r.fwd_chunks;
+    p.kchunk = r.fwd_steps * 32;
+    p.part_stride = (int64_t)T * E;
+    p.bias = split ? nullptr : bias;
+    hipStream_t s = (hipStream_t)stream;
+    int rc = launch<LAY_MN, EPI_F32, SCHED_ROWS>(p, s);
+    if (rc != MOE_OK || !split) return rc;
+    return moe_host::sum_partials((const float*)ws, r.fwd_chunks, (int64_t)T * E, (int64_t)T * E, bias, E, logits, s);
+}
+
+extern "C" int moe_router_backward(const moe_bf16* x, int T, int H, const moe_bf16* w_r, int E, const float* dlogits,
+                                   moe_bf16* dx, float* dw_r, void* ws, size_t ws_bytes, moe_stream stream) {
+    using namespace moe;
+    const int st = router_check(T, H, E);
+    if (st != MOE_OK) return st;
+    if (!w_r || !dw_r || (T > 0 && (!x || !dlogits || !dx))) return MOE_EINVAL;
+    if (misaligned(x) || misaligned(w_r) || misaligned(dlogits) || misaligned(dx) || misaligned(dw_r) ||
+        misaligned(ws))
+        return MOE_EALIGN;
+    const RouterPlan r = router_plan(T, H, E);
+    if (!ws || ws_bytes < r.bwd_bytes) return MOE_EWORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    uint16_t* dl16 = (uint16_t*)ws;
+    float* part = (float*)((char*)ws + round256((size_t)T * E * 2));
+    int rc = moe_host::cast_f32_bf16(dlogits, (int64_t)T * E, dl16, s);
+    if (rc != MOE_OK) return rc;
+    // dx = bf16(dlogits) . W_r^T: W_r [H][E] is the [N][Kd] weight, contraction contiguous
+    GemmParams p{};
+    p.a = dl16;
+    p.lda = E;
+    p.w0 = w_r;
+    p.ldw = E;
+    p.dense_rows = T;
+    p.row_chunk = T;
+    p.e_local = 1;
+    p.cap = T;
+    p.N = H;
+    p.Kd = E;
+    p.c = dx;
+    p.ldc = H;
+    if (T > 0) {
+        rc = launch<LAY_KC, EPI_BF16, SCHED_ROWS>(p, s);
+        if (rc != MOE_OK) return rc;
+    }
+    // dW_r = x^T . bf16(dlogits): the token rows in chunks, one fp32 partial each
+    const bool split = r.bwd_chunks > 1;
+    GemmParams q{};
+    q.a = x;
+    q.lda = H;
+    q.b = dl16;
+    q.ldb = E;
+    q.dense_rows = T;
+    q.row_chunk = r.bwd_rows;
+    q.e_local = r.bwd_chunks;
+    q.cap = T;
+    q.M = H;
+    q.N = E;
+    q.cf = split ? part : dw_r;
+    rc = launch<LAY_MN, EPI_F32, SCHED_WGRAD>(q, s);
+    if (rc != MOE_OK || !split) return rc;
+    return moe_host::sum_partials(part, r.bwd_chunks, (int64_t)H * E, (int64_t)H * E, nullptr, E, dw_r, s);
 }

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "moe.h"
 
 namespace moe {
@@ -52,6 +54,12 @@ namespace moe_host {
 inline bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
 int num_cus();  // compute units of the current device (cached per device)
+
+// Elementwise passes of the router (router.hip).  n and stride count floats;
+// n, stride and period are multiples of 4 (n of 8 for the cast).
+int sum_partials(const float* part, int S, int64_t n, int64_t stride, const float* bias, int period, float* out,
+                 hipStream_t s);
+int cast_f32_bf16(const float* in, int64_t n, uint16_t* out, hipStream_t s);
 
 inline int launch_status() {
     hipError_t e = hipGetLastError();

@@ -165,18 +165,25 @@ def router_logits(x_bits: np.ndarray, wr_bits: np.ndarray, bias: np.ndarray) -> 
 
 
 def make_inputs(shape: MoeShape, seed: int = 0, *, weights: bool = True,
-                d_out: bool | None = None, alpha: float | None = None) -> dict[str, np.ndarray]:
+                d_out: bool | None = None, alpha: float | None = None,
+                router: bool = False) -> dict[str, np.ndarray]:
     """All inputs of one layer pass as numpy arrays (bf16 as uint16 bit patterns).
 
     Keys: logits f32[T,E]; x u16[T,H]; w_gate, w_up u16[E_L,H,F];
-    w_down u16[E_L,F,H]; d_out u16[T,H] (when the backward is wanted).
+    w_down u16[E_L,F,H]; d_out u16[T,H] (when the backward is wanted);
+    with router=True also w_router u16[H,E] and router_bias f32[E], the
+    operands the logits were made from.
     """
     ss = _seedseq(shape, seed)
     T, H, F, E, EL = shape.T, shape.H, shape.F, shape.E, shape.EL
     out: dict[str, np.ndarray] = {}
     out["x"] = normal_bf16(ss["x"], (T, H), 1.0)
     wr = normal_bf16(ss["w_router"], (H, E), 0.02)
-    out["logits"] = router_logits(out["x"], wr, zipf_bias(shape, ss["perm"], alpha))
+    bias = zipf_bias(shape, ss["perm"], alpha)
+    out["logits"] = router_logits(out["x"], wr, bias)
+    if router:
+        out["w_router"] = wr
+        out["router_bias"] = bias
     if weights:
         out["w_gate"] = normal_bf16(ss["w_gate"], (EL, H, F), 0.02)
         out["w_up"] = normal_bf16(ss["w_up"], (EL, H, F), 0.02)

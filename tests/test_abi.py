@@ -22,7 +22,8 @@ def declared_symbols():
 def test_header_declares_the_entry_points():
     names = declared_symbols()
     for need in ("moe_route", "moe_permute", "moe_grouped_gemm_swiglu", "moe_grouped_gemm", "moe_combine",
-                 "moe_wgrad", "moe_gather", "moe_gather_gate_grad", "moe_route_backward"):
+                 "moe_wgrad", "moe_gather", "moe_gather_gate_grad", "moe_route_backward",
+                 "moe_grouped_gemm_swiglu_gather", "moe_router_logits", "moe_router_backward"):
         assert need in names
 
 
@@ -97,6 +98,27 @@ def test_permute_rejects():
     assert call(el=513) == -1
     assert call(offsets=None) == -1
     assert call(x=None) == -1          # rows to copy but no x
+
+
+def test_router_rejects():
+    lib = _lib.load()
+    # (x, T, H, w_r, E, bias, logits, ws, ws_bytes, stream)
+    assert lib.moe_router_logits(FAKE, 64, 128, FAKE, 8, None, FAKE, FAKE, 1 << 20, None) == -2    # E % 64
+    assert lib.moe_router_logits(FAKE, 64, 96, FAKE, 64, None, FAKE, FAKE, 1 << 20, None) == -2    # H % 64
+    assert lib.moe_router_logits(FAKE, -1, 128, FAKE, 64, None, FAKE, FAKE, 1 << 20, None) == -1
+    assert lib.moe_router_logits(FAKE, 64, 128, None, 64, None, FAKE, FAKE, 1 << 20, None) == -1
+    assert lib.moe_router_logits(FAKE, 64, 128, FAKE, 64, MIS, FAKE, FAKE, 1 << 20, None) == -3
+    # a split contraction needs the workspace
+    T, H, E = 512, 7168, 256
+    need = lib.moe_router_workspace_size(T, H, E)
+    assert need > 0
+    assert lib.moe_router_logits(FAKE, T, H, FAKE, E, None, FAKE, None, 0, None) == -4
+    assert lib.moe_router_logits(FAKE, T, H, FAKE, E, None, FAKE, FAKE, 256, None) == -4
+    # (x, T, H, w_r, E, dlogits, dx, dw_r, ws, ws_bytes, stream): the backward always needs it
+    assert lib.moe_router_backward(FAKE, T, H, FAKE, E, FAKE, FAKE, FAKE, None, 0, None) == -4
+    assert lib.moe_router_backward(FAKE, T, H, FAKE, E, FAKE, FAKE, None, FAKE, need, None) == -1
+    assert lib.moe_router_backward(FAKE, T, H, FAKE, 8, FAKE, FAKE, FAKE, FAKE, need, None) == -2
+    assert lib.moe_router_workspace_size(T, H, 8) == 0
 
 
 def test_gather_gemm_rejects():

@@ -1,0 +1,119 @@
+"""Router projection and its backward on the GPU against the CPU oracle.
+
+logits = x . W_r + bias (fp32), and from a score gradient dlogits:
+dx = bf16(bf16(dlogits) . W_r^T), dW_r = x^T . bf16(dlogits) (fp32).  Floating
+outputs must satisfy |gpu - oracle| <= 1e-2 + 1e-2*|oracle| (and the logits a
+tighter fp32-sum bound); reruns must be bitwise identical.  The GPU's top-k
+on its own logits is checked as a property (the chosen set is the exact
+top-K of those fp32 values under score desc, id asc), not against the
+oracle, since no oracle input may come from the GPU."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import assert_close, assert_equal
+from routing_permute_groupgemm_amd import _lib, pipeline, synth
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS
+# (shape, why): contraction split or not, E of 64/128/256, ragged T, long H
+SMALL = [
+    (W["ep_share_4k"].scaled(T=512, H=256), "E=256, weight gradient in 2 row chunks"),
+    (W["ep_share_4k"].scaled(T=512, H=1024), "E=256, contraction in 4 chunks"),
+    (W["skew_8k"].scaled(T=1000, H=256), "E=128, skew bias, ragged T"),
+    (synth.MoeShape("e64", 91, T=2048, H=128, F=64, E=64, K=4), "E=64"),
+    (W["ep_share_4k"].scaled(T=64, H=7168), "few rows, long contraction"),
+    (W["fwdbwd_16k"].scaled(T=4096, H=192), "many rows, short contraction"),
+]
+
+
+def bits(t):
+    return pipeline.to_numpy_bits(t)
+
+
+def dlogits_for(T, E, seed):
+    return (np.random.default_rng(seed).standard_normal((T, E)) * 0.1).astype(np.float32)
+
+
+def topk_property(logits, idx):
+    """idx[t] must be the first K experts of logits[t] under (score desc, id asc)."""
+    T, E = logits.shape
+    K = idx.shape[1]
+    s = logits.astype(np.float64) + 0.0  # -0 and +0 compare equal
+    order = np.lexsort((np.broadcast_to(np.arange(E), (T, E)), -s), axis=1)
+    assert_equal("topk_idx (property)", idx, order[:, :K].astype(np.int32))
+
+
+@pytest.mark.parametrize("k", range(len(SMALL)))
+def test_router_logits_and_backward(k):
+    shape, why = SMALL[k]
+    T, H, E = shape.T, shape.H, shape.E
+    print(f"[router] {why}: T={T} H={H} E={E} ws={_lib.moe_router_workspace_size(T, H, E)}", flush=True)
+    inp = synth.make_inputs(shape, seed=2, weights=False, router=True)
+    dev = pipeline.to_device(inp)
+    logits = _lib.moe_router_logits(dev["x"], dev["w_router"], dev["router_bias"])
+    logits2 = _lib.moe_router_logits(dev["x"], dev["w_router"], dev["router_bias"])
+    dl = dlogits_for(T, E, 5)
+    dx, dw = _lib.moe_router_backward(dev["x"], dev["w_router"], torch.from_numpy(dl).cuda())
+    dx2, dw2 = _lib.moe_router_backward(dev["x"], dev["w_router"], torch.from_numpy(dl).cuda())
+    idx, _ = _lib.moe_route(logits, shape.K)
+    torch.cuda.synchronize()
+    ref = oracle.router_logits(inp["x"], inp["w_router"], inp["router_bias"])
+    got = bits(logits)
+    assert_close("logits", got, ref)
+    # the fp32 sums in chunk order against the fp64 sum: far inside the layer tolerance
+    assert np.max(np.abs(got.astype(np.float64) - ref) / (1e-3 + np.abs(ref))) < 1e-3
+    assert_equal("logits rerun", got, bits(logits2))
+    topk_property(got, bits(idx))
+    rdx, rdw = oracle.router_backward(inp["x"], inp["w_router"], dl)
+    assert_close("dx", bits(dx), rdx)
+    assert_close("dw_r", bits(dw), rdw)
+    assert_equal("dx rerun", bits(dx), bits(dx2))
+    assert_equal("dw_r rerun", bits(dw), bits(dw2))
+
+
+def test_router_without_bias_and_zero_tokens():
+    shape = SMALL[0][0]
+    inp = synth.make_inputs(shape, seed=3, weights=False, router=True)
+    dev = pipeline.to_device(inp)
+    logits = _lib.moe_router_logits(dev["x"], dev["w_router"])
+    torch.cuda.synchronize()
+    assert_close("logits", bits(logits), oracle.router_logits(inp["x"], inp["w_router"]))
+    # T = 0: no logits; the weight gradient of no tokens is exactly 0
+    x0 = dev["x"][:0]
+    l0 = _lib.moe_router_logits(x0, dev["w_router"])
+    dw = torch.full((shape.H, shape.E), 7.0, device="cuda")
+    _, dw = _lib.moe_router_backward(x0, dev["w_router"], torch.empty((0, shape.E), device="cuda"), dw_r=dw)
+    torch.cuda.synchronize()
+    assert l0.shape == (0, shape.E)
+    assert torch.count_nonzero(dw).item() == 0
+
+
+@pytest.mark.parametrize("name", ["ep_share_4k", "skew_8k", "fwdbwd_16k", "ep_share_128k"])
+def test_router_full_size_sampled(name):
+    """Full workload sizes: logits and dx on sampled tokens, dW_r on sampled experts, reruns bitwise."""
+    shape = W[name]
+    T, H, E = shape.T, shape.H, shape.E
+    print(f"[router] {name}: T={T} H={H} E={E}", flush=True)
+    inp = synth.make_inputs(shape, seed=0, weights=False, router=True)
+    dev = pipeline.to_device(inp)
+    dl = dlogits_for(T, E, 6)
+    ws = torch.empty(_lib.moe_router_workspace_size(T, H, E), dtype=torch.uint8, device="cuda")
+    logits = _lib.moe_router_logits(dev["x"], dev["w_router"], dev["router_bias"], ws=ws)
+    dx, dw = _lib.moe_router_backward(dev["x"], dev["w_router"], torch.from_numpy(dl).cuda(), ws=ws)
+    logits2 = _lib.moe_router_logits(dev["x"], dev["w_router"], dev["router_bias"], ws=ws)
+    idx, _ = _lib.moe_route(logits, shape.K)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(11)
+    rows = np.unique(np.concatenate([[0, T - 1], rng.integers(0, T, 40)]))
+    cols = np.unique(np.concatenate([[0, E - 1], rng.integers(0, E, 4)]))
+    ref = oracle.router_logits(inp["x"], inp["w_router"], inp["router_bias"], rows=rows)
+    got = bits(logits)
+    assert_close("logits", got[rows], ref[rows])
+    assert_equal("logits rerun", got, bits(logits2))
+    topk_property(got[rows], bits(idx)[rows])
+    rdx, rdw = oracle.router_backward(inp["x"], inp["w_router"], dl, rows=rows, cols=cols)
+    assert_close("dx", bits(dx)[rows], rdx[rows])
+    assert_close("dw_r", bits(dw)[:, cols], rdw[:, cols])

@@ -514,3 +514,70 @@ def test_route_backward_invariants():
     assert np.allclose(dl2, 2 * dl, rtol=1e-6, atol=1e-7)
     i1, g1 = oracle.route(s, 1)
     assert np.all(oracle.route_backward(i1, g1, dg[:, :1], E) == 0.0)
+
+
+# ---------------------------------------------------------------- router projection
+
+def test_router_logits_vs_fp64_matmul():
+    """logits = fp32(x . W_r) + bias: numpy's fp64 matmul rounded to fp32 agrees to within one
+    fp32 rounding (the two fp64 sums differ only in order, ~1e-16 relative)."""
+    rng = np.random.default_rng(90)
+    T, H, E = 37, 192, 64
+    x = rand_bf16(rng, (T, H))
+    w = rand_bf16(rng, (H, E), 0.02)
+    bias = rng.standard_normal(E).astype(np.float32)
+    got = oracle.router_logits(x, w, bias)
+    dot = (f(x) @ f(w)).astype(np.float32)
+    ref = dot + bias[None, :]
+    assert np.all(np.abs(got.astype(np.float64) - ref) <= 2 * U32 * (np.abs(dot) + np.abs(ref)) + 1e-30)
+    # no bias: the dot product alone
+    assert np.array_equal(oracle.router_logits(x, w), oracle.router_logits(x, w, np.zeros(E, np.float32)))
+
+
+def test_router_logits_special_cases():
+    """Identity router weight: logits = x + bias exactly.  A one-hot token picks out a row of W_r
+    (a transposed W_r would give a column).  A row subset equals the same rows of the full result."""
+    rng = np.random.default_rng(91)
+    T, H = 9, 64
+    x = rand_bf16(rng, (T, H))
+    bias = rng.standard_normal(H).astype(np.float32)
+    eye = synth.f32_to_bf16_bits(np.eye(H, dtype=np.float32))
+    assert np.array_equal(oracle.router_logits(x, eye, bias), f(x).astype(np.float32) + bias[None, :])
+    w = rand_bf16(rng, (H, 128), 0.02)
+    onehot = np.zeros((3, H), np.float32)
+    onehot[0, 5] = onehot[1, 0] = onehot[2, H - 1] = 1.0
+    got = oracle.router_logits(synth.f32_to_bf16_bits(onehot), w)
+    assert np.array_equal(got, f(w)[[5, 0, H - 1]].astype(np.float32))
+    rows = np.array([0, 4, 8])
+    full = oracle.router_logits(x, eye, bias)
+    sub = oracle.router_logits(x, eye, bias, rows=rows)
+    assert np.array_equal(sub[rows], full[rows])
+
+
+def test_router_backward_vs_fp64_and_adjoint():
+    """dx against numpy's fp64 matmul of bf16(dlogits) and W_r^T within the fp32-sum bound plus the
+    final bf16 rounding; dW_r against fp64 x^T . bf16(dlogits) within the same kind of bound; and
+    the adjoint identity <dl, v . W_r> = <dx, v> that ties the two directions together."""
+    rng = np.random.default_rng(92)
+    T, H, E = 23, 128, 64
+    x = rand_bf16(rng, (T, H))
+    w = rand_bf16(rng, (H, E), 0.02)
+    dlog = (rng.standard_normal((T, E)) * 0.1).astype(np.float32)
+    dx, dw = oracle.router_backward(x, w, dlog)
+    dl = oracle.round_bf16(dlog)
+    assert np.array_equal(dl, synth.f32_to_bf16_bits(dlog))  # the rounding is RNE
+    exact = f(dl) @ f(w).T
+    bnd = gamma(E) * (np.abs(f(dl)) @ np.abs(f(w)).T)
+    assert np.all(np.abs(f(dx) - exact) <= bnd + U16 * (np.abs(exact) + bnd) + 1e-30)
+    exw = f(x).T @ f(dl)
+    bndw = gamma(T) * (np.abs(f(x)).T @ np.abs(f(dl)))
+    assert np.all(np.abs(dw.astype(np.float64) - exw) <= bndw + 1e-30)
+    v = rng.standard_normal((T, H))
+    lhs = float(np.sum(f(dl) * (v @ f(w))))
+    rhs = float(np.sum(exact * v))
+    assert abs(lhs - rhs) <= 1e-9 * (abs(lhs) + 1)
+    # row and column subsets
+    rows, cols = np.array([1, 22]), np.array([0, 63, 7])
+    dx2, dw2 = oracle.router_backward(x, w, dlog, rows=rows, cols=cols)
+    assert np.array_equal(dx2[rows], dx[rows])
+    assert np.array_equal(dw2[:, cols], dw[:, cols])
