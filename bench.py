@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--router", action="store_true",
+                    help="include the router projection x.W_r (and its backward) in the step; the pages' layer "
+                         "timings exclude gating, so the default leaves it out")
     ap.add_argument("--copy-rows", action="store_true",
                     help="forward-only workloads: permute with the row copy instead of zero-copy dispatch")
     ap.add_argument("--calib-copy", action="store_true",
@@ -48,7 +51,7 @@ def parse():
     return ap.parse_args()
 
 
-def algorithmic_work(shape, R, T_act, n_active, zero_copy=False):
+def algorithmic_work(shape, R, T_act, n_active, zero_copy=False, router=False):
     """Per-launch algorithmic bytes and flops of every step (real rows only, no padding).
     With zero-copy dispatch the permutation moves indices only and the gate/up
     GroupGEMM reads the routed rows from x (the same 2*R*H bytes as from x_perm)."""
@@ -61,6 +64,11 @@ def algorithmic_work(shape, R, T_act, n_active, zero_copy=False):
     w["expert_up"] = dict(bytes=2 * n_active * H * 2 * F + 2 * R * H + 2 * R * F + ab, flops=4 * R * H * F)
     w["expert_down"] = dict(bytes=2 * n_active * F * H + 2 * R * F + 2 * R * H, flops=2 * R * F * H)
     w["combine"] = dict(bytes=2 * H * R + 8 * T * K + 2 * H * T, flops=0)
+    if router:
+        w["router_fwd"] = dict(bytes=2 * T * H + 2 * H * E + 4 * T * E, flops=2 * T * H * E)
+        if shape.backward:
+            w["router_bwd"] = dict(bytes=4 * T * E + 2 * H * E + 2 * T * H + 2 * T * H + 4 * H * E,
+                                   flops=4 * T * H * E)
     if shape.backward:
         # gather + gate gradient: d_out rows read once, dy_perm written, y rows read, pos/gates in, dgates out
         w["bwd_gather"] = dict(bytes=2 * H * T_act + 2 * H * R + 2 * H * R + 12 * T * K, flops=2 * R * H)
@@ -160,13 +168,21 @@ def main():
     _lib.load()
     shape = synth.WORKLOADS[args.workload]
     print(f"[bench] {shape.name}: generating inputs", file=sys.stderr, flush=True)
-    inp = synth.make_inputs(shape, seed=args.seed)
+    inp = synth.make_inputs(shape, seed=args.seed, router=args.router)
     dev = pipeline.to_device(inp)
     zero_copy = not shape.backward and not args.copy_rows
     buf = pipeline.MoeBuffers.allocate(shape, zero_copy=zero_copy)
     stream = torch.cuda.current_stream()
 
-    steps = [("route", lambda: pipeline.route(buf, dev["logits"])),
+    steps = []
+    if args.router:
+        T, H, E = shape.T, shape.H, shape.E
+        r_ws = torch.empty(max(_lib.moe_router_workspace_size(T, H, E), 256), dtype=torch.uint8, device="cuda")
+        r_logits = torch.empty((T, E), dtype=torch.float32, device="cuda")
+        steps.append(("router_fwd", lambda: _lib.moe_router_logits(dev["x"], dev["w_router"], dev["router_bias"],
+                                                                   logits=r_logits, ws=r_ws)))
+        dev["logits"] = r_logits  # the route step consumes the projected scores
+    steps += [("route", lambda: pipeline.route(buf, dev["logits"])),
              ("permute", lambda: pipeline.permute(buf, dev["x"])),
              ("expert_up", lambda: pipeline.expert_up(buf, dev["w_gate"], dev["w_up"], dev["x"])),
              ("expert_down", lambda: pipeline.expert_down(buf, dev["w_down"])),
@@ -191,6 +207,11 @@ def main():
             ("wgrad_down", lambda: _lib.moe_wgrad(buf.h, F, buf.dy_perm, H, buf.offsets, EL, F, H, cap,
                                                   dw=buf.dw_down)),
         ]
+        if args.router:
+            r_dx = torch.empty((shape.T, H), dtype=torch.bfloat16, device="cuda")
+            r_dw = torch.empty((H, shape.E), dtype=torch.float32, device="cuda")
+            steps.append(("router_bwd", lambda: _lib.moe_router_backward(dev["x"], dev["w_router"], buf.dlogits,
+                                                                         dx=r_dx, dw_r=r_dw, ws=r_ws)))
 
     def one_step(evs=None):
         for i, (_, fn) in enumerate(steps):
@@ -225,12 +246,12 @@ def main():
     pos = buf.pos.cpu().numpy()
     T_act = int(np.sum(np.any(pos >= 0, axis=1)))
     n_active = int(np.sum(counts > 0))
-    work = algorithmic_work(shape, R, T_act, n_active, zero_copy)
+    work = algorithmic_work(shape, R, T_act, n_active, zero_copy, args.router)
     dom = max(per, key=per.get)
     rl = roofline(work[dom], per[dom])
     rl["kernel"] = dom
     rl["traffic"] = measured_traffic(dom, shape.name)
-    gemm_names = [n for n in per if work[n]["flops"]]
+    gemm_names = [n for n in per if n.startswith(("expert_", "bwd_down_dgrad", "bwd_up_dgrad", "wgrad_"))]
     gemm_flops = sum(work[n]["flops"] for n in gemm_names)
     gemm_ms = sum(per[n] for n in gemm_names)
     result = {
@@ -248,7 +269,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": shape.name, "T": shape.T, "H": shape.H, "F": shape.F, "E": shape.E, "K": shape.K,
                    "e_local": shape.EL, "cap_rows": buf.cap, "pass": "fwd+bwd" if shape.backward else "fwd",
-                   "dispatch": "zero-copy" if zero_copy else "row copy",
+                   "dispatch": "zero-copy" if zero_copy else "row copy", "router_projection": args.router,
                    "routed_rows": R, "maxvio": round(synth.maxvio(counts, shape.T, shape.K, shape.E), 3),
                    "seed": args.seed, "parallelism": "single GPU"},
         "roofline": rl,

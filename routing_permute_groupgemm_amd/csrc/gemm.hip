@@ -1108,11 +1108,12 @@ extern "C" int moe_wgrad(const moe_bf16* a, int lda, const moe_bf16* b, int ldb,
 namespace moe {
 
 // Chunks of a contraction of kt_total steps so that `tiles` output tiles
-// become about one workgroup per compute unit, each chunk at least 8 steps.
+// become at most one workgroup per compute unit (a second, partial round of
+// workgroups would double the time), each chunk at least 8 steps.
 static void split_steps(int64_t tiles, int64_t kt_total, int* n_chunks, int* steps) {
     kt_total = std::max<int64_t>(kt_total, 1);  // no tokens: one (empty) chunk
     const int64_t cus = moe_host::num_cus();
-    int64_t s = std::min<int64_t>((cus + tiles - 1) / std::max<int64_t>(tiles, 1), std::max<int64_t>(kt_total / 8, 1));
+    int64_t s = std::min<int64_t>(cus / std::max<int64_t>(tiles, 1), std::max<int64_t>(kt_total / 8, 1));
     s = std::max<int64_t>(s, 1);
     const int64_t st = (kt_total + s - 1) / s;
     *steps = (int)st;
@@ -1120,6 +1121,7 @@ static void split_steps(int64_t tiles, int64_t kt_total, int* n_chunks, int* ste
 }
 
 struct RouterPlan {
+    bool fwd_small;               // forward on 128x128 tiles (too few 256x256 tiles to fill the GPU)
     int fwd_chunks, fwd_steps;    // forward: contraction over H in chunks of fwd_steps * 32
     int bwd_chunks, bwd_rows;     // weight gradient: token rows in chunks of bwd_rows
     size_t fwd_bytes, bwd_bytes;  // workspace
@@ -1129,7 +1131,13 @@ static size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 
 static RouterPlan router_plan(int T, int H, int E) {
     RouterPlan r{};
-    split_steps((int64_t)((T + 255) / 256) * ((E + 255) / 256), H / 32, &r.fwd_chunks, &r.fwd_steps);
+    // Few rows: 128x128 tiles, whose smaller fp32 partials cost less to write
+    // and add than the 256x256 tiles' (the partials, not the MFMAs, bound a
+    // forward cut into many chunks).
+    const int64_t big_tiles = (int64_t)((T + 255) / 256) * ((E + 255) / 256);
+    r.fwd_small = big_tiles < moe_host::num_cus();
+    const int tm = r.fwd_small ? 128 : 256;
+    split_steps((int64_t)((T + tm - 1) / tm) * ((E + tm - 1) / tm), H / 32, &r.fwd_chunks, &r.fwd_steps);
     int steps;
     split_steps((int64_t)((H + 255) / 256) * ((E + 255) / 256), (T + 31) / 32, &r.bwd_chunks, &steps);
     r.bwd_rows = steps * 32;
@@ -1188,7 +1196,8 @@ extern "C" int moe_router_logits(const moe_bf16* x, int T, int H, const moe_bf16
     p.part_stride = (int64_t)T * E;
     p.bias = split ? nullptr : bias;
     hipStream_t s = (hipStream_t)stream;
-    int rc = launch<LAY_MN, EPI_F32, SCHED_ROWS>(p, s);
+    int rc = r.fwd_small ? launch_cfg<128, 128, 32, 2, 2, LAY_MN, EPI_F32, SCHED_ROWS, kLdsBudget>(p, s)
+                         : launch<LAY_MN, EPI_F32, SCHED_ROWS>(p, s);
     if (rc != MOE_OK || !split) return rc;
     return moe_host::sum_partials((const float*)ws, r.fwd_chunks, (int64_t)T * E, (int64_t)T * E, bias, E, logits, s);
 }
