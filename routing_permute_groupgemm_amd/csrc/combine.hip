@@ -13,12 +13,15 @@
 // valid rows (pos >= 0) are compacted in k order; a body sized for that count
 // then keeps NV x U independent 16-byte loads in flight per lane (NV rows x U
 // column vectors, 8 to 16 in all) before accumulating each column vector over
-// the rows in k order.  A token with no local row gets zeros.
+// the rows in k order.  A token with no local row gets zeros.  When the
+// output alone is a large share of the 256 MB last-level cache, the rows
+// cannot still be cached from the GEMM that wrote them, and they are read
+// with non-temporal loads (which cost time when the rows are still cached).
 #include "moe_common.hpp"
 
 namespace moe {
 
-template <bool GATED, int NV, int U>
+template <bool GATED, bool NT, int NV, int U>
 __device__ __forceinline__ void combine_rows(const u32x4* __restrict__ y, const int (&rows)[16], const float (&g)[16],
                                              int nv_rows, int nv, int lane, u32x4* __restrict__ orow) {
     for (int v0 = 0; v0 < nv; v0 += 64 * U) {
@@ -29,7 +32,7 @@ __device__ __forceinline__ void combine_rows(const u32x4* __restrict__ y, const 
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int v = v0 + u * 64 + lane;
-                if (r < nv_rows && v < nv) buf[r][u] = src[v];
+                if (r < nv_rows && v < nv) buf[r][u] = NT ? __builtin_nontemporal_load(src + v) : src[v];
             }
         }
 #pragma unroll
@@ -62,7 +65,7 @@ __device__ __forceinline__ void combine_rows(const u32x4* __restrict__ y, const 
     }
 }
 
-template <bool GATED>
+template <bool GATED, bool NT>
 __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ y, const int32_t* __restrict__ pos,
                                                       const float* __restrict__ gates, int T, int K, int H,
                                                       u32x4* __restrict__ out) {
@@ -92,14 +95,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ 
     if (nv_rows == 0) {
         const u32x4 z = {0u, 0u, 0u, 0u};
         for (int v = lane; v < nv; v += 64) __builtin_nontemporal_store(z, orow + v);
+    } else if (nv_rows == 1) {
+        combine_rows<GATED, NT, 1, 8>(y, rows, g, nv_rows, nv, lane, orow);
     } else if (nv_rows <= 2) {
-        combine_rows<GATED, 2, 4>(y, rows, g, nv_rows, nv, lane, orow);
+        combine_rows<GATED, NT, 2, 4>(y, rows, g, nv_rows, nv, lane, orow);
     } else if (nv_rows <= 4) {
-        combine_rows<GATED, 4, 2>(y, rows, g, nv_rows, nv, lane, orow);
+        combine_rows<GATED, NT, 4, 2>(y, rows, g, nv_rows, nv, lane, orow);
     } else if (nv_rows <= 8) {
-        combine_rows<GATED, 8, 2>(y, rows, g, nv_rows, nv, lane, orow);
+        combine_rows<GATED, NT, 8, 2>(y, rows, g, nv_rows, nv, lane, orow);
     } else {
-        combine_rows<GATED, 16, 1>(y, rows, g, nv_rows, nv, lane, orow);
+        combine_rows<GATED, NT, 16, 1>(y, rows, g, nv_rows, nv, lane, orow);
     }
 }
 
@@ -231,10 +236,14 @@ extern "C" int moe_combine(const moe_bf16* y, const int32_t* pos, const float* g
     dim3 grid((T + 3) / 4), block(256);
     const u32x4* yy = (const u32x4*)y;
     u32x4* oo = (u32x4*)out;
+    // an output of 64 MiB or more: a quarter of the last-level cache
+    const bool nt = (int64_t)T * H * 2 >= (64ll << 20);
     if (gates) {
-        combine_kernel<true><<<grid, block, 0, s>>>(yy, pos, gates, T, K, H, oo);
+        if (nt) combine_kernel<true, true><<<grid, block, 0, s>>>(yy, pos, gates, T, K, H, oo);
+        else combine_kernel<true, false><<<grid, block, 0, s>>>(yy, pos, gates, T, K, H, oo);
     } else {
-        combine_kernel<false><<<grid, block, 0, s>>>(yy, pos, gates, T, K, H, oo);
+        if (nt) combine_kernel<false, true><<<grid, block, 0, s>>>(yy, pos, gates, T, K, H, oo);
+        else combine_kernel<false, false><<<grid, block, 0, s>>>(yy, pos, gates, T, K, H, oo);
     }
     return moe_host::launch_status();
 }

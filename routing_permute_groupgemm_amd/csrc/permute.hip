@@ -226,6 +226,8 @@ __global__ __launch_bounds__(256) void perm_copy_kernel(const u32x4* __restrict_
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u) {
                 int v = v0 + u * 64 + lane;
+                // plain stores: non-temporal ones measured slower here once
+                // the GEMM that reads x_perm runs after the copy
                 if (v < nv) dst[v] = buf[u];
             }
         }
