@@ -9,8 +9,11 @@ weight-gradient GroupGEMMs.  Every step is a libmoe C-ABI call on one stream.
 
 Prints one JSON line: tokens/s, plus the roofline of the dominant kernel
 (achieved algorithmic bytes or flops per launch / its mean launch time, from
-HIP events recorded on the launch stream over the timed steps) and the CPU
-oracle's throughput on a bounded sample of the same workload.
+HIP events recorded on the launch stream around that kernel in the timed
+steps) and the CPU oracle's throughput on a bounded sample of the same
+workload.  `step_ms` comes from an untimed pass with events around every
+step: each recorded event costs the stream a short bubble, so the timed pass
+records them around the dominant step only.
 """
 from __future__ import annotations
 
@@ -213,30 +216,44 @@ def main():
             steps.append(("router_bwd", lambda: _lib.moe_router_backward(dev["x"], dev["w_router"], buf.dlogits,
                                                                          dx=r_dx, dw_r=r_dw, ws=r_ws)))
 
-    def one_step(evs=None):
+    def one_step(evs=None, only=None):
+        # evs: events around every step (breakdown pass), or around step `only`
         for i, (_, fn) in enumerate(steps):
-            if evs is not None:
-                evs[i].record(stream)
+            if evs is not None and (only is None or i == only):
+                evs[0 if only is not None else i].record(stream)
             fn()
-        if evs is not None:
+            if evs is not None and only is not None and i == only:
+                evs[1].record(stream)
+        if evs is not None and only is None:
             evs[len(steps)].record(stream)
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         one_step()
     torch.cuda.synchronize()
+    # Breakdown pass (untimed): events around every step give each step's mean
+    # time and the dominant step.  Every recorded event costs the stream a
+    # bubble of a few microseconds, so the timed pass below records events only
+    # around the dominant step, which its roofline needs.
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(steps) + 1)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        one_step(evs[k])
+    torch.cuda.synchronize()
+    per = {name: float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)]))
+           for i, (name, _) in enumerate(steps)}
+    dom_i = max(range(len(steps)), key=lambda i: per[steps[i][0]])
+    dom = steps[dom_i][0]
+    dev_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
     for k in range(args.steps):
-        one_step(evs[k])
+        one_step(dev_evs[k], only=dom_i)
     end.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / args.steps
-    per = {name: float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)]))
-           for i, (name, _) in enumerate(steps)}
+    dom_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in dev_evs]))
     print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
 
     status = int(buf.status[0].item())
@@ -247,8 +264,7 @@ def main():
     T_act = int(np.sum(np.any(pos >= 0, axis=1)))
     n_active = int(np.sum(counts > 0))
     work = algorithmic_work(shape, R, T_act, n_active, zero_copy, args.router)
-    dom = max(per, key=per.get)
-    rl = roofline(work[dom], per[dom])
+    rl = roofline(work[dom], dom_ms)
     rl["kernel"] = dom
     rl["traffic"] = measured_traffic(dom, shape.name)
     gemm_names = [n for n in per if n.startswith(("expert_", "bwd_down_dgrad", "bwd_up_dgrad", "wgrad_"))]
