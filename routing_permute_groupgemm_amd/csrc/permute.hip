@@ -9,6 +9,11 @@
 // most once, ordering by p inside an expert is ordering by token.
 //
 // Four launches, none of which reads device data back to the host:
+// TB (tokens per block of count and rank) is 64 while blocks x local experts
+// fits one 8192-entry pass of the one-block scan: there few blocks would
+// leave the GPU idle and each wave's ranking rounds are a latency chain.
+// Otherwise it is 256, which keeps the scan short.
+//
 //  1. count:   per block of TB tokens, an LDS histogram of local experts
 //              (integer adds commute, so the result has no order dependence);
 //              written expert-major to the workspace: ws[j*nblk + b].
@@ -25,17 +30,19 @@
 
 namespace moe {
 
-constexpr int kPermTB = 256;  // tokens per block for count / rank
 constexpr int kMaxLocal = 512;
 
+// tokens per block of the count and rank kernels
+inline int perm_tb(int64_t T, int e_local) { return (T + 63) / 64 * e_local <= 8192 ? 64 : 256; }
+
 __global__ __launch_bounds__(256) void perm_count_kernel(const int32_t* __restrict__ idx, int T, int K,
-                                                         int e_begin, int e_local, int nblk,
+                                                         int e_begin, int e_local, int nblk, int tb,
                                                          int32_t* __restrict__ ws) {
     __shared__ int hist[kMaxLocal];
     for (int j = threadIdx.x; j < e_local; j += 256) hist[j] = 0;
     __syncthreads();
-    const int64_t p0 = (int64_t)blockIdx.x * kPermTB * K;
-    const int64_t p1 = min(p0 + (int64_t)kPermTB * K, (int64_t)T * K);
+    const int64_t p0 = (int64_t)blockIdx.x * tb * K;
+    const int64_t p1 = min(p0 + (int64_t)tb * K, (int64_t)T * K);
     for (int64_t p = p0 + threadIdx.x; p < p1; p += 256) {
         int j = idx[p] - e_begin;
         if ((unsigned)j < (unsigned)e_local) atomicAdd(&hist[j], 1);
@@ -136,9 +143,10 @@ __device__ __forceinline__ uint64_t match_key(int key, bool active, int nbits) {
     return m;
 }
 
+// KMAX: an upper bound of the rounds of 64 pairs per wave (tb/4 tokens * K pairs)
 template <int KMAX>
 __global__ __launch_bounds__(256) void perm_rank_kernel(const int32_t* __restrict__ idx, int T, int K,
-                                                        int e_begin, int e_local, int nbits, int nblk,
+                                                        int e_begin, int e_local, int nbits, int nblk, int tb,
                                                         const int32_t* __restrict__ ws, int64_t cap_rows,
                                                         int32_t* __restrict__ pos, int32_t* __restrict__ src) {
     __shared__ int cnt[4][kMaxLocal];
@@ -146,17 +154,21 @@ __global__ __launch_bounds__(256) void perm_rank_kernel(const int32_t* __restric
     for (int j = lane; j < e_local; j += 64) cnt[wave][j] = 0;
     __syncthreads();
     const int64_t npairs = (int64_t)T * K;
-    const int64_t p0 = (int64_t)blockIdx.x * kPermTB * K + (int64_t)wave * (kPermTB / 4) * K;
+    // wave `wave` owns the pairs of tb/4 consecutive tokens, [p0, pend), in
+    // rounds of 64 consecutive pairs
+    const int64_t per_wave = (int64_t)(tb / 4) * K;
+    const int64_t p0 = (int64_t)blockIdx.x * tb * K + wave * per_wave;
+    const int64_t pend = min(p0 + per_wave, npairs);
+    const int rounds = (int)((per_wave + 63) / 64);
     const uint64_t lower = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     int rk[KMAX], jj[KMAX];
-    // wave `wave` owns pairs [p0, p0 + 64*K): K iterations of 64 consecutive pairs
 #pragma unroll
     for (int it = 0; it < KMAX; ++it) {
         rk[it] = 0;
         jj[it] = -1;
-        if (it < K) {
+        if (it < rounds) {
             const int64_t p = p0 + (int64_t)it * 64 + lane;
-            int j = p < npairs ? idx[p] - e_begin : -1;
+            int j = p < pend ? idx[p] - e_begin : -1;
             bool local = (unsigned)j < (unsigned)e_local;
             uint64_t m = match_key(local ? j : 0, local, nbits);
             if (local) {
@@ -182,9 +194,9 @@ __global__ __launch_bounds__(256) void perm_rank_kernel(const int32_t* __restric
     __syncthreads();
 #pragma unroll
     for (int it = 0; it < KMAX; ++it) {
-        if (it < K) {
+        if (it < rounds) {
             const int64_t p = p0 + (int64_t)it * 64 + lane;
-            if (p < npairs) {
+            if (p < pend) {
                 int j = jj[it];
                 int row = -1;
                 if (j >= 0) {
@@ -239,7 +251,8 @@ __global__ __launch_bounds__(256) void perm_copy_kernel(const u32x4* __restrict_
 extern "C" size_t moe_permute_workspace_size(int T, int K, int e_local) {
     (void)K;
     if (T < 0 || e_local < 0) return 0;
-    int64_t nblk = (T + moe::kPermTB - 1) / moe::kPermTB;
+    const int tb = moe::perm_tb(T, e_local);
+    int64_t nblk = (T + tb - 1) / tb;
     int64_t n = nblk * (int64_t)e_local;
     return (size_t)((n * 4 + 255) / 256 * 256 + 256);
 }
@@ -267,19 +280,24 @@ extern "C" int moe_permute(const int32_t* topk_idx, int T, int K, int e_begin, i
     const size_t need = moe_permute_workspace_size(T, K, e_local);
     if (!ws || ws_bytes < need) return MOE_EWORKSPACE;
     hipStream_t s = (hipStream_t)stream;
-    const int nblk = (T + kPermTB - 1) / kPermTB;
+    const int tb = perm_tb(T, e_local);
+    const int nblk = (T + tb - 1) / tb;
+    const int rounds = (tb / 4 * K + 63) / 64;
     int nbits = 0;
     while ((1 << nbits) < e_local) ++nbits;
     int32_t* w = (int32_t*)ws;
     if (nblk > 0 && e_local > 0)
-        perm_count_kernel<<<nblk, 256, 0, s>>>(topk_idx, T, K, e_begin, e_local, nblk, w);
+        perm_count_kernel<<<nblk, 256, 0, s>>>(topk_idx, T, K, e_begin, e_local, nblk, tb, w);
     perm_scan_kernel<<<1, 1024, 0, s>>>(w, e_local, nblk, cap_rows, counts, offsets, status);
     if (nblk > 0) {
-        if (K <= 8)
-            perm_rank_kernel<8><<<nblk, 256, 0, s>>>(topk_idx, T, K, e_begin, e_local, nbits, nblk, w,
+        if (rounds <= 4)
+            perm_rank_kernel<4><<<nblk, 256, 0, s>>>(topk_idx, T, K, e_begin, e_local, nbits, nblk, tb, w,
+                                                    cap_rows, pos, src);
+        else if (rounds <= 8)
+            perm_rank_kernel<8><<<nblk, 256, 0, s>>>(topk_idx, T, K, e_begin, e_local, nbits, nblk, tb, w,
                                                     cap_rows, pos, src);
         else
-            perm_rank_kernel<16><<<nblk, 256, 0, s>>>(topk_idx, T, K, e_begin, e_local, nbits, nblk, w,
+            perm_rank_kernel<16><<<nblk, 256, 0, s>>>(topk_idx, T, K, e_begin, e_local, nbits, nblk, tb, w,
                                                      cap_rows, pos, src);
         if (H > 0 && x_perm)
             perm_copy_kernel<4><<<(T + 3) / 4, 256, 0, s>>>((const u32x4*)x, T, K, H, pos, (u32x4*)x_perm);
