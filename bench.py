@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--router", action="store_true",
                     help="include the router projection x.W_r (and its backward) in the step; the pages' layer "
                          "timings exclude gating, so the default leaves it out")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time K replays of the whole step captured in a HIP graph (reported as "
+                         "graph_ms_per_step; value stays the eager timed pass)")
     ap.add_argument("--copy-rows", action="store_true",
                     help="forward-only workloads: permute with the row copy instead of zero-copy dispatch")
     ap.add_argument("--calib-copy", action="store_true",
@@ -255,6 +258,28 @@ def main():
     ms_per_step = total_ms / args.steps
     dom_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in dev_evs]))
     print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
+    graph_ms = None
+    if args.graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            one_step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            one_step()
+        for _ in range(2):
+            graph.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for _ in range(args.steps):
+            graph.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = g0.elapsed_time(g1) / args.steps
+        print(f"[bench] graph replays: {graph_ms:.3f} ms/step", file=sys.stderr, flush=True)
 
     status = int(buf.status[0].item())
     offsets = buf.offsets.cpu().numpy()
@@ -293,6 +318,8 @@ def main():
         "permute_gbps": round(work["permute"]["bytes"] / (per["permute"] * 1e-3) / 1e9, 1),
         "step_ms": {k: round(v, 4) for k, v in per.items()},
     }
+    if graph_ms is not None:
+        result["graph_ms_per_step"] = round(graph_ms, 4)
     if status != 0:
         result["warning"] = "row capacity overflow: rows were dropped"
     if not args.no_cpu_baseline:
