@@ -252,3 +252,30 @@ def test_full_layer_rerun_bitwise(case):
     for f in ["src", "x_perm", "h", "y"] + (["ab", "dy_perm", "dab", "dx_perm"] if s.backward else []):
         assert torch.equal(getattr(c.buf, f)[:R].view(torch.uint8), getattr(b2, f)[:R].view(torch.uint8)), f
     del b2
+
+
+def test_literal_zipf_bias_full_size_forward():
+    """skew_8k's shape with the recipe read literally (alpha = 1, one expert gets most of the 65536 rows):
+    indices and permutation in full, gate/up and the combine on sampled rows and tokens."""
+    shape = synth.WORKLOADS["skew_8k"]
+    inp = synth.make_inputs(shape, seed=0, alpha=1.0)
+    dev = pipeline.to_device(inp)
+    buf = pipeline.MoeBuffers.allocate(shape, backward=False)
+    pipeline.forward(buf, dev)
+    torch.cuda.synchronize()
+    idx, g = oracle.route(inp["logits"], shape.K)
+    pm = oracle.permute(idx, shape.e_begin, shape.EL, inp["x"], shape.cap)
+    counts = pm["counts"]
+    print(f"[fullsize] literal skew: rows per expert {counts.min()}..{counts.max()}", flush=True)
+    assert counts.max() > 4000
+    assert_equal("topk_idx", bits(buf.topk_idx), idx)
+    assert_equal("offsets", bits(buf.offsets), pm["offsets"])
+    assert_equal("pos", bits(buf.pos), pm["pos"])
+    R = min(int(pm["offsets"][-1]), shape.cap)
+    hot = int(np.argmax(counts))
+    lo, hi = int(pm["offsets"][hot]), int(pm["offsets"][hot + 1])
+    rng = np.random.default_rng(3)
+    rows = np.unique(np.concatenate([[lo, hi - 1, (lo + hi) // 2, 0, R - 1], rng.integers(0, R, 16)]))
+    h, _ = oracle.expert_up(pm["x_perm"], inp["w_gate"], inp["w_up"], pm["offsets"], shape.cap, rows=rows,
+                            want_ab=False)
+    assert_close("h", bits(buf.h)[rows], h[rows])

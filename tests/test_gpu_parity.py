@@ -114,6 +114,18 @@ def test_all_tokens_to_one_expert_and_empty_experts():
     assert sorted(ref["counts"].tolist()) == [0] * 6 + [300, 300]
 
 
+def test_literal_zipf_bias_stress():
+    """The skew recipe read literally (bias = ln Zipf(1.2), alpha = 1): one expert takes most of the rows
+    and many get few or none; the whole layer still matches the oracle."""
+    shape = SMALL["skew_small"]
+    inp = synth.make_inputs(shape, seed=7, d_out=True, alpha=1.0)
+    buf, _ = run_gpu(shape, inp)
+    ref = check_layer(shape, inp, buf, shape.cap)
+    counts = ref["counts"]
+    print(f"[parity] literal skew: rows per expert {counts.min()}..{counts.max()} of {counts.sum()}", flush=True)
+    assert counts.max() > 0.9 * shape.T  # a token picks an expert at most once: T rows is the most
+
+
 def test_local_share_single_expert_and_nonlocal_tokens():
     shape = synth.MoeShape("single_local", 91, T=200, H=64, F=64, E=8, K=2, e_begin=3, e_local=1,
                            backward=True)
