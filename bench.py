@@ -158,6 +158,28 @@ def calib_copy():
     print(json.dumps({"calib_copy_bytes_read": n, "calib_copy_bytes_written": n, "launches": 5}))
 
 
+def measured_copy_gbps(stream):
+    """Read+write GB/s of a plain 1 GiB device-to-device copy on this GPU: the practical HBM ceiling
+    that a kernel moving as many bytes in as out can approach."""
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    for _ in range(2):
+        b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(5):
+        b.copy_(a)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 5
+    del a, b
+    return round(2 * n / (ms * 1e-3) / 1e9, 1)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -292,6 +314,9 @@ def main():
     rl = roofline(work[dom], dom_ms)
     rl["kernel"] = dom
     rl["traffic"] = measured_traffic(dom, shape.name)
+    if rl["bound"] == "hbm":
+        # the spec peak above; beside it the rate a plain copy reaches on this GPU
+        rl["measured_copy_gbps"] = measured_copy_gbps(stream)
     gemm_names = [n for n in per if n.startswith(("expert_", "bwd_down_dgrad", "bwd_up_dgrad", "wgrad_"))]
     gemm_flops = sum(work[n]["flops"] for n in gemm_names)
     gemm_ms = sum(per[n] for n in gemm_names)
