@@ -141,7 +141,14 @@ def cpu_baseline(shape, inp, budget_s):
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu = next(line.split(":", 1)[1].strip() for line in fh if line.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
     return dict(value=round(done / dt, 2), unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
+                cpu=cpu, host_cpus=os.cpu_count(),
                 sample=f"first {done} of {T} tokens in chunks of {chunk} "
                        f"({'forward+backward' if shape.backward else 'forward'}), {dt:.1f} s")
 
