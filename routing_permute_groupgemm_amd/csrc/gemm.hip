@@ -123,6 +123,15 @@ __device__ __forceinline__ void lds_load16(i32x4 srd, uint32_t lds, uint32_t vof
                  : "memory");
 }
 
+// The same with the non-temporal hint: for data read exactly once (weights of
+// experts that fit one row tile), so that it does not displace reused lines.
+__device__ __forceinline__ void lds_load16_nt(i32x4 srd, uint32_t lds, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+                 :
+                 : "s"(lds), "v"(voff), "s"(srd)
+                 : "memory");
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const MOE_LDS void*)p;
 }
@@ -230,8 +239,9 @@ struct Tile {
 // The GEMM of one workgroup for one tile shape.  smem is the stage ring;
 // s_off holds the clamped row offsets (already loaded); s_start and s_wave are
 // scratch for the schedule; s_idx (GATHER only) holds the prefetched source
-// indices of the A rows.
-template <int BM, int BN, int BK, int WM, int WN, int LB, int EPI, int SCHED, int LDSB, bool GATHER>
+// indices of the A rows.  NTB: every expert fits one row tile, so each weight
+// byte is read once and the weight loads carry the non-temporal hint.
+template <int BM, int BN, int BK, int WM, int WN, int LB, int EPI, int SCHED, int LDSB, bool GATHER, bool NTB>
 __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, const int* s_off, int* s_start,
                                         int* s_wave, int* s_idx) {
     using TL = Tile<BM, BN, BK, WM, WN, LDSB>;
@@ -400,11 +410,12 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
     // Gathered A rows (GATHER): one descriptor over all of a; per lane, the
     // byte offset of the row behind each of its LA loads (kOOB past the
     // expert's rows).  The source indices of a tile's rows are fetched one
-    // tile ahead, by LDS-direct loads into this wave's half of a two-buffer
-    // area, so the switch to the next tile never waits for loads in flight:
-    // when the cursor reaches a tile, the KT >= 2 stages issued since its
-    // prefetch put it behind the (S-2)*LPW newest loads, which a free vmcnt
-    // wait then covers.
+    // tile ahead, by LDS-direct loads into this wave's slice of one of two
+    // buffers (alternating per tile), so the switch to the next tile never
+    // waits for loads in flight: when the cursor reaches a tile, the KT >= 2
+    // stages issued since its prefetch (the contraction is at least 64 long)
+    // put it behind the (S-2)*LPW newest loads, which a free vmcnt wait then
+    // covers.
     uint32_t c_rowoff[LA];
 #pragma unroll
     for (int u = 0; u < LA; ++u) c_rowoff[u] = kOOB;
@@ -561,7 +572,8 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
                     }
                     const uint32_t voff =
                         col < p.N ? lb0 + (uint32_t)(((mn_kr(u - LA) * 8 + k0) * p.ldw + col) * 2) : kOOB;
-                    lds_load16(r, sB + q * 1024, live ? voff : kOOB);
+                    if constexpr (NTB) lds_load16_nt(r, sB + q * 1024, live ? voff : kOOB);
+                    else lds_load16(r, sB + q * 1024, live ? voff : kOOB);
                 } else {
                     // weight [N][Kd], contraction contiguous; second segment from w1
                     const bool seg1 = p.two_seg && k0 >= p.Kd;
@@ -879,18 +891,41 @@ void gg_kernel(GemmParams p) {
     // GATHER: two buffers of 64 source indices per A load of each wave, and
     // 1 KiB of slack behind them
     __shared__ int s_idx[GATHER ? 2 * TL::kALoads * 64 + 256 : 1];
+    __shared__ int s_maxrows;
+    if (threadIdx.x == 0) s_maxrows = 0;
+    __syncthreads();
     for (int j = threadIdx.x; j <= p.e_local; j += TL::kThreads) {
         const int64_t o = p.offsets ? (int64_t)p.offsets[j] : min((int64_t)j * p.row_chunk, (int64_t)p.dense_rows);
         s_off[j] = (int)(o < p.cap ? o : p.cap);
     }
     __syncthreads();
+    // the non-temporal weight path exists for the forward GEMMs (weights N-contiguous)
+    constexpr bool kNtPath = SCHED == SCHED_ROWS && LB == LAY_MN && EPI != EPI_F32;
+    if constexpr (kNtPath) {
+        for (int j = threadIdx.x; j < p.e_local; j += TL::kThreads) atomicMax(&s_maxrows, s_off[j + 1] - s_off[j]);
+        __syncthreads();
+    }
+    const int max_rows = s_maxrows;
     if constexpr (ALT != 0) {
         if (prefer_alt<BM, ALT, BN, EPI, TL::kThreads>(p, s_off, s_wave)) {
-            gg_body<ALT, BN, BK, WM, WN, LB, EPI, SCHED, LDSB, GATHER>(p, smem, s_off, s_start, s_wave, s_idx);
+            if constexpr (kNtPath) {
+                if (max_rows <= ALT) {
+                    gg_body<ALT, BN, BK, WM, WN, LB, EPI, SCHED, LDSB, GATHER, true>(p, smem, s_off, s_start, s_wave,
+                                                                                     s_idx);
+                    return;
+                }
+            }
+            gg_body<ALT, BN, BK, WM, WN, LB, EPI, SCHED, LDSB, GATHER, false>(p, smem, s_off, s_start, s_wave, s_idx);
             return;
         }
     }
-    gg_body<BM, BN, BK, WM, WN, LB, EPI, SCHED, LDSB, GATHER>(p, smem, s_off, s_start, s_wave, s_idx);
+    if constexpr (kNtPath) {
+        if (max_rows <= BM) {
+            gg_body<BM, BN, BK, WM, WN, LB, EPI, SCHED, LDSB, GATHER, true>(p, smem, s_off, s_start, s_wave, s_idx);
+            return;
+        }
+    }
+    gg_body<BM, BN, BK, WM, WN, LB, EPI, SCHED, LDSB, GATHER, false>(p, smem, s_off, s_start, s_wave, s_idx);
 }
 
 // Tile configurations.
