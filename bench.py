@@ -319,6 +319,7 @@ def main():
     n_active = int(np.sum(counts > 0))
     work = algorithmic_work(shape, R, T_act, n_active, zero_copy, args.router)
     rl = roofline(work[dom], dom_ms)
+    rl["launch_ms"] = round(dom_ms, 4)  # the kernel's mean time between the events around it
     rl["kernel"] = dom
     rl["traffic"] = measured_traffic(dom, shape.name)
     if rl["bound"] == "hbm":
