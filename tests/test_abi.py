@@ -169,3 +169,20 @@ def test_router_backward_rejects():
     assert r(FAKE, None, FAKE, 8, 8, 2, FAKE, None) == -1
     assert r(FAKE, FAKE, FAKE, 8, 8, 2, MIS, None) == -3
     assert r(None, None, None, 0, 8, 2, None, None) == 0
+
+
+def test_pair_index_division_by_reciprocal():
+    """The zero-copy GEMM turns a pair index v = t*K + k (v < 2^31) into t with the host's
+    floor((2^32-1)/K), a high multiply and one correction; check that formula on edge values."""
+    import numpy as np
+    rng = np.random.default_rng(0)
+    for K in range(1, 17):
+        rcp = 0xFFFFFFFF // K
+        t = np.concatenate([np.arange(0, 4096), rng.integers(0, (1 << 31) // K, 20000),
+                            [(1 << 31) // K - 1]]).astype(np.uint64)
+        for k in range(K):
+            v = t * K + k
+            v = v[v < (1 << 31)]
+            q = (v * rcp) >> 32
+            q = q + ((v - q * K) >= K)
+            assert np.array_equal(q, v // K), K

@@ -98,6 +98,18 @@ def test_zero_copy_forward_equals_copy_forward(name):
     assert_close("out", bits(b.out), o["out"])
 
 
+@pytest.mark.parametrize("K", [1, 3, 5, 16])
+def test_gather_every_topk(K):
+    """The row of pair index src = t*K + k is t = src / K, computed with a reciprocal and one correction:
+    other K than the workloads' 2 and 8, including K = 1 and the largest K."""
+    shape = synth.MoeShape(f"zc_k{K}", 95, T=333, H=128, F=64, E=max(16, K), K=K)
+    inp = synth.make_inputs(shape, seed=K)
+    ref, pm, h, ab = gate_up_both_ways(shape, inp, shape.cap)
+    R = min(int(bits(ref.offsets)[-1]), shape.cap)
+    assert_equal("h", bits(h)[:R], bits(ref.h)[:R])
+    assert_equal("ab_save", bits(ab)[:R], bits(ref.ab)[:R])
+
+
 def test_zero_copy_is_forward_only():
     with pytest.raises(ValueError):
         pipeline.MoeBuffers.allocate(SHAPES["tiny"], backward=True, zero_copy=True)
