@@ -83,6 +83,18 @@ def _need(t, dtype, name):
                        f"contiguous={t.is_contiguous()} device={t.device}")
 
 
+def _shape(t, shape, name):
+    """A caller-provided buffer must have exactly this shape (the kernels write all of it)."""
+    if tuple(t.shape) != tuple(shape):
+        raise MoeError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _rows(t, rows, cols, name):
+    """A row buffer of the expert-grouped order: at least `rows` rows of exactly `cols` columns."""
+    if t.dim() != 2 or t.shape[0] < rows or t.shape[1] != cols:
+        raise MoeError(f"{name}: expected at least {rows} rows of {cols} columns, got {tuple(t.shape)}")
+
+
 def moe_route(logits, K, topk_idx=None, gates=None, stream=None):
     _need(logits, torch.float32, "logits")
     T, E = logits.shape
@@ -90,6 +102,10 @@ def moe_route(logits, K, topk_idx=None, gates=None, stream=None):
         topk_idx = torch.empty((T, K), dtype=torch.int32, device=logits.device)
     if gates is None:
         gates = torch.empty((T, K), dtype=torch.float32, device=logits.device)
+    _need(topk_idx, torch.int32, "topk_idx")
+    _need(gates, torch.float32, "gates")
+    _shape(topk_idx, (T, K), "topk_idx")
+    _shape(gates, (T, K), "gates")
     _check(load().moe_route(_ptr(logits), T, E, K, _ptr(topk_idx), _ptr(gates), _stream(stream)))
     return topk_idx, gates
 
@@ -102,6 +118,9 @@ def moe_route_backward(topk_idx, gates, dgates, E, dlogits=None, stream=None):
     if dlogits is None:
         dlogits = torch.empty((T, E), dtype=torch.float32, device=gates.device)
     _need(dlogits, torch.float32, "dlogits")
+    _shape(gates, (T, K), "gates")
+    _shape(dgates, (T, K), "dgates")
+    _shape(dlogits, (T, E), "dlogits")
     _check(load().moe_route_backward(_ptr(topk_idx), _ptr(gates), _ptr(dgates), T, E, K, _ptr(dlogits),
                                      _stream(stream)))
     return dlogits
@@ -145,6 +164,15 @@ def moe_permute(topk_idx, e_begin, e_local, x, cap_rows, out=None, ws=None, stre
     need = moe_permute_workspace_size(T, K, e_local)
     if ws is None or ws.numel() < need:
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    for t, name, dt in ((counts, "counts", torch.int32), (offsets, "offsets", torch.int32), (pos, "pos", torch.int32),
+                        (src, "src", torch.int32), (status, "status", torch.int32)):
+        _need(t, dt, name)
+    if counts.numel() < e_local or offsets.numel() < e_local + 1 or src.numel() < cap_rows or status.numel() < 1:
+        raise MoeError("moe_permute: counts, offsets, src or status smaller than e_local, e_local+1, cap_rows, 1")
+    _shape(pos, (T, K), "pos")
+    if x_perm is not None:
+        _need(x_perm, torch.bfloat16, "x_perm")
+        _rows(x_perm, cap_rows, H, "x_perm")
     _check(load().moe_permute(_ptr(topk_idx), T, K, e_begin, e_local, _ptr(x), H, cap_rows,
                               _ptr(counts), _ptr(offsets), _ptr(pos), _ptr(src), _ptr(x_perm),
                               _ptr(status), _ptr(ws), ws.numel(), _stream(stream)))
@@ -159,6 +187,11 @@ def moe_gather(d_out, pos, gates, dy_perm, stream=None):
         _need(gates, torch.float32, "gates")
     _need(dy_perm, torch.bfloat16, "dy_perm")
     T, K = pos.shape
+    _shape(d_out, (T, d_out.shape[1]), "d_out")
+    if dy_perm.dim() != 2 or dy_perm.shape[1] != d_out.shape[1]:
+        raise MoeError(f"dy_perm: expected rows of {d_out.shape[1]} columns, got {tuple(dy_perm.shape)}")
+    if gates is not None:
+        _shape(gates, (T, K), "gates")
     _check(load().moe_gather(_ptr(d_out), _ptr(pos), _ptr(gates), T, K, d_out.shape[1], _ptr(dy_perm),
                              _stream(stream)))
     return dy_perm
@@ -175,9 +208,28 @@ def moe_gather_gate_grad(d_out, pos, gates, y, dy_perm, dgates=None, stream=None
     if dgates is None:
         dgates = torch.empty((T, K), dtype=torch.float32, device=d_out.device)
     _need(dgates, torch.float32, "dgates")
+    H = d_out.shape[1]
+    _shape(d_out, (T, H), "d_out")
+    _shape(gates, (T, K), "gates")
+    _shape(dgates, (T, K), "dgates")
+    for t, name in ((y, "y"), (dy_perm, "dy_perm")):
+        if t.dim() != 2 or t.shape[1] != H:
+            raise MoeError(f"{name}: expected rows of {H} columns, got {tuple(t.shape)}")
     _check(load().moe_gather_gate_grad(_ptr(d_out), _ptr(pos), _ptr(gates), _ptr(y), T, K, d_out.shape[1],
                                        _ptr(dy_perm), _ptr(dgates), _stream(stream)))
     return dy_perm, dgates
+
+
+def _gate_up_checks(w_gate, w_up, offsets, cap_rows, h, ab_save):
+    EL, H, F = w_gate.shape
+    _shape(w_up, (EL, H, F), "w_up")
+    if offsets.numel() < EL + 1:
+        raise MoeError(f"offsets: expected {EL + 1} entries, got {offsets.numel()}")
+    _need(h, torch.bfloat16, "h")
+    _rows(h, cap_rows, F, "h")
+    if ab_save is not None:
+        _need(ab_save, torch.bfloat16, "ab_save")
+        _rows(ab_save, cap_rows, 2 * F, "ab_save")
 
 
 def moe_grouped_gemm_swiglu(x_perm, w_gate, w_up, offsets, cap_rows, h=None, ab_save=None, stream=None):
@@ -188,6 +240,8 @@ def moe_grouped_gemm_swiglu(x_perm, w_gate, w_up, offsets, cap_rows, h=None, ab_
     EL, H, F = w_gate.shape
     if h is None:
         h = torch.empty((x_perm.shape[0], F), dtype=torch.bfloat16, device=x_perm.device)
+    _gate_up_checks(w_gate, w_up, offsets, cap_rows, h, ab_save)
+    _rows(x_perm, cap_rows, H, "x_perm")
     _check(load().moe_grouped_gemm_swiglu(_ptr(x_perm), _ptr(w_gate), _ptr(w_up), _ptr(offsets), EL, H, F,
                                           cap_rows, _ptr(h), _ptr(ab_save), _stream(stream)))
     return h
@@ -206,6 +260,10 @@ def moe_grouped_gemm_swiglu_gather(x, src, K, w_gate, w_up, offsets, cap_rows, h
     T = x.shape[0]
     if h is None:
         h = torch.empty((max(cap_rows, 1), F), dtype=torch.bfloat16, device=x.device)
+    _gate_up_checks(w_gate, w_up, offsets, cap_rows, h, ab_save)
+    _shape(x, (T, H), "x")
+    if src.numel() < cap_rows:
+        raise MoeError(f"src: expected at least {cap_rows} entries, got {src.numel()}")
     _check(load().moe_grouped_gemm_swiglu_gather(_ptr(x), T, _ptr(src), int(K), _ptr(w_gate), _ptr(w_up),
                                                  _ptr(offsets), EL, H, F, cap_rows, _ptr(h), _ptr(ab_save),
                                                  _stream(stream)))
@@ -225,6 +283,17 @@ def moe_grouped_gemm(a, w0, w1, trans_w, offsets, Kd, N, cap_rows, c, epilogue=M
     EL = w0.shape[0]
     lda = a.shape[1] if lda is None else lda
     ldc = c.shape[1] if ldc is None else ldc
+    _shape(w0, (EL, N, Kd) if trans_w else (EL, Kd, N), "w0")
+    if w1 is not None:
+        _shape(w1, tuple(w0.shape), "w1")
+    if offsets.numel() < EL + 1:
+        raise MoeError(f"offsets: expected {EL + 1} entries, got {offsets.numel()}")
+    # every row r < cap_rows of a and c may be touched, at strides lda and ldc
+    for t, ld, name in ((a, lda, "a"), (c, ldc, "c")):
+        if t.dim() != 2 or t.shape[0] < cap_rows or (cap_rows > 0 and t.shape[1] < ld):
+            raise MoeError(f"{name}: expected at least {cap_rows} rows of {ld} columns, got {tuple(t.shape)}")
+    if ab is not None:
+        _rows(ab, cap_rows, 2 * N, "ab")
     _check(load().moe_grouped_gemm(_ptr(a), lda, _ptr(w0), _ptr(w1), int(trans_w), _ptr(offsets), EL, Kd, N,
                                    cap_rows, epilogue, _ptr(ab), _ptr(c), ldc, _stream(stream)))
     return c
@@ -239,6 +308,10 @@ def moe_combine(y, pos, gates, out=None, stream=None):
     H = y.shape[1]
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
+    _need(out, torch.bfloat16, "out")
+    _shape(out, (T, H), "out")
+    if gates is not None:
+        _shape(gates, (T, K), "gates")
     _check(load().moe_combine(_ptr(y), _ptr(pos), _ptr(gates), T, K, H, _ptr(out), _stream(stream)))
     return out
 
@@ -251,6 +324,13 @@ def moe_wgrad(a, lda, b, ldb, offsets, e_local, M, N, cap_rows, dw=None, a_col0=
     if dw is None:
         dw = torch.empty((e_local, M, N), dtype=torch.float32, device=a.device)
     _need(dw, torch.float32, "dw")
+    _shape(dw, (e_local, M, N), "dw")
+    if offsets.numel() < e_local + 1:
+        raise MoeError(f"offsets: expected {e_local + 1} entries, got {offsets.numel()}")
+    # rows r < cap_rows are read at strides lda and ldb from the column offsets
+    for t, ld, c0, w, name in ((a, lda, a_col0, M, "a"), (b, ldb, b_col0, N, "b")):
+        if cap_rows > 0 and t.numel() < (cap_rows - 1) * ld + c0 + w:
+            raise MoeError(f"{name}: too small for {cap_rows} rows at stride {ld} from column {c0}")
     pa = a.data_ptr() + 2 * a_col0
     pb = b.data_ptr() + 2 * b_col0
     _check(load().moe_wgrad(pa, lda, pb, ldb, _ptr(offsets), e_local, M, N, cap_rows, _ptr(dw),
@@ -279,6 +359,11 @@ def moe_router_logits(x, w_r, bias=None, logits=None, ws=None, stream=None):
     E = w_r.shape[1]
     if logits is None:
         logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    _shape(w_r, (H, E), "w_r")
+    if bias is not None:
+        _shape(bias, (E,), "bias")
+    _need(logits, torch.float32, "logits")
+    _shape(logits, (T, E), "logits")
     ws = _router_ws(T, H, E, ws, x.device)
     _check(load().moe_router_logits(_ptr(x), T, H, _ptr(w_r), E, _ptr(bias), _ptr(logits), _ptr(ws), ws.numel(),
                                     _stream(stream)))
@@ -296,6 +381,12 @@ def moe_router_backward(x, w_r, dlogits, dx=None, dw_r=None, ws=None, stream=Non
         dx = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
     if dw_r is None:
         dw_r = torch.empty((H, E), dtype=torch.float32, device=x.device)
+    _shape(w_r, (H, E), "w_r")
+    _shape(dlogits, (T, E), "dlogits")
+    _need(dx, torch.bfloat16, "dx")
+    _shape(dx, (T, H), "dx")
+    _need(dw_r, torch.float32, "dw_r")
+    _shape(dw_r, (H, E), "dw_r")
     ws = _router_ws(T, H, E, ws, x.device)
     _check(load().moe_router_backward(_ptr(x), T, H, _ptr(w_r), E, _ptr(dlogits), _ptr(dx), _ptr(dw_r), _ptr(ws),
                                       ws.numel(), _stream(stream)))

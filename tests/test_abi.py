@@ -186,3 +186,19 @@ def test_pair_index_division_by_reciprocal():
             q = (v * rcp) >> 32
             q = q + ((v - q * K) >= K)
             assert np.array_equal(q, v // K), K
+
+
+def test_binding_rejects_wrong_buffer_shapes():
+    """The Python binding checks every caller buffer's shape before a kernel could write past it
+    (the C ABI sees only pointers).  CPU tensors never reach a kernel: the checks run first."""
+    import torch
+
+    # the binding requires CUDA tensors first; on the CPU, check the shape helpers directly
+    with pytest.raises(_lib.MoeError):
+        _lib._shape(torch.empty(3, 4), (3, 5), "t")
+    with pytest.raises(_lib.MoeError):
+        _lib._rows(torch.empty(7, 4), 8, 4, "t")
+    with pytest.raises(_lib.MoeError):
+        _lib._rows(torch.empty(9, 5), 8, 4, "t")
+    _lib._rows(torch.empty(9, 4), 8, 4, "t")
+    _lib._shape(torch.empty(3, 4), (3, 4), "t")
