@@ -189,11 +189,10 @@ def test_pair_index_division_by_reciprocal():
 
 
 def test_binding_rejects_wrong_buffer_shapes():
-    """The Python binding checks every caller buffer's shape before a kernel could write past it
-    (the C ABI sees only pointers).  CPU tensors never reach a kernel: the checks run first."""
+    """The shape checks the binding applies to every caller buffer before the C call (the C ABI sees
+    only pointers), exercised on CPU tensors; the wrappers themselves take CUDA tensors only."""
     import torch
 
-    # the binding requires CUDA tensors first; on the CPU, check the shape helpers directly
     with pytest.raises(_lib.MoeError):
         _lib._shape(torch.empty(3, 4), (3, 5), "t")
     with pytest.raises(_lib.MoeError):

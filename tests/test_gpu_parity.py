@@ -232,3 +232,21 @@ def test_layer_matches_oracle_in_every_tile_configuration(name, tile, monkeypatc
     inp = synth.make_inputs(shape, seed=4, d_out=True)
     buf, _ = run_gpu(shape, inp)
     check_layer(shape, inp, buf, shape.cap)
+
+
+def test_binding_rejects_undersized_outputs():
+    """A caller buffer that is too small is refused before any kernel runs."""
+    shape = SMALL["tiny"]
+    inp = synth.make_inputs(shape, seed=1)
+    dev = pipeline.to_device(inp)
+    buf = pipeline.MoeBuffers.allocate(shape, backward=False)
+    pipeline.forward(buf, dev)
+    T, H, K = shape.T, shape.H, shape.K
+    with pytest.raises(_lib.MoeError):
+        _lib.moe_combine(buf.y, buf.pos, buf.gates, out=torch.empty((T - 1, H), dtype=torch.bfloat16, device="cuda"))
+    with pytest.raises(_lib.MoeError):
+        _lib.moe_route(dev["logits"], K, topk_idx=torch.empty((T, K - 1), dtype=torch.int32, device="cuda"))
+    with pytest.raises(_lib.MoeError):
+        _lib.moe_grouped_gemm_swiglu(buf.x_perm, dev["w_gate"], dev["w_up"], buf.offsets, buf.cap,
+                                     h=torch.empty((buf.cap - 1, shape.F), dtype=torch.bfloat16, device="cuda"))
+    torch.cuda.synchronize()
