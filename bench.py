@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--graph", action="store_true",
                     help="also time K replays of the whole step captured in a HIP graph (reported as "
                          "graph_ms_per_step; value stays the eager timed pass)")
+    ap.add_argument("--dense-reference", action="store_true",
+                    help="MFMA-bound dominant GEMM: also time torch.matmul (hipBLASLt) on a dense bf16 GEMM of "
+                         "the same rows x depth x width, as a vendor-library reference on this GPU")
     ap.add_argument("--copy-rows", action="store_true",
                     help="forward-only workloads: permute with the row copy instead of zero-copy dispatch")
     ap.add_argument("--calib-copy", action="store_true",
@@ -185,6 +188,34 @@ def measured_copy_gbps(stream):
     ms = e0.elapsed_time(e1) / 5
     del a, b
     return round(2 * n / (ms * 1e-3) / 1e9, 1)
+
+
+# (depth, width) of each GroupGEMM step as one dense product over all routed rows
+def dense_dims(name, shape):
+    H, F = shape.H, shape.F
+    return {"expert_up": (H, 2 * F), "expert_down": (F, H), "bwd_down_dgrad": (H, F), "bwd_up_dgrad": (2 * F, H),
+            "wgrad_gate": None, "wgrad_up": None, "wgrad_down": None}.get(name)
+
+
+def dense_reference(M, Kd, N, steps):
+    """TFLOP/s of torch.matmul (hipBLASLt) on a dense [M,Kd] x [Kd,N] bf16 product."""
+    import torch
+    a = torch.randn(M, Kd, device="cuda").to(torch.bfloat16)
+    b = (torch.randn(Kd, N, device="cuda") * 0.02).to(torch.bfloat16)
+    for _ in range(2):
+        c = a @ b
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        c = a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    del a, b, c
+    tf = 2 * M * Kd * N / (ms * 1e-3) / 1e12
+    return dict(library="torch.matmul (hipBLASLt)", shape=[M, Kd, N], ms=round(ms, 4), achieved=round(tf, 2),
+                frac=round(tf / MFMA_BF16_PEAK_TFS, 4))
 
 
 def main():
@@ -353,6 +384,9 @@ def main():
     }
     if graph_ms is not None:
         result["graph_ms_per_step"] = round(graph_ms, 4)
+    if args.dense_reference and rl["bound"] == "mfma" and dense_dims(dom, shape):
+        kd, n = dense_dims(dom, shape)
+        result["dense_reference"] = dense_reference(R, kd, n, max(3, args.steps // 4))
     if status != 0:
         result["warning"] = "row capacity overflow: rows were dropped"
     if not args.no_cpu_baseline:
