@@ -463,9 +463,10 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
                     const uint32_t v = (uint32_t)si[u * 64];
                     uint32_t tok = __umulhi(v, p.topk_rcp);
                     if (v - tok * (uint32_t)p.topk >= (uint32_t)p.topk) ++tok;
-                    // the lane's 16-byte column chunk is folded in here
+                    // the lane's 16-byte column chunk (its swizzle by load index) is folded in here
+                    const uint32_t lt = LY::kc_period(u * TL::kWaves + wave) ? lt_a1 : lt_a0;
                     c_rowoff[u] = a_rowl < ic.valid - a_row0(u) && tok < (uint32_t)p.a_rows
-                                      ? tok * (uint32_t)(p.lda * 2) + lt_a0
+                                      ? tok * (uint32_t)(p.lda * 2) + lt
                                       : kOOB;
                 }
                 idx_buf ^= 1;
