@@ -190,6 +190,32 @@ def measured_copy_gbps(stream):
     return round(2 * n / (ms * 1e-3) / 1e9, 1)
 
 
+def measured_mfma_tflops(stream, target_ms=20.0):
+    """TFLOP/s that back-to-back bf16 MFMAs reach on this GPU with N(0,1) operands held in registers
+    (libmoe's probe, one workgroup of four waves per CU): the practical ceiling of an MFMA-bound kernel
+    on real data, since the clock the chip holds under MFMA load depends on the operand bits."""
+    import torch
+    from routing_permute_groupgemm_amd import _lib
+    blocks = torch.cuda.get_device_properties(0).multi_processor_count
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    ops = torch.randn((blocks * 4, 8, 64, 8), device="cuda", generator=gen).to(torch.bfloat16)
+    out = torch.empty((blocks * 4, 64), dtype=torch.float32, device="cuda")
+    flop_per_iter = blocks * 4 * 16 * 2 * 32 * 32 * 16
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def run(iters):
+        e0.record(stream)
+        _lib.moe_probe_mfma(ops, iters, out=out)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    iters = max(1, int(2000 * target_ms / max(run(2000), 1e-3)))
+    rates = [flop_per_iter * iters / (run(iters) * 1e-3) / 1e12 for _ in range(3)]
+    del ops, out
+    return round(float(np.median(rates)), 1)
+
+
 # (depth, width) of each GroupGEMM step as one dense product over all routed rows
 def dense_dims(name, shape):
     H, F = shape.H, shape.F
@@ -356,6 +382,9 @@ def main():
     if rl["bound"] == "hbm":
         # the spec peak above; beside it the rate a plain copy reaches on this GPU
         rl["measured_copy_gbps"] = measured_copy_gbps(stream)
+    else:
+        # likewise the rate back-to-back MFMAs on random operands reach on this GPU
+        rl["measured_mfma_tflops"] = measured_mfma_tflops(stream)
     gemm_names = [n for n in per if n.startswith(("expert_", "bwd_down_dgrad", "bwd_up_dgrad", "wgrad_"))]
     gemm_flops = sum(work[n]["flops"] for n in gemm_names)
     gemm_ms = sum(per[n] for n in gemm_names)

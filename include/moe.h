@@ -285,6 +285,24 @@ int moe_router_backward(const moe_bf16* x, int T, int H, const moe_bf16* w_r, in
                         const float* dlogits, moe_bf16* dx, float* dw_r, void* ws,
                         size_t ws_bytes, moe_stream stream);
 
+/*
+ * Measurement aid, not a step of the layer: the bf16 MFMA rate this GPU
+ * sustains.  Each of the blocks x 4 waves keeps its own 8 fragments of
+ * operands in registers and runs iters rounds of a 4 x 4 block of
+ * independent 32x32x16 bf16 MFMAs (16 * 32768 flop per round and wave),
+ * then writes one float per lane: the sum of its accumulator elements.
+ *   operands  bf16 [blocks*4][8][64][8]: for wave w, fragments 0..3 are its
+ *             A operands, 4..7 its B operands; lane l of fragment f holds the
+ *             8 values at [w][f][l][0..7].
+ *   out       fp32 [blocks*4*64].
+ * For each wave the sum of out over its 64 lanes equals
+ *   iters * sum_{m,n<4} sum_{h<2, j<8} (sum_{l in half h} A_m[l][j]) * (sum_{l in half h} B_n[l][j])
+ * (lanes 0..31 and 32..63 carry the two halves of the 16-deep contraction).
+ * blocks in 1..2^20, iters >= 0 (MOE_EINVAL), both pointers 16-byte aligned
+ * (MOE_EALIGN).  The caller owns both buffers; nothing is allocated.
+ */
+int moe_probe_mfma(const moe_bf16* operands, int blocks, int iters, float* out, moe_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -36,6 +36,7 @@ SIGNATURES = {
     "moe_router_workspace_size": ([_i, _i, _i], _z),
     "moe_router_logits": ([_p, _i, _i, _p, _i, _p, _p, _p, _z, _p], _i),
     "moe_router_backward": ([_p, _i, _i, _p, _i, _p, _p, _p, _p, _z, _p], _i),
+    "moe_probe_mfma": ([_p, _i, _i, _p, _p], _i),
 }
 
 MOE_EPI_NONE = 0
@@ -391,3 +392,18 @@ def moe_router_backward(x, w_r, dlogits, dx=None, dw_r=None, ws=None, stream=Non
     _check(load().moe_router_backward(_ptr(x), T, H, _ptr(w_r), E, _ptr(dlogits), _ptr(dx), _ptr(dw_r), _ptr(ws),
                                       ws.numel(), _stream(stream)))
     return dx, dw_r
+
+
+def moe_probe_mfma(operands, iters, out=None, stream=None):
+    """Measurement aid: back-to-back bf16 MFMAs on register-held operands.
+    operands bf16 [blocks*4, 8, 64, 8] (per wave: 4 A then 4 B fragments) -> out fp32 [blocks*4, 64]."""
+    _need(operands, torch.bfloat16, "operands")
+    if operands.dim() != 4 or tuple(operands.shape[1:]) != (8, 64, 8) or operands.shape[0] % 4:
+        raise MoeError(f"operands: expected shape (4*blocks, 8, 64, 8), got {tuple(operands.shape)}")
+    waves = operands.shape[0]
+    if out is None:
+        out = torch.empty((waves, 64), dtype=torch.float32, device=operands.device)
+    _need(out, torch.float32, "out")
+    _shape(out, (waves, 64), "out")
+    _check(load().moe_probe_mfma(_ptr(operands), waves // 4, iters, _ptr(out), _stream(stream)))
+    return out

@@ -1,0 +1,55 @@
+// MFMA throughput probe: a measurement aid beside the layer's path.
+//
+// The GroupGEMMs are priced against the bf16 MFMA peak of the data sheet
+// (256 CUs x 4096 flop per clock x 2.4 GHz).  Under sustained MFMA load the
+// chip holds a lower clock, and how much lower depends on the operand bits,
+// so a bench also reports what back-to-back MFMAs reach on this GPU with the
+// caller's operands: every wave keeps four A and four B fragments in
+// registers and runs a 4 x 4 block of independent 32x32x16 bf16 MFMAs, the
+// accumulator footprint of the GroupGEMM's 128 x 128 wave tile, with no
+// memory traffic inside the loop.
+#include "moe_common.hpp"
+
+namespace moe {
+
+__global__ __launch_bounds__(256) void mfma_probe_kernel(const bf16x8* __restrict__ ops, int iters,
+                                                         float* __restrict__ out) {
+    const int lane = threadIdx.x & 63;
+    const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const bf16x8* o = ops + w * 8 * 64 + lane;
+    bf16x8 a[4], b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        a[i] = o[i * 64];
+        b[i] = o[(4 + i) * 64];
+    }
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int n = 0; n < 4; ++n) acc[m][n] = f32x16{};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int n = 0; n < 4; ++n)
+                acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m], b[n], acc[m][n], 0, 0, 0);
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int n = 0; n < 4; ++n)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s += acc[m][n][i];
+    out[w * 64 + lane] = s;
+}
+
+}  // namespace moe
+
+extern "C" int moe_probe_mfma(const moe_bf16* operands, int blocks, int iters, float* out, moe_stream stream) {
+    if (blocks < 1 || blocks > (1 << 20) || iters < 0 || !operands || !out) return MOE_EINVAL;
+    if (moe_host::misaligned(operands) || moe_host::misaligned(out)) return MOE_EALIGN;
+    moe::mfma_probe_kernel<<<blocks, 256, 0, (hipStream_t)stream>>>((const moe::bf16x8*)operands, iters, out);
+    return moe_host::launch_status();
+}

@@ -201,3 +201,13 @@ def test_binding_rejects_wrong_buffer_shapes():
         _lib._rows(torch.empty(9, 5), 8, 4, "t")
     _lib._rows(torch.empty(9, 4), 8, 4, "t")
     _lib._shape(torch.empty(3, 4), (3, 4), "t")
+
+
+def test_probe_rejects():
+    lib = _lib.load()
+    p = lib.moe_probe_mfma
+    assert p(FAKE, 0, 10, FAKE, None) == -1      # no blocks
+    assert p(FAKE, 4, -1, FAKE, None) == -1      # negative iteration count
+    assert p(None, 4, 10, FAKE, None) == -1
+    assert p(FAKE, 4, 10, None, None) == -1
+    assert p(MIS, 4, 10, FAKE, None) == -3

@@ -1,0 +1,41 @@
+"""The MFMA throughput probe (a measurement aid for the bench) computes what it
+claims: per wave, iters rounds of a 4 x 4 block of 32x32x16 bf16 products of
+its register-held fragments.  With operands in {-1, 0, 1} every product and
+sum is exact in fp32, so the sum over a wave's lanes must equal the closed
+form of the header exactly: each 16-deep contraction splits into the lanes
+0..31 and 32..63 halves, and the sum of all entries of A.B is the sum over
+the contraction index of (column sums of A) x (row sums of B)."""
+import numpy as np
+import pytest
+import torch
+
+from routing_permute_groupgemm_amd import _lib
+
+pytestmark = pytest.mark.gpu
+
+
+def expected_wave_sums(ops, iters):
+    """ops int [waves, 8, 64, 8]: fragments 0..3 are A, 4..7 are B."""
+    o = ops.astype(np.float64).reshape(ops.shape[0], 8, 2, 32, 8)  # [w, frag, half, lane%32, j]
+    col = o.sum(axis=3)                                              # [w, frag, half, j]
+    a, b = col[:, :4], col[:, 4:]
+    return iters * np.einsum("wmhj,wnhj->w", a, b)
+
+
+@pytest.mark.parametrize("blocks,iters", [(1, 1), (3, 7), (256, 64)])
+def test_probe_matches_closed_form(blocks, iters):
+    rng = np.random.default_rng(blocks * 1000 + iters)
+    ops = rng.integers(-1, 2, size=(blocks * 4, 8, 64, 8))
+    dev = torch.from_numpy(ops.astype(np.float32)).to(torch.bfloat16).cuda()
+    out = _lib.moe_probe_mfma(dev, iters)
+    torch.cuda.synchronize()
+    got = out.double().sum(dim=1).cpu().numpy()
+    np.testing.assert_array_equal(got, expected_wave_sums(ops, iters))
+
+
+def test_probe_zero_iterations_writes_zeros():
+    ops = torch.ones((8, 8, 64, 8), dtype=torch.bfloat16, device="cuda")
+    out = torch.full((8, 64), 7.0, dtype=torch.float32, device="cuda")
+    _lib.moe_probe_mfma(ops, 0, out=out)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out).item() == 0
