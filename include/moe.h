@@ -34,7 +34,9 @@
  *    atomics, every sum has a fixed order.
  *  - Rows of the permuted buffers at or beyond R are unspecified.
  *  - Limits: H and F multiples of 64; 1 <= K <= 16, K <= E <= 512;
- *    e_local <= 512; T*K < 2^31; cap_rows <= T*K.
+ *    e_local <= 512; T*K < 2^31; cap_rows <= T*K; one expert's weight
+ *    matrix below 2 GiB (H*F*2 < 2^31) and 256 rows of any GEMM operand
+ *    below 2 GiB, since load offsets are 32-bit (MOE_EINVAL).
  */
 #ifndef MOE_H
 #define MOE_H
@@ -229,8 +231,9 @@ int moe_grouped_gemm(const moe_bf16* a, int lda, const moe_bf16* w0, const moe_b
  * in fp32 from +0; a token with no local pair gets +0.  gates == NULL means
  * weight 1: the backward's combine-gradient dX[t] = sum_k dx_perm[pos[t,k]]
  * (MoonEP: the dispatch gradient sums each token's K copies).
- *   y bf16 [cap_rows,H];  pos int32 [T,K];  gates fp32 [T,K] or NULL;
- *   out bf16 [T,H].
+ *   y bf16 [cap_rows,H];  pos int32 [T,K] as moe_permute writes it (-1, or
+ *   a row of y: the rows are not bounds-checked);  gates fp32 [T,K] or
+ *   NULL;  out bf16 [T,H].
  */
 int moe_combine(const moe_bf16* y, const int32_t* pos, const float* gates,
                 int T, int K, int H, moe_bf16* out, moe_stream stream);

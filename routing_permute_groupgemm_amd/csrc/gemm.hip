@@ -1003,7 +1003,9 @@ extern "C" int moe_grouped_gemm_swiglu(const moe_bf16* x_perm, const moe_bf16* w
     if (misaligned(x_perm) || misaligned(w_gate) || misaligned(w_up) || misaligned(offsets) || misaligned(h) ||
         misaligned(ab_save))
         return MOE_EALIGN;
-    if ((int64_t)256 * H * 2 >= (1ll << 31) || (int64_t)64 * F * 2 >= (1ll << 31)) return MOE_EINVAL;
+    // load offsets are 32-bit and those at or past 2^31 mean "out of range":
+    // 256 rows of A, and one expert's whole weight matrix, stay below that
+    if ((int64_t)256 * H * 2 >= (1ll << 31) || (int64_t)H * F * 2 >= (1ll << 31)) return MOE_EINVAL;
     GemmParams p{};
     p.a = x_perm;
     p.lda = H;
@@ -1033,7 +1035,7 @@ extern "C" int moe_grouped_gemm_swiglu_gather(const moe_bf16* x, int T, const in
     if (H % 64 || F % 64) return MOE_ESHAPE;
     // every A load offset (row * H * 2 + column bytes) must stay below the
     // out-of-range offset that masks rows past an expert's end
-    if ((int64_t)T * H * 2 >= (1ll << 31) || (int64_t)64 * F * 2 >= (1ll << 31)) return MOE_EINVAL;
+    if ((int64_t)T * H * 2 >= (1ll << 31) || (int64_t)H * F * 2 >= (1ll << 31)) return MOE_EINVAL;
     if ((int64_t)cap_rows > (int64_t)T * K) return MOE_EINVAL;
     if (!offsets) return MOE_EINVAL;
     if (e_local == 0 || cap_rows == 0 || F == 0) return MOE_OK;
@@ -1081,8 +1083,9 @@ extern "C" int moe_grouped_gemm(const moe_bf16* a, int lda, const moe_bf16* w0, 
     if (misaligned(a) || misaligned(w0) || misaligned(w1) || misaligned(offsets) || misaligned(ab) ||
         misaligned(c))
         return MOE_EALIGN;
+    // 32-bit load offsets below 2^31 (see moe_grouped_gemm_swiglu)
     if ((int64_t)256 * lda * 2 >= (1ll << 31) || (int64_t)256 * Kd * 2 >= (1ll << 31) ||
-        (int64_t)64 * N * 2 >= (1ll << 31))
+        (int64_t)Kd * N * 2 >= (1ll << 31))
         return MOE_EINVAL;
     GemmParams p{};
     p.a = a;

@@ -146,6 +146,12 @@ def test_gemm_rejects():
     assert lib.moe_grouped_gemm(FAKE, 64, FAKE, FAKE, 1, FAKE, 4, 64, 64, 16, 0, None, FAKE, 64, None) == -1
     assert lib.moe_grouped_gemm(FAKE, 64, FAKE, None, 0, FAKE, 4, 64, 64, 16, 7, None, FAKE, 64, None) == -1
     assert lib.moe_grouped_gemm(FAKE, 64, FAKE, None, 1, FAKE, 4, 64, 64, 16, 1, None, FAKE, 128, None) == -1
+    # one expert's weight matrix of 2 GiB or more (32-bit load offsets)
+    assert lib.moe_grouped_gemm_swiglu(FAKE, FAKE, FAKE, FAKE, 4, 16384, 65536, 16, FAKE, None, None) == -1
+    assert lib.moe_grouped_gemm_swiglu_gather(FAKE, 8, FAKE, 2, FAKE, FAKE, FAKE, 4, 16384, 65536, 16, FAKE,
+                                              None, None) == -1
+    assert lib.moe_grouped_gemm(FAKE, 16384, FAKE, None, 0, FAKE, 4, 16384, 65536, 16, 0, None, FAKE, 65536,
+                                None) == -1
     assert lib.moe_wgrad(FAKE, 64, FAKE, 64, FAKE, 4, 96, 64, 16, FAKE, None) == -2
     assert lib.moe_wgrad(FAKE, 32, FAKE, 64, FAKE, 4, 64, 64, 16, FAKE, None) == -1
     assert lib.moe_combine(FAKE, FAKE, None, 8, 2, 100, FAKE, None) == -2
