@@ -26,6 +26,9 @@
 //              strictly in pair order; writes pos and src.
 //  4. copy:    one wave per token reads the token's row once (16-byte
 //              loads) and writes it to each of its local destination rows.
+// With TB = 64 and at most 256 blocks, step 2 runs inside step 3 instead:
+// every rank block reads the whole count matrix (at most 8192 entries) and
+// derives its own first rows, which costs less than the one-block launch.
 #include "moe_common.hpp"
 
 namespace moe {
@@ -143,15 +146,77 @@ __device__ __forceinline__ uint64_t match_key(int key, bool active, int nbits) {
     return m;
 }
 
-// KMAX: an upper bound of the rounds of 64 pairs per wave (tb/4 tokens * K pairs)
-template <int KMAX>
+// Largest block count for which the rank kernel also does the scan: each of
+// its blocks then reads the whole e_local x nblk count matrix (at most 8192
+// entries), which stays cheap only while the blocks are few.
+constexpr int kFusedScanBlocks = 256;
+
+// KMAX: an upper bound of the rounds of 64 pairs per wave (tb/4 tokens * K pairs).
+// FUSED: ws holds the raw per-(expert, block) counts and every block derives
+// its own first row per expert from them (the expert's offset, an exclusive
+// scan of the totals over experts, plus the counts of the blocks before it);
+// block 0 also writes counts, offsets and status.  Otherwise ws holds those
+// first rows already (the scan kernel's output).
+template <int KMAX, bool FUSED>
 __global__ __launch_bounds__(256) void perm_rank_kernel(const int32_t* __restrict__ idx, int T, int K,
                                                         int e_begin, int e_local, int nbits, int nblk, int tb,
                                                         const int32_t* __restrict__ ws, int64_t cap_rows,
-                                                        int32_t* __restrict__ pos, int32_t* __restrict__ src) {
+                                                        int32_t* __restrict__ pos, int32_t* __restrict__ src,
+                                                        int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                        int32_t* __restrict__ status) {
     __shared__ int cnt[4][kMaxLocal];
+    __shared__ int s_base[FUSED ? kMaxLocal : 1];   // FUSED: this block's first row per expert
+    __shared__ int s_tot[FUSED ? kMaxLocal : 1];
+    __shared__ int s_wsum[4];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     for (int j = lane; j < e_local; j += 64) cnt[wave][j] = 0;
+    if constexpr (FUSED) {
+        for (int j = threadIdx.x; j < e_local; j += 256) s_base[j] = s_tot[j] = 0;
+        __syncthreads();
+        // per expert: the total over all blocks and the part before this block
+        // (integer adds, so the order of the LDS atomics does not matter)
+        const int64_t n = (int64_t)e_local * nblk;
+        for (int64_t q = threadIdx.x; q < n; q += 256) {
+            const int c = ws[q];
+            const int j = (int)(q / nblk), b = (int)(q - (int64_t)j * nblk);
+            if (c) {
+                atomicAdd(&s_tot[j], c);
+                if (b < (int)blockIdx.x) atomicAdd(&s_base[j], c);
+            }
+        }
+        __syncthreads();
+        // exclusive scan of the totals over experts: thread i owns experts 2i, 2i+1
+        const int j0 = 2 * threadIdx.x;
+        const int t0 = j0 < e_local ? s_tot[j0] : 0, t1 = j0 + 1 < e_local ? s_tot[j0 + 1] : 0;
+        int v = t0 + t1;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int o = __shfl_up(v, off, 64);
+            if (lane >= off) v += o;
+        }
+        if (lane == 63) s_wsum[wave] = v;
+        __syncthreads();
+        int before = 0;
+        for (int w = 0; w < wave; ++w) before += s_wsum[w];
+        const int off0 = before + v - (t0 + t1);
+        if (j0 < e_local) s_base[j0] += off0;
+        if (j0 + 1 < e_local) s_base[j0 + 1] += off0 + t0;
+        if (blockIdx.x == 0) {
+            if (j0 < e_local) {
+                counts[j0] = t0;
+                offsets[j0] = off0;
+            }
+            if (j0 + 1 < e_local) {
+                counts[j0 + 1] = t1;
+                offsets[j0 + 1] = off0 + t0;
+            }
+            if (threadIdx.x == 0) {
+                const int total = s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
+                offsets[e_local] = total;
+                status[0] = (int64_t)total > cap_rows ? 1 : 0;
+            }
+        }
+    }
     __syncthreads();
     const int64_t npairs = (int64_t)T * K;
     // wave `wave` owns the pairs of tb/4 consecutive tokens, [p0, pend), in
@@ -200,7 +265,8 @@ __global__ __launch_bounds__(256) void perm_rank_kernel(const int32_t* __restric
                 int j = jj[it];
                 int row = -1;
                 if (j >= 0) {
-                    int64_t r = (int64_t)ws[(int64_t)j * nblk + blockIdx.x] + cnt[wave][j] + rk[it];
+                    const int first = FUSED ? s_base[j] : ws[(int64_t)j * nblk + blockIdx.x];
+                    int64_t r = (int64_t)first + cnt[wave][j] + rk[it];
                     if (r < cap_rows) {
                         row = (int)r;
                         src[r] = (int32_t)p;
@@ -286,19 +352,25 @@ extern "C" int moe_permute(const int32_t* topk_idx, int T, int K, int e_begin, i
     int nbits = 0;
     while ((1 << nbits) < e_local) ++nbits;
     int32_t* w = (int32_t*)ws;
+    // few blocks of the small token block: the rank kernel does the scan too
+    const bool fused = tb == 64 && nblk > 0 && nblk <= kFusedScanBlocks;
     if (nblk > 0 && e_local > 0)
         perm_count_kernel<<<nblk, 256, 0, s>>>(topk_idx, T, K, e_begin, e_local, nblk, tb, w);
-    perm_scan_kernel<<<1, 1024, 0, s>>>(w, e_local, nblk, cap_rows, counts, offsets, status);
+    if (!fused) perm_scan_kernel<<<1, 1024, 0, s>>>(w, e_local, nblk, cap_rows, counts, offsets, status);
     if (nblk > 0) {
-        if (rounds <= 4)
-            perm_rank_kernel<4><<<nblk, 256, 0, s>>>(topk_idx, T, K, e_begin, e_local, nbits, nblk, tb, w,
-                                                    cap_rows, pos, src);
-        else if (rounds <= 8)
-            perm_rank_kernel<8><<<nblk, 256, 0, s>>>(topk_idx, T, K, e_begin, e_local, nbits, nblk, tb, w,
-                                                    cap_rows, pos, src);
-        else
-            perm_rank_kernel<16><<<nblk, 256, 0, s>>>(topk_idx, T, K, e_begin, e_local, nbits, nblk, tb, w,
-                                                     cap_rows, pos, src);
+#define MOE_RANK(KM, FU)                                                                                    \
+    perm_rank_kernel<KM, FU><<<nblk, 256, 0, s>>>(topk_idx, T, K, e_begin, e_local, nbits, nblk, tb, w, cap_rows, \
+                                                  pos, src, counts, offsets, status)
+        if (fused) {
+            if (rounds <= 4) MOE_RANK(4, true);
+            else if (rounds <= 8) MOE_RANK(8, true);
+            else MOE_RANK(16, true);
+        } else {
+            if (rounds <= 4) MOE_RANK(4, false);
+            else if (rounds <= 8) MOE_RANK(8, false);
+            else MOE_RANK(16, false);
+        }
+#undef MOE_RANK
         if (H > 0 && x_perm)
             perm_copy_kernel<4><<<(T + 3) / 4, 256, 0, s>>>((const u32x4*)x, T, K, H, pos, (u32x4*)x_perm);
     }

@@ -163,6 +163,18 @@ def test_zero_tokens():
     assert offsets.tolist() == [0] * 9 and counts.tolist() == [0] * 8 and status[0].item() == 0
 
 
+def test_permute_no_local_experts():
+    """Tokens but no local experts: every pair is non-local (pos -1), offsets [0], status 0."""
+    idx = torch.randint(0, 8, (100, 2), dtype=torch.int32, device="cuda")
+    x = torch.zeros((100, 64), dtype=torch.bfloat16, device="cuda")
+    offsets = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+    status = torch.full((4,), -7, dtype=torch.int32, device="cuda")
+    out = _lib.moe_permute(idx, 0, 0, x, 0, out=dict(offsets=offsets, status=status), copy_rows=False)
+    torch.cuda.synchronize()
+    assert offsets.tolist() == [0] and status[0].item() == 0
+    assert torch.all(out["pos"] == -1).item()
+
+
 def test_wgrad_empty_expert_writes_zeros_and_grid_independence():
     """An expert with no rows gets exact zeros; a rerun (the persistent grid
     visits tiles in a different interleaving across workgroups) is identical."""
@@ -199,14 +211,17 @@ def test_route_ties_and_signed_zeros(E, K):
     assert_close("gates", bits(g), ref_g)
 
 
-@pytest.mark.parametrize("T,K", [(8192, 8), (8193, 8), (20000, 4)])
-def test_permute_local_share_and_capacity(T, K):
-    """A local share (experts 8..47 of 64) at several thousand tokens: counts, offsets, pos, src and
+# (T, K, local experts): the permute's three schedules.  64-token blocks with the scan done inside the
+# rank kernel (at most 256 blocks; 256 exactly for T=16384), 64-token blocks with the one-block scan
+# (313 blocks), and 256-token blocks (blocks x local experts above 8192).
+@pytest.mark.parametrize("T,K,EL", [(8192, 8, 40), (8193, 8, 40), (16384, 4, 16), (20000, 4, 16), (20000, 4, 40)])
+def test_permute_local_share_and_capacity(T, K, EL):
+    """A local share (experts 8.. of 64) at several thousand tokens: counts, offsets, pos, src and
     x_perm exactly as the oracle's, with the expected capacity and with half of it (rows dropped)."""
-    shape = synth.MoeShape(f"paths_T{T}_K{K}", 93, T=T, H=64, F=64, E=64, K=K, e_begin=8, e_local=40)
+    shape = synth.MoeShape(f"paths_T{T}_K{K}", 93, T=T, H=64, F=64, E=64, K=K, e_begin=8, e_local=EL)
     inp = synth.make_inputs(shape, seed=5)
     dev = pipeline.to_device(inp)
-    for cap in (shape.cap, shape.T * shape.K * 40 // 64 // 2):
+    for cap in (shape.cap, shape.T * shape.K * EL // 64 // 2):
         buf = pipeline.MoeBuffers.allocate(shape, cap=cap, backward=False)
         pipeline.route(buf, dev["logits"])
         pipeline.permute(buf, dev["x"])
