@@ -163,6 +163,18 @@ def test_zero_tokens():
     assert offsets.tolist() == [0] * 9 and counts.tolist() == [0] * 8 and status[0].item() == 0
 
 
+def test_layer_at_the_largest_expert_counts():
+    """The largest E (512, all local: the most groups a GroupGEMM takes) with the largest K (16): most
+    experts get a handful of rows, some none, and the ranking matches 9-bit expert ids."""
+    shape = synth.MoeShape("max_experts", 97, T=150, H=128, F=64, E=512, K=16, backward=True)
+    inp = synth.make_inputs(shape, seed=3, d_out=True)
+    buf, _ = run_gpu(shape, inp)
+    ref = check_layer(shape, inp, buf, shape.cap)
+    counts = ref["counts"]
+    print(f"[parity] max_experts: rows per expert {counts.min()}..{counts.max()}, "
+          f"{int(np.sum(counts == 0))} empty", flush=True)
+
+
 def test_permute_no_local_experts():
     """Tokens but no local experts: every pair is non-local (pos -1), offsets [0], status 0."""
     idx = torch.randint(0, 8, (100, 2), dtype=torch.int32, device="cuda")
