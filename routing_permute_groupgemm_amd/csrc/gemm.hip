@@ -44,6 +44,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "moe_common.hpp"
 
@@ -324,6 +325,13 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
     }
 
     // B column (within the BN-wide tile) of this wave's nt-th 32-column MFMA tile
+    // first row (within the tile) of the wave's mt-th 32-row MFMA tile.  In
+    // bodies that leave MFMA rows idle past a tile's valid rows the row
+    // blocks are dealt to the wave rows in turn (block mt*WM + wm), so both
+    // wave rows keep an equal share; elsewhere each wave row owns a run.
+    auto row_base = [&](int mt) {
+        return (SCHED == SCHED_ROWS && BM < 256) ? (mt * WM + wm) * 32 : wm * (BM / WM) + mt * 32;
+    };
     auto col_of = [&](int nt) {
         if (EPI == EPI_SWIGLU) {
             constexpr int HW = BN / 2 / WN;  // h columns per wave
@@ -611,12 +619,15 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
     // Two fragment buffers: the fragments of k16 step s+1 are read while
     // the MFMAs of step s run.
     bf16x8 af[2][MTW], bfv[2][NTW];
-    auto load_frags = [&](int slot, int kk, int buf) {
+    // Reading the fragments of NB of the wave's MFMA rows (the others stay
+    // idle for tiles whose valid rows end before them).
+    auto load_frags = [&](int slot, int kk, int buf, auto nb_tag) {
+        constexpr int NB = decltype(nb_tag)::value;
         const uint8_t* sA = smem + slot * TL::kStage;
         const uint8_t* sB = sA + TL::kABytes;
 #pragma unroll
-        for (int mt = 0; mt < MTW; ++mt) {
-            const int rb = wm * (BM / WM) + mt * 32;
+        for (int mt = 0; mt < NB; ++mt) {
+            const int rb = row_base(mt);
             af[buf][mt] = SCHED == SCHED_ROWS ? LY::frag_kc(sA, rb, kk, lane) : LY::frag_mn(sA, rb, kk, lane);
         }
 #pragma unroll
@@ -626,12 +637,6 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
                                                                  : LY::frag_mn(sB, cb, kk, lane);
         }
     };
-    // LDS reads one fragment set takes: a KC fragment is one 16-byte read,
-    // an MN fragment two transposing 8-byte reads
-    constexpr int kReadsA = SCHED == SCHED_ROWS ? MTW : 2 * MTW;
-    constexpr int kReadsB = (SCHED == SCHED_ROWS && LB == LAY_KC) ? NTW : 2 * NTW;
-    constexpr int kReads = kReadsA + kReadsB;
-    constexpr int kMfma = MTW * NTW;
     static_assert(KK == 2, "two k16 steps per stage");
 
     // Pipeline over a ring of S LDS stages, loads S-1 stages ahead.  The k16
@@ -654,6 +659,61 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
     pf_issued = false;  // the prologue's wait covered any prefetch
 
     unsigned gs = 0;  // global stage index of this workgroup; its LDS slot is gs % S
+    // One stage of the current tile on NB of the wave's MFMA rows.
+    auto stage = [&](auto nb_tag) {
+        constexpr int NB = decltype(nb_tag)::value;
+        // LDS reads one fragment set takes: a KC fragment is one 16-byte read,
+        // an MN fragment two transposing 8-byte reads
+        constexpr int kReadsA = SCHED == SCHED_ROWS ? NB : 2 * NB;
+        constexpr int kReadsB = (SCHED == SCHED_ROWS && LB == LAY_KC) ? NTW : 2 * NTW;
+        constexpr int kReads = kReadsA + kReadsB;
+        constexpr int kMfma = NB * NTW;
+        const bool live = itile < n_tiles_total;
+        const int kn = ik;  // the issue cursor's stage, loaded into the slot of gs-1
+        const int nslot = (int)((gs + S - 1) % S);
+        const int slot = (int)(gs % S), slot1 = (int)((gs + 1) % S);
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            // next step: (gs, 1) or (gs+1, 0)
+            if (kk + 1 < KK) load_frags(slot, kk + 1, (kk + 1) & 1, nb_tag);
+            else load_frags(slot1, 0, (kk + 1) & 1, nb_tag);
+#pragma unroll
+            for (int mt = 0; mt < NB; ++mt) {
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt)
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfv[kk & 1][nt], af[kk & 1][mt],
+                                                                          acc[mt][nt], 0, 0, 0);
+                // this step's share of the stage's loads, spread over its MFMA rows
+                const int lo = kk * LPW / KK, n = (kk + 1) * LPW / KK - lo;
+#pragma unroll
+                for (int i = 0; i < LPW; ++i)
+                    if (i < n && i * NB / n == mt) load_one(kn, nslot, lo + i, live);
+            }
+            // each MFMA followed by its share of the LDS reads (at most one
+            // per MFMA when there are more MFMAs than reads)
+            constexpr int kPer = (kReads + kMfma - 1) / kMfma;
+#pragma unroll
+            for (int t = 0; t < kMfma; ++t) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                if (t * kPer < kReads) __builtin_amdgcn_sched_group_barrier(0x100, kPer, 0);  // LDS reads
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        advance();
+        if (GATHER && pf_issued) {
+            // the LA index loads advance() just issued are the newest
+            pf_issued = false;
+            wait_vmcnt<kWaitLoads + LA>();
+        } else {
+            wait_vmcnt<kWaitLoads>();
+        }
+        __syncthreads();
+    };
+    auto run_tile = [&](int KT, auto nb_tag) {
+        if (KT > 0) load_frags((int)(gs % S), 0, 0, nb_tag);
+        for (int kt = 0; kt < KT; ++kt, ++gs) stage(nb_tag);
+    };
+
     for (int tile = tile0; tile < n_tiles_total; tile += G) {
         const TileDesc cd = decode(tile);
         const int j = cd.j, row0 = cd.row0, valid = cd.valid, ni = cd.ni, mi_w = cd.mi_w, KT = cd.KT, ks = cd.ks;
@@ -661,48 +721,73 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
         for (int a = 0; a < MTW; ++a)
 #pragma unroll
             for (int b = 0; b < NTW; ++b) acc[a][b] = f32x16{};
-        if (KT > 0) load_frags((int)(gs % S), 0, 0);
-        for (int kt = 0; kt < KT; ++kt, ++gs) {
-            const bool live = itile < n_tiles_total;
-            const int kn = ik;  // the issue cursor's stage, loaded into the slot of gs-1
-            const int nslot = (int)((gs + S - 1) % S);
-            const int slot = (int)(gs % S), slot1 = (int)((gs + 1) % S);
+        // Row-tiled GEMMs: the wave's MFMA rows that hold valid rows (row
+        // blocks are dealt to the waves in turn, so both wave rows keep an
+        // equal share); the rest of the wave's rows stay idle.  Every wave
+        // still issues its loads and meets every barrier of every stage.
+        // Tiles whose rows fill every MFMA row of the wave (and every tile of
+        // the 256-row body, the large workloads' body) run the loop written
+        // out below; the stage lambda compiles into slower code for them.
+        constexpr bool kIdleRows = SCHED == SCHED_ROWS && BM < 256;
+        int nb = MTW;
+        if (kIdleRows) {
+            const int blocks = (valid + 31) / 32;
+            nb = __builtin_amdgcn_readfirstlane(min(MTW, max(1, (blocks - wm + WM - 1) / WM)));
+        }
+        if (!kIdleRows || nb >= MTW) {
+            constexpr int kReadsA = SCHED == SCHED_ROWS ? MTW : 2 * MTW;
+            constexpr int kReadsB = (SCHED == SCHED_ROWS && LB == LAY_KC) ? NTW : 2 * NTW;
+            constexpr int kReads = kReadsA + kReadsB;
+            constexpr int kMfma = MTW * NTW;
+            constexpr auto kAll = std::integral_constant<int, MTW>{};
+            if (KT > 0) load_frags((int)(gs % S), 0, 0, kAll);
+            for (int kt = 0; kt < KT; ++kt, ++gs) {
+                const bool live = itile < n_tiles_total;
+                const int kn = ik;  // the issue cursor's stage, loaded into the slot of gs-1
+                const int nslot = (int)((gs + S - 1) % S);
+                const int slot = (int)(gs % S), slot1 = (int)((gs + 1) % S);
 #pragma unroll
-            for (int kk = 0; kk < KK; ++kk) {
-                // next step: (gs, 1) or (gs+1, 0)
-                if (kk + 1 < KK) load_frags(slot, kk + 1, (kk + 1) & 1);
-                else load_frags(slot1, 0, (kk + 1) & 1);
+                for (int kk = 0; kk < KK; ++kk) {
+                    // next step: (gs, 1) or (gs+1, 0)
+                    if (kk + 1 < KK) load_frags(slot, kk + 1, (kk + 1) & 1, kAll);
+                    else load_frags(slot1, 0, (kk + 1) & 1, kAll);
 #pragma unroll
-                for (int mt = 0; mt < MTW; ++mt) {
+                    for (int mt = 0; mt < MTW; ++mt) {
 #pragma unroll
-                    for (int nt = 0; nt < NTW; ++nt)
-                        acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfv[kk & 1][nt], af[kk & 1][mt],
-                                                                              acc[mt][nt], 0, 0, 0);
-                    // this step's share of the stage's loads, spread over its MFMA rows
-                    const int lo = kk * LPW / KK, n = (kk + 1) * LPW / KK - lo;
+                        for (int nt = 0; nt < NTW; ++nt)
+                            acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfv[kk & 1][nt], af[kk & 1][mt],
+                                                                                  acc[mt][nt], 0, 0, 0);
+                        // this step's share of the stage's loads, spread over its MFMA rows
+                        const int lo = kk * LPW / KK, n = (kk + 1) * LPW / KK - lo;
 #pragma unroll
-                    for (int i = 0; i < LPW; ++i)
-                        if (i < n && i * MTW / n == mt) load_one(kn, nslot, lo + i, live);
+                        for (int i = 0; i < LPW; ++i)
+                            if (i < n && i * MTW / n == mt) load_one(kn, nslot, lo + i, live);
+                    }
+                    constexpr int kPer = (kReads + kMfma - 1) / kMfma;
+#pragma unroll
+                    for (int t = 0; t < kMfma; ++t) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                        if (t * kPer < kReads) __builtin_amdgcn_sched_group_barrier(0x100, kPer, 0);  // LDS reads
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-                // each MFMA followed by its share of the LDS reads (at most one
-                // per MFMA when there are more MFMAs than reads)
-                constexpr int kPer = (kReads + kMfma - 1) / kMfma;
-#pragma unroll
-                for (int t = 0; t < kMfma; ++t) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-                    if (t * kPer < kReads) __builtin_amdgcn_sched_group_barrier(0x100, kPer, 0);  // LDS reads
+                advance();
+                if (GATHER && pf_issued) {
+                    pf_issued = false;
+                    wait_vmcnt<kWaitLoads + LA>();
+                } else {
+                    wait_vmcnt<kWaitLoads>();
                 }
-                __builtin_amdgcn_sched_barrier(0);
+                __syncthreads();
             }
-            advance();
-            if (GATHER && pf_issued) {
-                // the LA index loads advance() just issued are the newest
-                pf_issued = false;
-                wait_vmcnt<kWaitLoads + LA>();
+        } else if constexpr (kIdleRows) {
+            // fewer MFMA rows than the wave has (nb < MTW <= 3)
+            if constexpr (MTW >= 3) {
+                if (nb >= 2) run_tile(KT, std::integral_constant<int, 2>{});
+                else run_tile(KT, std::integral_constant<int, 1>{});
             } else {
-                wait_vmcnt<kWaitLoads>();
+                run_tile(KT, std::integral_constant<int, 1>{});
             }
-            __syncthreads();
         }
 
         // ---- epilogue: lane holds row (l%32) and columns 8*j4 + 4*(l/32) + 0..3 ----
@@ -744,7 +829,7 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
                     for (int i = 0; i < 4; ++i) {
                         const int rr = 8 * i + (lane >> 3), c = lane & 7;
                         const u32x4 v = *(const MOE_LDS u32x4*)stage_addr(rr, c);
-                        const int mloc = wm * (BM / WM) + mt * 32 + rr;
+                        const int mloc = row_base(mt) + rr;
                         if (EPI == EPI_BF16) {
                             const int n = ni * BN + wn * (BN / WN) + 64 * np + 8 * c;
                             if (mloc < valid && n < p.N) *(u32x4*)(p.c + (int64_t)(row0 + mloc) * p.ldc + n) = v;
@@ -774,7 +859,7 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
         const int cq = 4 * (lane >> 5);
 #pragma unroll
         for (int mt = 0; mt < MTW; ++mt) {
-            const int mloc = wm * (BM / WM) + mt * 32 + (lane & 31);
+            const int mloc = row_base(mt) + (lane & 31);
             if (SCHED == SCHED_WGRAD) {
                 const int m = mi_w * BM + mloc;
                 if (m >= p.M) continue;
