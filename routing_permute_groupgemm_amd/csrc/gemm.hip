@@ -729,6 +729,7 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
         // the 256-row body, the large workloads' body) run the loop written
         // out below; the stage lambda compiles into slower code for them.
         constexpr bool kIdleRows = SCHED == SCHED_ROWS && BM < 256;
+        static_assert(!kIdleRows || MTW <= 3, "idle-row bodies have at most three MFMA rows per wave");
         int nb = MTW;
         if (kIdleRows) {
             const int blocks = (valid + 31) / 32;
