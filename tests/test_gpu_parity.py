@@ -261,6 +261,45 @@ def test_layer_matches_oracle_in_every_tile_configuration(name, tile, monkeypatc
     check_layer(shape, inp, buf, shape.cap)
 
 
+# Row counts on each side of the 32-row MFMA blocks and of the 128/192/256-row tiles: the 128- and
+# 192-row bodies run only the MFMA rows that hold valid rows, with the row blocks dealt to the two
+# wave rows in turn, so a tile of up to 32 rows leaves one wave row without a valid block.
+EDGE_COUNTS = [1, 31, 32, 33, 63, 64, 65, 95, 96, 97, 127, 128, 129, 159, 160, 161, 191, 192, 193, 255, 256, 257,
+               0, 300]
+
+
+@pytest.mark.parametrize("tile", ["0", "256", "192", "128"])
+def test_gemms_at_row_block_edges(tile, monkeypatch):
+    """Gate/up (copy and zero-copy) and down GroupGEMMs on experts whose row counts sit at every
+    row-block and tile edge, element by element against the oracle, in each tile configuration
+    (0: the automatic choice)."""
+    monkeypatch.setenv("MOE_GEMM_TILE", tile)
+    counts = np.array(EDGE_COUNTS, np.int32)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R, EL, H, F, K = int(offsets[-1]), len(counts), 128, 192, 1
+    x_perm = synth.operand_bf16((R, H), seed=31, tag=1)
+    wg = synth.operand_bf16((EL, H, F), seed=31, tag=2, std=0.05)
+    wu = synth.operand_bf16((EL, H, F), seed=31, tag=3, std=0.05)
+    wd = synth.operand_bf16((EL, F, H), seed=31, tag=4, std=0.05)
+    hin = synth.operand_bf16((R, F), seed=31, tag=5)
+    dev = pipeline.to_device(dict(x=x_perm, wg=wg, wu=wu, wd=wd, h=hin, off=offsets,
+                                  src=np.arange(R, dtype=np.int32)))
+    h = torch.empty((R, F), dtype=torch.bfloat16, device="cuda")
+    ab = torch.empty((R, 2 * F), dtype=torch.bfloat16, device="cuda")
+    _lib.moe_grouped_gemm_swiglu(dev["x"], dev["wg"], dev["wu"], dev["off"], R, h=h, ab_save=ab)
+    # zero-copy with K = 1: row r of the grouped order is token src[r] = r
+    hz = torch.empty_like(h)
+    _lib.moe_grouped_gemm_swiglu_gather(dev["x"], dev["src"], K, dev["wg"], dev["wu"], dev["off"], R, h=hz)
+    y = torch.empty((R, H), dtype=torch.bfloat16, device="cuda")
+    _lib.moe_grouped_gemm(dev["h"], dev["wd"], None, 0, dev["off"], F, H, R, y)
+    torch.cuda.synchronize()
+    ref_h, ref_ab = oracle.expert_up(x_perm, wg, wu, offsets, R, want_ab=True)
+    assert_close("h", bits(h), ref_h)
+    assert_close("ab_save", bits(ab), ref_ab)
+    assert torch.equal(h.view(torch.int16), hz.view(torch.int16))
+    assert_close("y", bits(y), oracle.expert_down(hin, wd, offsets, R))
+
+
 def test_binding_rejects_undersized_outputs():
     """A caller buffer that is too small is refused before any kernel runs."""
     shape = SMALL["tiny"]
