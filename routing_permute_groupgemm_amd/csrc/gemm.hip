@@ -801,7 +801,13 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
             // 16-byte chunks XOR-swizzled by row.
             static_assert(TL::kStage / TL::kWaves >= 4096, "staging space per wave");
             uint8_t* stg = smem + ((gs + S - 1) % S) * TL::kStage + wave * 4096;
-            const int r = lane & 31, h = lane >> 5;
+            // the lane id passes through an opaque copy: the addresses derived
+            // from it are rebuilt here, per tile, instead of being hoisted out
+            // of the tile loop, where the 256-row body has no registers left
+            // for them and spills them (each reload then waits for every
+            // store issued before it)
+            const int ln = opaque(lane);
+            const int r = ln & 31, h = ln >> 5;
             auto stage_addr = [&](int row, int chunk) {
                 return (MOE_LDS uint8_t*)(stg + row * 128 + ((chunk ^ (row & 7)) << 4));
             };
@@ -828,7 +834,7 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
                     // read back 8 rows x 128 bytes per instruction and store whole lines
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int rr = 8 * i + (lane >> 3), c = lane & 7;
+                        const int rr = 8 * i + (ln >> 3), c = ln & 7;
                         const u32x4 v = *(const MOE_LDS u32x4*)stage_addr(rr, c);
                         const int mloc = row_base(mt) + rr;
                         if (EPI == EPI_BF16) {
