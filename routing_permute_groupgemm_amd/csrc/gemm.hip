@@ -216,6 +216,16 @@ __device__ __forceinline__ float silu_f(float a) { return a * sigmoid_f(a); }
 
 __device__ __forceinline__ int xcd_remap(int b, int G) { return (b & 7) * (G >> 3) + (b >> 3); }
 
+// The lane id (0..63) read from the hardware where it is needed: the asm can be
+// neither hoisted nor merged, so no lane-derived value stays live across the
+// persistent tile loop (the large bodies would spill it, and every reload
+// waits for all the loads and stores in flight).
+__device__ __forceinline__ int lane_id_here() {
+    int v;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(v));
+    return v;
+}
+
 // Block tile BM x BN (B columns; for SWIGLU the gate half then the up half),
 // contraction step BK, a ring of STAGES LDS stages, WM x WN waves each owning a
 // (BM/WM) x (BN/WN) tile of 32x32 MFMA tiles.
@@ -436,18 +446,13 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
     }
     // lane's row in A load u of this wave: rows q*16 + l/4 of the tile, the
     // uniform part q*16 and the lane part l/4
-    // (per-tile code takes the lane part through an opaque copy so that
-    // nothing derived from it is hoisted out of the loop and kept live)
+    // (per-tile code reads the lane id afresh, so that nothing derived from
+    // it is hoisted out of the loop and kept live)
     auto a_row0 = [&](int u) { return (u * TL::kWaves + wave) * LY::kRowsPerLoad; };
-    const int a_rowl_v = lane / LY::kChunks;
-    auto opaque = [](int v) {
-        asm volatile("" : "+v"(v));
-        return v;
-    };
     auto prefetch_rows = [&](int tile, int buf) {
         const TileDesc d = decode(tile);
         const uint32_t base = lds_addr(s_idx) + (uint32_t)(((buf * TL::kWaves + wave) * LA) * 256);
-        const int a_rowl = opaque(a_rowl_v);
+        const int a_rowl = lane_id_here() / LY::kChunks;
 #pragma unroll
         for (int u = 0; u < LA; ++u) {
             const uint32_t voff = (uint32_t)(d.row0 + a_row0(u)) * 4u + (uint32_t)a_rowl * 4u;
@@ -463,8 +468,9 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
         if (SCHED == SCHED_ROWS && itile < n_tiles_total) {
             if (GATHER) {
                 wait_vmcnt_mem<(S - 2) * LPW>();
-                const int a_rowl = opaque(a_rowl_v);
-                const int* si = s_idx + ((idx_buf * TL::kWaves + wave) * LA) * 64 + opaque(lane);
+                const int ln = lane_id_here();
+                const int a_rowl = ln / LY::kChunks;
+                const int* si = s_idx + ((idx_buf * TL::kWaves + wave) * LA) * 64 + ln;
 #pragma unroll
                 for (int u = 0; u < LA; ++u) {
                     // src = t*K + k; the quotient estimate is t or t - 1
@@ -801,18 +807,33 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
             // 16-byte chunks XOR-swizzled by row.
             static_assert(TL::kStage / TL::kWaves >= 4096, "staging space per wave");
             uint8_t* stg = smem + ((gs + S - 1) % S) * TL::kStage + wave * 4096;
-            // the lane id passes through an opaque copy: the addresses derived
-            // from it are rebuilt here, per tile, instead of being hoisted out
-            // of the tile loop, where the 256-row body has no registers left
-            // for them and spills them (each reload then waits for every
-            // store issued before it)
-            const int ln = opaque(lane);
+            // the addresses derived from the lane are rebuilt here, per tile,
+            // instead of being hoisted out of the tile loop, where the 256-row
+            // body has no registers left for them and spills them (each reload
+            // then waits for every store issued before it)
+            const int ln = lane_id_here();
             const int r = ln & 31, h = ln >> 5;
             auto stage_addr = [&](int row, int chunk) {
                 return (MOE_LDS uint8_t*)(stg + row * 128 + ((chunk ^ (row & 7)) << 4));
             };
             // column groups per round: 64 bf16 (two MFMA tiles) or 32 fp32 (one)
             constexpr int kTilesPerRound = EPI == EPI_BF16 ? 2 : 1;
+            // row-tiled fp32 output with a bias: the bias of this lane's
+            // columns is loaded, and waited for once, before the tile's first
+            // store (a load issued behind stores also waits for them)
+            constexpr bool kBias = EPI == EPI_F32 && SCHED == SCHED_ROWS;
+            f32x4 bias_v[kBias ? NTW : 1] = {};
+            if constexpr (kBias) {
+                if (p.bias) {
+#pragma unroll
+                    for (int np = 0; np < NTW; ++np) {
+                        const int n = ni * BN + wn * (BN / WN) + 32 * np + 4 * (ln & 7);
+                        if (n < p.N) bias_v[np] = *(const f32x4*)(p.bias + n);
+                    }
+#pragma unroll
+                    for (int np = 0; np < NTW; ++np) asm volatile("" ::"v"(bias_v[np]));
+                }
+            }
 #pragma unroll
             for (int mt = 0; mt < MTW; ++mt) {
 #pragma unroll
@@ -851,7 +872,7 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
                                 u32x4 w = v;
                                 if (p.bias) {
                                     f32x4 f = __builtin_bit_cast(f32x4, v);
-                                    f += *(const f32x4*)(p.bias + n);
+                                    f += bias_v[kBias ? np : 0];
                                     w = __builtin_bit_cast(u32x4, f);
                                 }
                                 *(u32x4*)(p.cf + ks * p.part_stride + (int64_t)(row0 + mloc) * p.ldc + n) = w;
