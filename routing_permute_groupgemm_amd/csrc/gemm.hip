@@ -932,36 +932,57 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
                         }
                     }
                 }
-            } else {
+            } else if (EPI == EPI_BF16) {
 #pragma unroll
                 for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
                     for (int j4 = 0; j4 < 4; ++j4) {
                         const int n = ni * BN + col_of(nt) + 8 * j4 + cq;
                         if (n >= p.N) continue;
-                        float v[4];
+                        const f32x16& a = acc[mt][nt];
+                        u32x2 w = {pack_bf2(a[4 * j4], a[4 * j4 + 1]), pack_bf2(a[4 * j4 + 2], a[4 * j4 + 3])};
+                        *(u32x2*)(p.c + row * p.ldc + n) = w;
+                    }
+            } else {  // EPI_SWIGLU_BWD: the accumulators are dh
+                // the row block's saved (a, b) pairs are all loaded before any
+                // of its results is stored: a load issued behind stores also
+                // waits for them
+                u32x2 aw[NTW][4], bw[NTW][4];
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) v[i] = acc[mt][nt][4 * j4 + i];
-                        if (EPI == EPI_BF16) {
-                            u32x2 w = {pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])};
-                            *(u32x2*)(p.c + row * p.ldc + n) = w;
-                        } else {  // EPI_SWIGLU_BWD: v is dh
-                            u32x2 aw = *(const u32x2*)(p.ab + row * 2 * p.N + n);
-                            u32x2 bw = *(const u32x2*)(p.ab + row * 2 * p.N + p.N + n);
-                            float da[4], db[4];
+                for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
-                            for (int i = 0; i < 4; ++i) {
-                                float a = (i & 1) ? bf_hi(aw[i >> 1]) : bf_lo(aw[i >> 1]);
-                                float b = (i & 1) ? bf_hi(bw[i >> 1]) : bf_lo(bw[i >> 1]);
-                                float s = sigmoid_f(a);
-                                da[i] = v[i] * b * s * (1.0f + a * (1.0f - s));
-                                db[i] = v[i] * a * s;
-                            }
-                            u32x2 dw = {pack_bf2(da[0], da[1]), pack_bf2(da[2], da[3])};
-                            u32x2 ew = {pack_bf2(db[0], db[1]), pack_bf2(db[2], db[3])};
-                            *(u32x2*)(p.c + row * p.ldc + n) = dw;
-                            *(u32x2*)(p.c + row * p.ldc + p.N + n) = ew;
+                    for (int j4 = 0; j4 < 4; ++j4) {
+                        const int n = ni * BN + col_of(nt) + 8 * j4 + cq;
+                        aw[nt][j4] = bw[nt][j4] = u32x2{0u, 0u};
+                        if (n < p.N) {
+                            aw[nt][j4] = *(const u32x2*)(p.ab + row * 2 * p.N + n);
+                            bw[nt][j4] = *(const u32x2*)(p.ab + row * 2 * p.N + p.N + n);
                         }
+                    }
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+                    for (int j4 = 0; j4 < 4; ++j4) asm volatile("" ::"v"(aw[nt][j4]), "v"(bw[nt][j4]));
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+                    for (int j4 = 0; j4 < 4; ++j4) {
+                        const int n = ni * BN + col_of(nt) + 8 * j4 + cq;
+                        if (n >= p.N) continue;
+                        float da[4], db[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const float v = acc[mt][nt][4 * j4 + i];
+                            float a = (i & 1) ? bf_hi(aw[nt][j4][i >> 1]) : bf_lo(aw[nt][j4][i >> 1]);
+                            float b = (i & 1) ? bf_hi(bw[nt][j4][i >> 1]) : bf_lo(bw[nt][j4][i >> 1]);
+                            float s = sigmoid_f(a);
+                            da[i] = v * b * s * (1.0f + a * (1.0f - s));
+                            db[i] = v * a * s;
+                        }
+                        u32x2 dw = {pack_bf2(da[0], da[1]), pack_bf2(da[2], da[3])};
+                        u32x2 ew = {pack_bf2(db[0], db[1]), pack_bf2(db[2], db[3])};
+                        *(u32x2*)(p.c + row * p.ldc + n) = dw;
+                        *(u32x2*)(p.c + row * p.ldc + p.N + n) = ew;
                     }
             }
         }
