@@ -18,7 +18,7 @@ from routing_permute_groupgemm_amd import _lib, pipeline, synth
 pytestmark = pytest.mark.gpu
 
 W = synth.WORKLOADS
-# (shape, why): contraction split or not, E of 64/128/256, ragged T, long H
+# (shape, why): contraction split or not, E of 64/128/256/320, ragged T, long H
 SMALL = [
     (W["ep_share_4k"].scaled(T=512, H=256), "E=256, weight gradient in 2 row chunks"),
     (W["ep_share_4k"].scaled(T=512, H=1024), "E=256, contraction in 4 chunks"),
@@ -26,6 +26,10 @@ SMALL = [
     (synth.MoeShape("e64", 91, T=2048, H=128, F=64, E=64, K=4), "E=64"),
     (W["ep_share_4k"].scaled(T=64, H=7168), "few rows, long contraction"),
     (W["fwdbwd_16k"].scaled(T=4096, H=192), "many rows, short contraction"),
+    (synth.MoeShape("e320s", 92, T=2048, H=64, F=64, E=320, K=4),
+     "E=320 on 128-column tiles: three column tiles, the last half full, bias in the GEMM epilogue"),
+    (synth.MoeShape("e320", 93, T=32768, H=128, F=64, E=320, K=4),
+     "E=320 on 256-column tiles: two column tiles, bias in the GEMM epilogue"),
 ]
 
 
