@@ -7,13 +7,18 @@ SwiGLU -> down GroupGEMM -> combine, plus (workloads with a backward) the
 gate-scaled gather, both dgrad GroupGEMMs, the combine-gradient and the three
 weight-gradient GroupGEMMs.  Every step is a libmoe C-ABI call on one stream.
 
-Prints one JSON line: tokens/s, plus the roofline of the dominant kernel
-(achieved algorithmic bytes or flops per launch / its mean launch time, from
-HIP events recorded on the launch stream around that kernel in the timed
-steps) and the CPU oracle's throughput on a bounded sample of the same
-workload.  `step_ms` comes from an untimed pass with events around every
-step: each recorded event costs the stream a short bubble, so the timed pass
-records them around the dominant step only.
+The headline workload (default ep_share_128k: T=131072, H=7168, F=2048, the
+32 local experts of E=256, K=8, forward+backward with the row-copy permute) is
+timed first.  Prints one JSON line: tokens/s, the roofline of the dominant
+kernel (achieved algorithmic bytes or flops per launch / its mean launch time,
+from HIP events recorded on the launch stream around that kernel in the timed
+steps), every GroupGEMM's fraction of the bf16 MFMA peak, the permute's and
+the combine's fraction of HBM bandwidth, one summary per --also workload
+(timed the same way, after the headline's buffers are freed) and the CPU
+oracle's throughput on a bounded sample of the headline workload.  `step_ms`
+comes from an untimed pass with events around every step: each recorded event
+costs the stream a short bubble, so the timed pass records them around the
+dominant step only.
 """
 from __future__ import annotations
 
@@ -40,9 +45,14 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="ep_share_4k")
+    ap.add_argument("--workload", default="ep_share_128k",
+                    help="the headline workload (default: the largest one-GPU configuration, forward+backward)")
+    ap.add_argument("--also", default="ep_share_4k,skew_8k,fwdbwd_16k",
+                    help="comma-separated workloads also timed after the headline, reported under 'workloads' "
+                         "(empty: none)")
+    ap.add_argument("--also-steps", type=int, default=10, help="timed steps of each --also workload")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the CPU-oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--router", action="store_true",
                     help="include the router projection x.W_r (and its backward) in the step; the pages' layer "
@@ -51,8 +61,8 @@ def parse():
                     help="also time K replays of the whole step captured in a HIP graph (reported as "
                          "graph_ms_per_step; value stays the eager timed pass)")
     ap.add_argument("--dense-reference", action="store_true",
-                    help="MFMA-bound dominant GEMM: also time torch.matmul (hipBLASLt) on a dense bf16 GEMM of "
-                         "the same rows x depth x width, as a vendor-library reference on this GPU")
+                    help="also time torch.matmul (hipBLASLt) on a dense bf16 GEMM of each row-tiled GroupGEMM's "
+                         "rows x depth x width, as a vendor-library reference on this GPU")
     ap.add_argument("--copy-rows", action="store_true",
                     help="forward-only workloads: permute with the row copy instead of zero-copy dispatch")
     ap.add_argument("--calib-copy", action="store_true",
@@ -125,37 +135,43 @@ def measured_traffic(kernel, workload):
 
 
 def cpu_baseline(shape, inp, budget_s):
-    """The oracle as it stands on contiguous token chunks of the same workload, cycling through the batch
-    until the budget is spent (a small batch is passed over more than once)."""
+    """The oracle as it stands, timed on the first n tokens of the same batch (the tokens are i.i.d.): one
+    forward and, for workloads with a backward, one backward whose weight gradients sum over every routed
+    row of the sample, as the GPU step sums over every row of the batch.  n comes from two calibration
+    passes (128 and 512 tokens) that separate the per-token time from the fixed part (the fp32 weight
+    gradients are written in full whatever the sample), so the timed pass takes about budget_s."""
     import oracle
     T, K, EL = shape.T, shape.K, shape.EL
-    chunk = max(16, min(T, 256))
-    t0 = time.perf_counter()
-    done = 0  # tokens processed, repeats included
-    while True:
-        lo = done % T
-        hi = min(T, lo + chunk)
-        sub = {k: inp[k][lo:hi] for k in ("logits", "x")}
+
+    def run(n):
+        sub = {k: inp[k][:n] for k in ("logits", "x")}
         sub.update({k: inp[k] for k in ("w_gate", "w_up", "w_down")})
-        cap = (hi - lo) * K
+        cap = n * K
+        t0 = time.perf_counter()
         fwd = oracle.forward(sub, shape.e_begin, EL, K, cap)
         if shape.backward:
-            sub["d_out"] = inp["d_out"][lo:hi]
+            sub["d_out"] = inp["d_out"][:n]
             oracle.backward(sub, fwd, cap)
-        done += hi - lo
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = time.perf_counter() - t0
+        return time.perf_counter() - t0
+
+    n1, n2 = min(T, 128), min(T, 512)
+    t1 = run(n1)
+    t2 = run(n2) if n2 > n1 else t1
+    slope = max((t2 - t1) / max(n2 - n1, 1), 1e-7)
+    fixed = max(t1 - slope * n1, 0.0)
+    n = int(min(T, max(n2, (budget_s - fixed) / slope)))
+    dt = run(n) if n > n2 else t2
     cpu = "unknown"
     try:
         with open("/proc/cpuinfo") as fh:
             cpu = next(line.split(":", 1)[1].strip() for line in fh if line.startswith("model name"))
     except (OSError, StopIteration):
         pass
-    return dict(value=round(done / dt, 2), unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
+    what = "forward+backward pass (weight gradients over the sample's rows)" if shape.backward else "forward pass"
+    return dict(value=round(n / dt, 2), unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
                 cpu=cpu, host_cpus=os.cpu_count(),
-                sample=f"{done} tokens ({done / T:.2f} passes over the {T}-token batch) in chunks of {chunk} "
-                       f"({'forward+backward' if shape.backward else 'forward'}), {dt:.1f} s")
+                sample=f"first {n} of the {T} tokens, one {what}, {dt:.1f} s (n sized from 128- and "
+                       f"512-token calibration passes: {slope * 1e3:.2f} ms/token + {fixed:.1f} s fixed)")
 
 
 def calib_copy():
@@ -246,30 +262,16 @@ def dense_reference(M, Kd, N, steps):
                 frac=round(tf / MFMA_BF16_PEAK_TFS, 4))
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
-              "(expert-parallel sharding across GPUs is not built)", file=sys.stderr)
-        sys.exit(2)
+GEMM_STEPS = ("expert_up", "expert_down", "bwd_down_dgrad", "bwd_up_dgrad", "wgrad_gate", "wgrad_up", "wgrad_down")
+HBM_STEPS = ("route", "permute", "combine", "bwd_gather", "route_bwd", "bwd_combine")
+
+
+def layer_steps(shape, dev, buf, router):
+    """(name, call) of every step of one pass, in order; each call is one or more libmoe C-ABI calls."""
     import torch
-
-    if args.calib_copy:
-        calib_copy()
-        return
-    from routing_permute_groupgemm_amd import _lib, pipeline, synth
-
-    _lib.load()
-    shape = synth.WORKLOADS[args.workload]
-    print(f"[bench] {shape.name}: generating inputs", file=sys.stderr, flush=True)
-    inp = synth.make_inputs(shape, seed=args.seed, router=args.router)
-    dev = pipeline.to_device(inp)
-    zero_copy = not shape.backward and not args.copy_rows
-    buf = pipeline.MoeBuffers.allocate(shape, zero_copy=zero_copy)
-    stream = torch.cuda.current_stream()
-
+    from routing_permute_groupgemm_amd import _lib, pipeline
     steps = []
-    if args.router:
+    if router:
         T, H, E = shape.T, shape.H, shape.E
         r_ws = torch.empty(max(_lib.moe_router_workspace_size(T, H, E), 256), dtype=torch.uint8, device="cuda")
         r_logits = torch.empty((T, E), dtype=torch.float32, device="cuda")
@@ -277,10 +279,10 @@ def main():
                                                                    logits=r_logits, ws=r_ws)))
         dev["logits"] = r_logits  # the route step consumes the projected scores
     steps += [("route", lambda: pipeline.route(buf, dev["logits"])),
-             ("permute", lambda: pipeline.permute(buf, dev["x"])),
-             ("expert_up", lambda: pipeline.expert_up(buf, dev["w_gate"], dev["w_up"], dev["x"])),
-             ("expert_down", lambda: pipeline.expert_down(buf, dev["w_down"])),
-             ("combine", lambda: pipeline.combine(buf))]
+              ("permute", lambda: pipeline.permute(buf, dev["x"])),
+              ("expert_up", lambda: pipeline.expert_up(buf, dev["w_gate"], dev["w_up"], dev["x"])),
+              ("expert_down", lambda: pipeline.expert_down(buf, dev["w_down"])),
+              ("combine", lambda: pipeline.combine(buf))]
     if shape.backward:
         H, F, EL, cap = shape.H, shape.F, shape.EL, buf.cap
         steps += [
@@ -301,14 +303,21 @@ def main():
             ("wgrad_down", lambda: _lib.moe_wgrad(buf.h, F, buf.dy_perm, H, buf.offsets, EL, F, H, cap,
                                                   dw=buf.dw_down)),
         ]
-        if args.router:
+        if router:
             r_dx = torch.empty((shape.T, H), dtype=torch.bfloat16, device="cuda")
             r_dw = torch.empty((H, shape.E), dtype=torch.float32, device="cuda")
             steps.append(("router_bwd", lambda: _lib.moe_router_backward(dev["x"], dev["w_router"], buf.dlogits,
                                                                          dx=r_dx, dw_r=r_dw, ws=r_ws)))
+    return steps
+
+
+def time_steps(steps, stream, n_steps, warmup):
+    """Warm-up, then an untimed breakdown pass (events around every step: each step's mean time and the
+    dominant step), then the timed pass of n_steps whole steps, which records events only around the
+    dominant step (every recorded event costs the stream a short bubble)."""
+    import torch
 
     def one_step(evs=None, only=None):
-        # evs: events around every step (breakdown pass), or around step `only`
         for i, (_, fn) in enumerate(steps):
             if evs is not None and (only is None or i == only):
                 evs[0 if only is not None else i].record(stream)
@@ -318,36 +327,123 @@ def main():
         if evs is not None and only is None:
             evs[len(steps)].record(stream)
 
-    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         one_step()
     torch.cuda.synchronize()
-    # Breakdown pass (untimed): events around every step give each step's mean
-    # time and the dominant step.  Every recorded event costs the stream a
-    # bubble of a few microseconds, so the timed pass below records events only
-    # around the dominant step, which its roofline needs.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(steps) + 1)] for _ in range(args.steps)]
-    for k in range(args.steps):
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(steps) + 1)] for _ in range(n_steps)]
+    for k in range(n_steps):
         one_step(evs[k])
     torch.cuda.synchronize()
-    per = {name: float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)]))
+    per = {name: float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(n_steps)]))
            for i, (name, _) in enumerate(steps)}
     dom_i = max(range(len(steps)), key=lambda i: per[steps[i][0]])
-    dom = steps[dom_i][0]
-    dev_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    dev_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
-    for k in range(args.steps):
+    for k in range(n_steps):
         one_step(dev_evs[k], only=dom_i)
     end.record(stream)
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    ms_per_step = total_ms / args.steps
+    ms_per_step = start.elapsed_time(end) / n_steps
     dom_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in dev_evs]))
-    print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
+    return dict(per=per, dom=steps[dom_i][0], dom_ms=dom_ms, ms_per_step=ms_per_step, one_step=one_step)
+
+
+def routing_stats(buf):
+    offsets = buf.offsets.cpu().numpy()
+    counts = np.diff(offsets)
+    R = int(min(offsets[-1], buf.cap))
+    pos = buf.pos.cpu().numpy()
+    return dict(counts=counts, R=R, T_act=int(np.sum(np.any(pos >= 0, axis=1))), n_active=int(np.sum(counts > 0)),
+                status=int(buf.status[0].item()))
+
+
+def step_fracs(work, per):
+    """Fraction of its roofline reached by every GroupGEMM (bf16 MFMA) and every HBM-bound step."""
+    g = {n: round(work[n]["flops"] / (per[n] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4) for n in GEMM_STEPS if n in per}
+    h = {n: round(work[n]["bytes"] / (per[n] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4) for n in HBM_STEPS if n in per}
+    return g, h
+
+
+def run_workload(name, args, n_steps, warmup, log):
+    """Generate one workload's inputs, build its buffers and time it.  Returns the summary and the state the
+    headline needs afterwards (the caller drops it before the next workload)."""
+    import torch
+    from routing_permute_groupgemm_amd import pipeline, synth
+    shape = synth.WORKLOADS[name]
+    log(f"{shape.name}: generating inputs")
+    inp = synth.make_inputs(shape, seed=args.seed, router=args.router)
+    dev = pipeline.to_device(inp)
+    zero_copy = not shape.backward and not args.copy_rows
+    buf = pipeline.MoeBuffers.allocate(shape, zero_copy=zero_copy)
+    stream = torch.cuda.current_stream()
+    steps = layer_steps(shape, dev, buf, args.router)
+    log(f"{shape.name}: warmup {warmup}, then {n_steps} steps with events around every step and "
+        f"{n_steps} timed")
+    t = time_steps(steps, stream, n_steps, warmup)
+    log(f"{shape.name}: timed {n_steps} steps: {t['ms_per_step']:.3f} ms/step")
+    rs = routing_stats(buf)
+    work = algorithmic_work(shape, rs["R"], rs["T_act"], rs["n_active"], zero_copy, args.router)
+    per = t["per"]
+    gfrac, hfrac = step_fracs(work, per)
+    gemm_names = [n for n in GEMM_STEPS if n in per]
+    gemm_flops = sum(work[n]["flops"] for n in gemm_names)
+    gemm_ms = sum(per[n] for n in gemm_names)
+    summ = dict(
+        ms_per_step=round(t["ms_per_step"], 4),
+        tokens_per_s=round(shape.T / (t["ms_per_step"] * 1e-3), 1),
+        pass_="fwd+bwd" if shape.backward else "fwd",
+        dispatch="zero-copy" if zero_copy else "row copy",
+        routed_rows=rs["R"],
+        maxvio=round(synth.maxvio(rs["counts"], shape.T, shape.K, shape.E), 3),
+        dominant=t["dom"],
+        dominant_frac=roofline(work[t["dom"]], t["dom_ms"])["frac"],
+        groupgemm_mfma_frac=round(gemm_flops / (gemm_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4),
+        gemm_mfma_frac=gfrac,
+        hbm_frac=hfrac,
+        step_ms={k: round(v, 4) for k, v in per.items()},
+    )
+    if rs["status"] != 0:
+        summ["warning"] = "row capacity overflow: rows were dropped"
+    state = dict(shape=shape, inp=inp, dev=dev, buf=buf, steps=steps, t=t, work=work, rs=rs, zero_copy=zero_copy,
+                 stream=stream)
+    return summ, state
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
+              "(expert-parallel sharding across GPUs is not built)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    if args.calib_copy:
+        calib_copy()
+        return
+    from routing_permute_groupgemm_amd import _lib, synth
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    _lib.load()
+    summ, st = run_workload(args.workload, args, args.steps, args.warmup, log)
+    shape, buf, work, t, stream = st["shape"], st["buf"], st["work"], st["t"], st["stream"]
+    dom, dom_ms, per = t["dom"], t["dom_ms"], t["per"]
+    rl = roofline(work[dom], dom_ms)
+    rl["launch_ms"] = round(dom_ms, 4)  # the kernel's mean time between the events around it
+    rl["kernel"] = dom
+    rl["traffic"] = measured_traffic(dom, shape.name)
+    if rl["bound"] == "hbm":
+        # the spec peak above; beside it the rate a plain copy reaches on this GPU
+        rl["measured_copy_gbps"] = measured_copy_gbps(stream)
+    else:
+        # likewise the rate back-to-back MFMAs on random operands reach on this GPU
+        rl["measured_mfma_tflops"] = measured_mfma_tflops(stream)
     graph_ms = None
     if args.graph:
+        one_step = t["one_step"]
         side = torch.cuda.Stream()
         side.wait_stream(stream)
         with torch.cuda.stream(side):
@@ -367,61 +463,65 @@ def main():
         g1.record(stream)
         torch.cuda.synchronize()
         graph_ms = g0.elapsed_time(g1) / args.steps
-        print(f"[bench] graph replays: {graph_ms:.3f} ms/step", file=sys.stderr, flush=True)
-
-    status = int(buf.status[0].item())
-    offsets = buf.offsets.cpu().numpy()
-    counts = np.diff(offsets)
-    R = int(min(offsets[-1], buf.cap))
-    pos = buf.pos.cpu().numpy()
-    T_act = int(np.sum(np.any(pos >= 0, axis=1)))
-    n_active = int(np.sum(counts > 0))
-    work = algorithmic_work(shape, R, T_act, n_active, zero_copy, args.router)
-    rl = roofline(work[dom], dom_ms)
-    rl["launch_ms"] = round(dom_ms, 4)  # the kernel's mean time between the events around it
-    rl["kernel"] = dom
-    rl["traffic"] = measured_traffic(dom, shape.name)
-    if rl["bound"] == "hbm":
-        # the spec peak above; beside it the rate a plain copy reaches on this GPU
-        rl["measured_copy_gbps"] = measured_copy_gbps(stream)
-    else:
-        # likewise the rate back-to-back MFMAs on random operands reach on this GPU
-        rl["measured_mfma_tflops"] = measured_mfma_tflops(stream)
-    gemm_names = [n for n in per if n.startswith(("expert_", "bwd_down_dgrad", "bwd_up_dgrad", "wgrad_"))]
-    gemm_flops = sum(work[n]["flops"] for n in gemm_names)
-    gemm_ms = sum(per[n] for n in gemm_names)
+        log(f"graph replays: {graph_ms:.3f} ms/step")
+    perm_gbs = work["permute"]["bytes"] / (per["permute"] * 1e-3) / 1e9
+    comb_gbs = work["combine"]["bytes"] / (per["combine"] * 1e-3) / 1e9
     result = {
         "metric": "MoE layer tokens/s on 1 GPU; GroupGEMM % bf16 MFMA peak; permute GB/s",
-        "value": round(shape.T / (ms_per_step * 1e-3), 1),
+        "value": summ["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": summ["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": shape.name, "T": shape.T, "H": shape.H, "F": shape.F, "E": shape.E, "K": shape.K,
-                   "e_local": shape.EL, "cap_rows": buf.cap, "pass": "fwd+bwd" if shape.backward else "fwd",
-                   "dispatch": "zero-copy" if zero_copy else "row copy", "router_projection": args.router,
-                   "routed_rows": R, "maxvio": round(synth.maxvio(counts, shape.T, shape.K, shape.E), 3),
+                   "e_local": shape.EL, "cap_rows": buf.cap, "pass": summ["pass_"], "dispatch": summ["dispatch"],
+                   "router_projection": args.router, "routed_rows": summ["routed_rows"], "maxvio": summ["maxvio"],
                    "seed": args.seed, "parallelism": "single GPU"},
         "roofline": rl,
-        "groupgemm_mfma_frac": round(gemm_flops / (gemm_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4),
-        "permute_gbps": round(work["permute"]["bytes"] / (per["permute"] * 1e-3) / 1e9, 1),
-        "step_ms": {k: round(v, 4) for k, v in per.items()},
+        "groupgemm_mfma_frac": summ["groupgemm_mfma_frac"],
+        "gemm_mfma_frac": summ["gemm_mfma_frac"],
+        # the permute step as a whole (count, scan, rank and the row copy), on its algorithmic bytes
+        "permute_gbps": round(perm_gbs, 1),
+        "permute_hbm_frac": round(perm_gbs / HBM_PEAK_GBS, 4),
+        "permute_dispatch": summ["dispatch"],
+        "combine_gbps": round(comb_gbs, 1),
+        "combine_hbm_frac": round(comb_gbs / HBM_PEAK_GBS, 4),
+        "hbm_frac": summ["hbm_frac"],
+        "step_ms": summ["step_ms"],
     }
     if graph_ms is not None:
         result["graph_ms_per_step"] = round(graph_ms, 4)
-    if args.dense_reference and rl["bound"] == "mfma" and dense_dims(dom, shape):
-        kd, n = dense_dims(dom, shape)
-        result["dense_reference"] = dense_reference(R, kd, n, max(3, args.steps // 4))
-    if status != 0:
-        result["warning"] = "row capacity overflow: rows were dropped"
+    if args.dense_reference:
+        refs = {}
+        for n in GEMM_STEPS:
+            if n in per and dense_dims(n, shape):
+                kd, nn = dense_dims(n, shape)
+                refs[n] = dense_reference(summ["routed_rows"], kd, nn, max(3, args.steps // 4))
+        result["dense_reference"] = refs
+    if "warning" in summ:
+        result["warning"] = summ["warning"]
+    inp = st["inp"]
+    del st, buf
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    others = [w for w in args.also.split(",") if w and w != args.workload]
+    if others:
+        result["workloads"] = {}
+        for name in others:
+            s2, st2 = run_workload(name, args, args.also_steps, min(args.warmup, 3), log)
+            del st2
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+            s2["pass"] = s2.pop("pass_")
+            result["workloads"][name] = s2
     if not args.no_cpu_baseline:
-        print(f"[bench] cpu baseline (~{args.cpu_seconds:.0f} s)", file=sys.stderr, flush=True)
+        log(f"cpu baseline (~{args.cpu_seconds:.0f} s)")
         result["cpu_baseline"] = cpu_baseline(shape, inp, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
