@@ -22,8 +22,9 @@
  * Conventions common to every entry point:
  *  - All data pointers are DEVICE pointers, owned by the caller, and must be
  *    16-byte aligned.  The library allocates nothing and keeps no state
- *    between calls; calls on different streams with disjoint buffers may
- *    run concurrently.
+ *    between calls (the one exception is moe_permute_noalloc's device
+ *    array); calls on different streams with disjoint buffers may run
+ *    concurrently.
  *  - Arguments are validated on the host before anything is enqueued; a
  *    negative moe_status is returned and nothing runs on error.  Launch
  *    failures are reported as MOE_EHIP.
@@ -129,6 +130,31 @@ int moe_permute(const int32_t* topk_idx, int T, int K, int e_begin, int e_local,
                 int32_t* counts, int32_t* offsets, int32_t* pos, int32_t* src,
                 moe_bf16* x_perm, int32_t* status, void* ws, size_t ws_bytes,
                 moe_stream stream);
+
+/*
+ * moe_permute for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same permutation with the same results, but the per-(expert, block) count
+ * matrix that moe_permute keeps in the caller's ws lives in a device array of
+ * this library instead, MOE_PERMUTE_SCRATCH_BYTES per GPU, held until the
+ * process ends.  Nothing is allocated: no hipMalloc, hipFree or allocating
+ * library call.  The array's device address is looked up once per device
+ * (hipGetSymbolAddress) on the first call with that device current.
+ *   Arguments as moe_permute, without ws / ws_bytes.
+ *   Errors: as moe_permute; MOE_EWORKSPACE when
+ *   moe_permute_workspace_size(T, K, e_local) > MOE_PERMUTE_SCRATCH_BYTES
+ *   (T = 131072 fits with e_local up to 256, T = 2^20 with e_local up to
+ *   32); MOE_EHIP if the address lookup fails.
+ * Every call on one GPU uses that GPU's one array, so calls that overlap on
+ * one GPU (different streams, or host threads without ordering) race and
+ * must not be made.  Each call writes every entry it later reads, so no
+ * clearing is needed between calls.
+ */
+#define MOE_PERMUTE_SCRATCH_BYTES ((size_t)1 << 20)
+int moe_permute_noalloc(const int32_t* topk_idx, int T, int K, int e_begin, int e_local,
+                        const moe_bf16* x, int H, int cap_rows,
+                        int32_t* counts, int32_t* offsets, int32_t* pos, int32_t* src,
+                        moe_bf16* x_perm, int32_t* status, moe_stream stream);
 
 /*
  * Gate-scaled gather of the output gradient into expert-grouped order

@@ -26,6 +26,7 @@ SIGNATURES = {
     "moe_route_backward": ([_p, _p, _p, _i, _i, _i, _p, _p], _i),
     "moe_permute_workspace_size": ([_i, _i, _i], _z),
     "moe_permute": ([_p, _i, _i, _i, _i, _p, _i, _i, _p, _p, _p, _p, _p, _p, _p, _z, _p], _i),
+    "moe_permute_noalloc": ([_p, _i, _i, _i, _i, _p, _i, _i, _p, _p, _p, _p, _p, _p, _p], _i),
     "moe_gather": ([_p, _p, _p, _i, _i, _i, _p, _p], _i),
     "moe_gather_gate_grad": ([_p, _p, _p, _p, _i, _i, _i, _p, _p, _p], _i),
     "moe_grouped_gemm_swiglu": ([_p, _p, _p, _p, _i, _i, _i, _i, _p, _p, _p], _i),
@@ -179,6 +180,34 @@ def moe_permute(topk_idx, e_begin, e_local, x, cap_rows, out=None, ws=None, stre
                               _ptr(status), _ptr(ws), ws.numel(), _stream(stream)))
     return dict(counts=counts[:e_local], offsets=offsets, pos=pos, src=src, x_perm=x_perm,
                 status=status, ws=ws)
+
+
+def moe_permute_noalloc(topk_idx, e_begin, e_local, x, cap_rows, out, stream=None, copy_rows=True):
+    """moe_permute without a workspace: the library's own device array holds the count matrix.  Every
+    output buffer is the caller's (out: counts, offsets, pos, src, status, and x_perm unless
+    copy_rows=False); nothing is allocated here either."""
+    _need(topk_idx, torch.int32, "topk_idx")
+    _need(x, torch.bfloat16, "x")
+    T, K = topk_idx.shape
+    H = x.shape[1]
+    counts, offsets, pos, src, status = (out[k] for k in ("counts", "offsets", "pos", "src", "status"))
+    x_perm = out.get("x_perm") if copy_rows else None
+    if copy_rows and x_perm is None:
+        raise MoeError("moe_permute_noalloc: out['x_perm'] is required with copy_rows=True")
+    for t, name, dt in ((counts, "counts", torch.int32), (offsets, "offsets", torch.int32), (pos, "pos", torch.int32),
+                        (src, "src", torch.int32), (status, "status", torch.int32)):
+        _need(t, dt, name)
+    if counts.numel() < e_local or offsets.numel() < e_local + 1 or src.numel() < cap_rows or status.numel() < 1:
+        raise MoeError("moe_permute_noalloc: counts, offsets, src or status smaller than e_local, e_local+1, "
+                       "cap_rows, 1")
+    _shape(pos, (T, K), "pos")
+    if x_perm is not None:
+        _need(x_perm, torch.bfloat16, "x_perm")
+        _rows(x_perm, cap_rows, H, "x_perm")
+    _check(load().moe_permute_noalloc(_ptr(topk_idx), T, K, e_begin, e_local, _ptr(x), H, cap_rows,
+                                      _ptr(counts), _ptr(offsets), _ptr(pos), _ptr(src), _ptr(x_perm),
+                                      _ptr(status), _stream(stream)))
+    return dict(counts=counts[:e_local], offsets=offsets, pos=pos, src=src, x_perm=x_perm, status=status)
 
 
 def moe_gather(d_out, pos, gates, dy_perm, stream=None):

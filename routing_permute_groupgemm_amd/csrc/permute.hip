@@ -29,6 +29,8 @@
 // With TB = 64 and at most 256 blocks, step 2 runs inside step 3 instead:
 // every rank block reads the whole count matrix (at most 8192 entries) and
 // derives its own first rows, which costs less than the one-block launch.
+#include <mutex>
+
 #include "moe_common.hpp"
 
 namespace moe {
@@ -323,11 +325,12 @@ extern "C" size_t moe_permute_workspace_size(int T, int K, int e_local) {
     return (size_t)((n * 4 + 255) / 256 * 256 + 256);
 }
 
-extern "C" int moe_permute(const int32_t* topk_idx, int T, int K, int e_begin, int e_local,
-                           const moe_bf16* x, int H, int cap_rows, int32_t* counts, int32_t* offsets,
-                           int32_t* pos, int32_t* src, moe_bf16* x_perm, int32_t* status, void* ws,
-                           size_t ws_bytes, moe_stream stream) {
-    using namespace moe;
+namespace moe {
+
+// Host-side argument checks of the permutation (shared by both entry points).
+static int permute_check(const int32_t* topk_idx, int T, int K, int e_begin, int e_local, const moe_bf16* x, int H,
+                         int cap_rows, const int32_t* counts, const int32_t* offsets, const int32_t* pos,
+                         const int32_t* src, const moe_bf16* x_perm, const int32_t* status) {
     using moe_host::misaligned;
     if (T < 0 || K < 1 || K > 16 || e_begin < 0 || e_local < 0 || e_local > kMaxLocal || H < 0 ||
         cap_rows < 0)
@@ -341,17 +344,22 @@ extern "C" int moe_permute(const int32_t* topk_idx, int T, int K, int e_begin, i
     if (cap_rows > 0 && !src) return MOE_EINVAL;
     if (x_perm && T > 0 && cap_rows > 0 && H > 0 && !x) return MOE_EINVAL;
     if (misaligned(topk_idx) || misaligned(x) || misaligned(counts) || misaligned(offsets) ||
-        misaligned(pos) || misaligned(src) || misaligned(x_perm) || misaligned(status) || misaligned(ws))
+        misaligned(pos) || misaligned(src) || misaligned(x_perm) || misaligned(status))
         return MOE_EALIGN;
-    const size_t need = moe_permute_workspace_size(T, K, e_local);
-    if (!ws || ws_bytes < need) return MOE_EWORKSPACE;
-    hipStream_t s = (hipStream_t)stream;
+    return MOE_OK;
+}
+
+// The launches of the permutation, with the per-(expert, block) count matrix
+// in w (every entry of it is written by the count kernel before it is read,
+// so w needs no clearing).
+static int permute_launch(const int32_t* topk_idx, int T, int K, int e_begin, int e_local, const moe_bf16* x, int H,
+                          int cap_rows, int32_t* counts, int32_t* offsets, int32_t* pos, int32_t* src,
+                          moe_bf16* x_perm, int32_t* status, int32_t* w, hipStream_t s) {
     const int tb = perm_tb(T, e_local);
     const int nblk = (T + tb - 1) / tb;
     const int rounds = (tb / 4 * K + 63) / 64;
     int nbits = 0;
     while ((1 << nbits) < e_local) ++nbits;
-    int32_t* w = (int32_t*)ws;
     // few blocks of the small token block: the rank kernel does the scan too
     const bool fused = tb == 64 && nblk > 0 && nblk <= kFusedScanBlocks;
     if (nblk > 0 && e_local > 0)
@@ -375,4 +383,64 @@ extern "C" int moe_permute(const int32_t* topk_idx, int T, int K, int e_begin, i
             perm_copy_kernel<4><<<(T + 3) / 4, 256, 0, s>>>((const u32x4*)x, T, K, H, pos, (u32x4*)x_perm);
     }
     return moe_host::launch_status();
+}
+
+// Scratch of the allocation-free entry point: the count matrix lives in this
+// file-scope device array (one copy per GPU, held until the process ends)
+// instead of a caller's workspace.  Host code never passes the array's name
+// to a kernel (on the host it is a stand-in, not a device address): it uses
+// the address hipGetSymbolAddress returns, fetched once per device.
+constexpr size_t kPermuteScratchBytes = MOE_PERMUTE_SCRATCH_BYTES;
+static __device__ __align__(256) int32_t scratch[kPermuteScratchBytes / 4];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+// The current device's address of `scratch`, looked up on the first call on
+// that device (with it current) and kept.
+static int scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_EHIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_EHIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return MOE_OK;
+}
+
+}  // namespace moe
+
+extern "C" int moe_permute(const int32_t* topk_idx, int T, int K, int e_begin, int e_local,
+                           const moe_bf16* x, int H, int cap_rows, int32_t* counts, int32_t* offsets,
+                           int32_t* pos, int32_t* src, moe_bf16* x_perm, int32_t* status, void* ws,
+                           size_t ws_bytes, moe_stream stream) {
+    using namespace moe;
+    const int rc = permute_check(topk_idx, T, K, e_begin, e_local, x, H, cap_rows, counts, offsets, pos, src,
+                                 x_perm, status);
+    if (rc != MOE_OK) return rc;
+    if (moe_host::misaligned(ws)) return MOE_EALIGN;
+    const size_t need = moe_permute_workspace_size(T, K, e_local);
+    if (!ws || ws_bytes < need) return MOE_EWORKSPACE;
+    return permute_launch(topk_idx, T, K, e_begin, e_local, x, H, cap_rows, counts, offsets, pos, src, x_perm,
+                          status, (int32_t*)ws, (hipStream_t)stream);
+}
+
+extern "C" int moe_permute_noalloc(const int32_t* topk_idx, int T, int K, int e_begin, int e_local,
+                                   const moe_bf16* x, int H, int cap_rows, int32_t* counts, int32_t* offsets,
+                                   int32_t* pos, int32_t* src, moe_bf16* x_perm, int32_t* status,
+                                   moe_stream stream) {
+    using namespace moe;
+    const int rc = permute_check(topk_idx, T, K, e_begin, e_local, x, H, cap_rows, counts, offsets, pos, src,
+                                 x_perm, status);
+    if (rc != MOE_OK) return rc;
+    if (moe_permute_workspace_size(T, K, e_local) > kPermuteScratchBytes) return MOE_EWORKSPACE;
+    void* w = nullptr;
+    const int st = scratch_address(&w);
+    if (st != MOE_OK) return st;
+    return permute_launch(topk_idx, T, K, e_begin, e_local, x, H, cap_rows, counts, offsets, pos, src, x_perm,
+                          status, (int32_t*)w, (hipStream_t)stream);
 }

@@ -217,3 +217,17 @@ def test_probe_rejects():
     assert p(None, 4, 10, FAKE, None) == -1
     assert p(FAKE, 4, 10, None, None) == -1
     assert p(MIS, 4, 10, FAKE, None) == -3
+
+
+def test_permute_noalloc_rejects_on_the_host():
+    # more count matrix than the library's 1 MiB device array holds, and a NULL status word: both are
+    # refused before any device call
+    lib = _lib.load()
+    T, K, e_local = 1 << 20, 2, 64
+    assert lib.moe_permute_workspace_size(T, K, e_local) > (1 << 20)
+    assert lib.moe_permute_noalloc(FAKE, T, K, 0, e_local, FAKE, 64, T * K, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   None) == -4
+    assert lib.moe_permute_noalloc(FAKE, 64, 2, 0, 8, FAKE, 64, 128, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                   None) == -1
+    assert lib.moe_permute_noalloc(MIS, 64, 2, 0, 8, FAKE, 64, 128, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   None) == -3
