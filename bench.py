@@ -37,7 +37,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-GEMM_SRC = os.path.join(ROOT, "routing_permute_groupgemm_amd", "csrc", "gemm.hip")
+GEMM_SRCS = os.path.join(ROOT, "routing_permute_groupgemm_amd", "csrc", "gemm*")
 
 
 def parse():
@@ -117,8 +117,13 @@ def roofline(work, ms):
 
 
 def src_hash():
-    with open(GEMM_SRC, "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()[:16]
+    """Hash of the GroupGEMM sources (kernel header and its translation units)."""
+    import glob
+    h = hashlib.sha256()
+    for path in sorted(glob.glob(GEMM_SRCS)):
+        with open(path, "rb") as fh:
+            h.update(os.path.basename(path).encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel, workload):

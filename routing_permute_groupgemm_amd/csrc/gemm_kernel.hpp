@@ -41,6 +41,8 @@
 // its first operand, so each lane ends with 4 consecutive output columns of
 // one row.  Workgroups are persistent, and block ids are remapped so each XCD
 // (own L2) walks a contiguous run of tiles.
+#pragma once
+
 #include <stdlib.h>
 
 #include <algorithm>
@@ -1092,13 +1094,13 @@ void gg_kernel(GemmParams p) {
 // MOE_GEMM_TILE=256, 192 or 128 pins one configuration (for comparisons).
 enum : int { CFG_AUTO = 0, CFG_BIG = 1, CFG_MID = 2, CFG_SMALL = 3 };
 
-static int env_int(const char* name, int dflt) {
+inline int env_int(const char* name, int dflt) {
     const char* e = getenv(name);
     return e ? atoi(e) : dflt;
 }
 
 // read on every call, so a process can compare configurations
-static int tile_config() {
+inline int tile_config() {
     const int t = env_int("MOE_GEMM_TILE", 0);
     return t == 128 ? CFG_SMALL : t == 192 ? CFG_MID : t == 256 ? CFG_BIG : CFG_AUTO;
 }
@@ -1136,309 +1138,11 @@ static int launch(const GemmParams& p, hipStream_t s) {
     return launch_cfg<256, 256, 32, 2, 2, LB, EPI, SCHED, kLdsBudget, 0, GATHER>(p, s);
 }
 
-}  // namespace moe
-
-using moe_host::misaligned;
-
-extern "C" int moe_grouped_gemm_swiglu(const moe_bf16* x_perm, const moe_bf16* w_gate, const moe_bf16* w_up,
-                                       const int32_t* offsets, int e_local, int H, int F, int cap_rows,
-                                       moe_bf16* h, moe_bf16* ab_save, moe_stream stream) {
-    using namespace moe;
-    if (e_local < 0 || e_local > kMaxGroups || H < 0 || F < 0 || cap_rows < 0) return MOE_EINVAL;
-    if (H % 64 || F % 64) return MOE_ESHAPE;
-    if (!offsets) return MOE_EINVAL;
-    if (e_local == 0 || cap_rows == 0 || F == 0) return MOE_OK;
-    if (!x_perm || !w_gate || !w_up || !h) return MOE_EINVAL;
-    if (misaligned(x_perm) || misaligned(w_gate) || misaligned(w_up) || misaligned(offsets) || misaligned(h) ||
-        misaligned(ab_save))
-        return MOE_EALIGN;
-    // load offsets are 32-bit and those at or past 2^31 mean "out of range":
-    // 256 rows of A, and one expert's whole weight matrix, stay below that
-    if ((int64_t)256 * H * 2 >= (1ll << 31) || (int64_t)H * F * 2 >= (1ll << 31)) return MOE_EINVAL;
-    GemmParams p{};
-    p.a = x_perm;
-    p.lda = H;
-    p.w0 = w_gate;
-    p.w1 = w_up;
-    p.w_stride = (int64_t)H * F;
-    p.ldw = F;
-    p.offsets = offsets;
-    p.e_local = e_local;
-    p.cap = cap_rows;
-    p.N = F;
-    p.Kd = H;
-    p.c = h;
-    p.ldc = F;
-    p.c2 = ab_save;
-    if (H == 0) return MOE_EINVAL;
-    return launch<LAY_MN, EPI_SWIGLU, SCHED_ROWS>(p, (hipStream_t)stream);
-}
-
-extern "C" int moe_grouped_gemm_swiglu_gather(const moe_bf16* x, int T, const int32_t* src, int K,
-                                              const moe_bf16* w_gate, const moe_bf16* w_up, const int32_t* offsets,
-                                              int e_local, int H, int F, int cap_rows, moe_bf16* h,
-                                              moe_bf16* ab_save, moe_stream stream) {
-    using namespace moe;
-    if (e_local < 0 || e_local > kMaxGroups || H <= 0 || F < 0 || cap_rows < 0 || T < 0 || K < 1 || K > 16)
-        return MOE_EINVAL;
-    if (H % 64 || F % 64) return MOE_ESHAPE;
-    // every A load offset (row * H * 2 + column bytes) must stay below the
-    // out-of-range offset that masks rows past an expert's end
-    if ((int64_t)T * H * 2 >= (1ll << 31) || (int64_t)H * F * 2 >= (1ll << 31)) return MOE_EINVAL;
-    if ((int64_t)cap_rows > (int64_t)T * K) return MOE_EINVAL;
-    if (!offsets) return MOE_EINVAL;
-    if (e_local == 0 || cap_rows == 0 || F == 0) return MOE_OK;
-    if (!x || !src || !w_gate || !w_up || !h) return MOE_EINVAL;
-    if (misaligned(x) || misaligned(src) || misaligned(w_gate) || misaligned(w_up) || misaligned(offsets) ||
-        misaligned(h) || misaligned(ab_save))
-        return MOE_EALIGN;
-    GemmParams p{};
-    p.a = x;
-    p.lda = H;
-    p.src = src;
-    p.topk = K;
-    p.topk_rcp = 0xffffffffu / (uint32_t)K;
-    p.a_rows = T;
-    p.w0 = w_gate;
-    p.w1 = w_up;
-    p.w_stride = (int64_t)H * F;
-    p.ldw = F;
-    p.offsets = offsets;
-    p.e_local = e_local;
-    p.cap = cap_rows;
-    p.N = F;
-    p.Kd = H;
-    p.c = h;
-    p.ldc = F;
-    p.c2 = ab_save;
-    return launch<LAY_MN, EPI_SWIGLU, SCHED_ROWS, true>(p, (hipStream_t)stream);
-}
-
-extern "C" int moe_grouped_gemm(const moe_bf16* a, int lda, const moe_bf16* w0, const moe_bf16* w1, int trans_w,
-                                const int32_t* offsets, int e_local, int Kd, int N, int cap_rows, int epilogue,
-                                const moe_bf16* ab, moe_bf16* c, int ldc, moe_stream stream) {
-    using namespace moe;
-    if (e_local < 0 || e_local > kMaxGroups || Kd <= 0 || N < 0 || cap_rows < 0) return MOE_EINVAL;
-    if (trans_w != 0 && trans_w != 1) return MOE_EINVAL;
-    if (epilogue != MOE_EPI_NONE && epilogue != MOE_EPI_SWIGLU_BWD) return MOE_EINVAL;
-    if (Kd % 64 || N % 64) return MOE_ESHAPE;
-    if (w1 && !trans_w) return MOE_EINVAL;
-    const int acols = w1 ? 2 * Kd : Kd;
-    const int ccols = epilogue == MOE_EPI_SWIGLU_BWD ? 2 * N : N;
-    if (lda < acols || ldc < ccols || lda % 8 || ldc % 8) return MOE_EINVAL;
-    if (!offsets) return MOE_EINVAL;
-    if (e_local == 0 || cap_rows == 0 || N == 0) return MOE_OK;
-    if (!a || !w0 || !c || (epilogue == MOE_EPI_SWIGLU_BWD && !ab)) return MOE_EINVAL;
-    if (misaligned(a) || misaligned(w0) || misaligned(w1) || misaligned(offsets) || misaligned(ab) ||
-        misaligned(c))
-        return MOE_EALIGN;
-    // 32-bit load offsets below 2^31 (see moe_grouped_gemm_swiglu)
-    if ((int64_t)256 * lda * 2 >= (1ll << 31) || (int64_t)256 * Kd * 2 >= (1ll << 31) ||
-        (int64_t)Kd * N * 2 >= (1ll << 31))
-        return MOE_EINVAL;
-    GemmParams p{};
-    p.a = a;
-    p.lda = lda;
-    p.w0 = w0;
-    p.w1 = w1;
-    p.w_stride = (int64_t)Kd * N;
-    p.ldw = trans_w ? Kd : N;
-    p.two_seg = w1 != nullptr;
-    p.offsets = offsets;
-    p.e_local = e_local;
-    p.cap = cap_rows;
-    p.N = N;
-    p.Kd = Kd;
-    p.c = c;
-    p.ldc = ldc;
-    p.ab = ab;
-    hipStream_t s = (hipStream_t)stream;
-    if (trans_w) {
-        if (epilogue == MOE_EPI_SWIGLU_BWD) return launch<LAY_KC, EPI_SWIGLU_BWD, SCHED_ROWS>(p, s);
-        return launch<LAY_KC, EPI_BF16, SCHED_ROWS>(p, s);
-    }
-    if (epilogue == MOE_EPI_SWIGLU_BWD) return launch<LAY_MN, EPI_SWIGLU_BWD, SCHED_ROWS>(p, s);
-    return launch<LAY_MN, EPI_BF16, SCHED_ROWS>(p, s);
-}
-
-extern "C" int moe_wgrad(const moe_bf16* a, int lda, const moe_bf16* b, int ldb, const int32_t* offsets,
-                         int e_local, int M, int N, int cap_rows, float* dw, moe_stream stream) {
-    using namespace moe;
-    if (e_local < 0 || e_local > kMaxGroups || M < 0 || N < 0 || cap_rows < 0) return MOE_EINVAL;
-    if (M % 64 || N % 64) return MOE_ESHAPE;
-    if (lda < M || ldb < N || lda % 8 || ldb % 8) return MOE_EINVAL;
-    if (!offsets) return MOE_EINVAL;
-    if (e_local == 0 || M == 0 || N == 0) return MOE_OK;
-    if (!dw || (cap_rows > 0 && (!a || !b))) return MOE_EINVAL;
-    if (misaligned(a) || misaligned(b) || misaligned(offsets) || misaligned(dw)) return MOE_EALIGN;
-    if ((int64_t)64 * lda * 2 >= (1ll << 31) || (int64_t)64 * ldb * 2 >= (1ll << 31)) return MOE_EINVAL;
-    GemmParams p{};
-    p.a = a;
-    p.lda = lda;
-    p.b = b;
-    p.ldb = ldb;
-    p.offsets = offsets;
-    p.e_local = e_local;
-    p.cap = cap_rows;
-    p.M = M;
-    p.N = N;
-    p.cf = dw;
-    return launch<LAY_MN, EPI_F32, SCHED_WGRAD>(p, (hipStream_t)stream);
-}
-
-// ---- router projection -------------------------------------------------------
-// Dense GEMMs on the same kernel: one group of all T rows (no offsets array).
-// Few output tiles (E columns) would leave most of the chip idle, so the
-// contraction is cut into chunks, each leaving an fp32 partial that a second
-// pass adds in chunk order: the result is fixed for a given device, whatever
-// the scheduling.
-
-namespace moe {
-
-// Chunks of a contraction of kt_total steps so that `tiles` output tiles
-// become at most one workgroup per compute unit (a second, partial round of
-// workgroups would double the time), each chunk at least 8 steps.
-static void split_steps(int64_t tiles, int64_t kt_total, int* n_chunks, int* steps) {
-    kt_total = std::max<int64_t>(kt_total, 1);  // no tokens: one (empty) chunk
-    const int64_t cus = moe_host::num_cus();
-    int64_t s = std::min<int64_t>(cus / std::max<int64_t>(tiles, 1), std::max<int64_t>(kt_total / 8, 1));
-    s = std::max<int64_t>(s, 1);
-    const int64_t st = (kt_total + s - 1) / s;
-    *steps = (int)st;
-    *n_chunks = (int)((kt_total + st - 1) / st);
-}
-
-struct RouterPlan {
-    bool fwd_small;               // forward on 128x128 tiles (too few 256x256 tiles to fill the GPU)
-    int fwd_chunks, fwd_steps;    // forward: contraction over H in chunks of fwd_steps * 32
-    int bwd_chunks, bwd_rows;     // weight gradient: token rows in chunks of bwd_rows
-    size_t fwd_bytes, bwd_bytes;  // workspace
-};
-
-static size_t round256(size_t b) { return (b + 255) / 256 * 256; }
-
-static RouterPlan router_plan(int T, int H, int E) {
-    RouterPlan r{};
-    // Few rows: 128x128 tiles, whose smaller fp32 partials cost less to write
-    // and add than the 256x256 tiles' (the partials, not the MFMAs, bound a
-    // forward cut into many chunks).
-    const int64_t big_tiles = (int64_t)((T + 255) / 256) * ((E + 255) / 256);
-    r.fwd_small = big_tiles < moe_host::num_cus();
-    const int tm = r.fwd_small ? 128 : 256;
-    split_steps((int64_t)((T + tm - 1) / tm) * ((E + tm - 1) / tm), H / 32, &r.fwd_chunks, &r.fwd_steps);
-    int steps;
-    split_steps((int64_t)((H + 255) / 256) * ((E + 255) / 256), (T + 31) / 32, &r.bwd_chunks, &steps);
-    r.bwd_rows = steps * 32;
-    r.bwd_chunks = std::max(1, (T + r.bwd_rows - 1) / r.bwd_rows);
-    r.fwd_bytes = r.fwd_chunks > 1 ? (size_t)r.fwd_chunks * T * E * 4 : 0;
-    r.bwd_bytes = round256((size_t)T * E * 2) + (r.bwd_chunks > 1 ? (size_t)r.bwd_chunks * H * E * 4 : 0);
-    return r;
-}
-
-static int router_check(int T, int H, int E) {
-    if (T < 0 || H <= 0 || E <= 0 || E > 4096) return MOE_EINVAL;
-    if (H % 64 || E % 64) return MOE_ESHAPE;
-    // every buffer descriptor spans at most 256 rows of x or all of W_r
-    if ((int64_t)T * E >= (1ll << 31) || (int64_t)T * H >= (1ll << 40) || (int64_t)256 * H * 2 >= (1ll << 31) ||
-        (int64_t)H * E * 2 >= (1ll << 31))
-        return MOE_EINVAL;
-    return MOE_OK;
-}
+// Launchers of the instantiations, each compiled in one translation unit
+// (gemm_rows.hip, gemm_dgrad.hip, gemm_wgrad.hip), so that no kernel is
+// instantiated twice in the library.
+int launch_rows_mn(const GemmParams& p, int epi, hipStream_t s);  // B [Kd][N]; EPI_BF16 or EPI_SWIGLU_BWD
+int launch_rows_kc(const GemmParams& p, int epi, hipStream_t s);  // B [N][Kd]; EPI_BF16 or EPI_SWIGLU_BWD
+int launch_wgrad(const GemmParams& p, hipStream_t s);             // SCHED_WGRAD, fp32 out
 
 }  // namespace moe
-
-extern "C" size_t moe_router_workspace_size(int T, int H, int E) {
-    using namespace moe;
-    if (router_check(T, H, E) != MOE_OK) return 0;
-    const RouterPlan r = router_plan(T, H, E);
-    return std::max(r.fwd_bytes, r.bwd_bytes) + 256;
-}
-
-extern "C" int moe_router_logits(const moe_bf16* x, int T, int H, const moe_bf16* w_r, int E, const float* bias,
-                                 float* logits, void* ws, size_t ws_bytes, moe_stream stream) {
-    using namespace moe;
-    const int st = router_check(T, H, E);
-    if (st != MOE_OK) return st;
-    if (T == 0) return MOE_OK;
-    if (!x || !w_r || !logits) return MOE_EINVAL;
-    if (misaligned(x) || misaligned(w_r) || misaligned(bias) || misaligned(logits) || misaligned(ws))
-        return MOE_EALIGN;
-    const RouterPlan r = router_plan(T, H, E);
-    if (r.fwd_bytes && (!ws || ws_bytes < r.fwd_bytes)) return MOE_EWORKSPACE;
-    const bool split = r.fwd_chunks > 1;
-    GemmParams p{};
-    p.a = x;
-    p.lda = H;
-    p.w0 = w_r;
-    p.ldw = E;
-    p.dense_rows = T;
-    p.row_chunk = T;
-    p.e_local = 1;
-    p.cap = T;
-    p.N = E;
-    p.Kd = H;
-    p.cf = split ? (float*)ws : logits;
-    p.ldc = E;
-    p.ksplit = r.fwd_chunks;
-    p.kchunk = r.fwd_steps * 32;
-    p.part_stride = (int64_t)T * E;
-    p.bias = split ? nullptr : bias;
-    hipStream_t s = (hipStream_t)stream;
-    int rc = r.fwd_small ? launch_cfg<128, 128, 32, 2, 2, LAY_MN, EPI_F32, SCHED_ROWS, kLdsBudget>(p, s)
-                         : launch<LAY_MN, EPI_F32, SCHED_ROWS>(p, s);
-    if (rc != MOE_OK || !split) return rc;
-    return moe_host::sum_partials((const float*)ws, r.fwd_chunks, (int64_t)T * E, (int64_t)T * E, bias, E, logits, s);
-}
-
-extern "C" int moe_router_backward(const moe_bf16* x, int T, int H, const moe_bf16* w_r, int E, const float* dlogits,
-                                   moe_bf16* dx, float* dw_r, void* ws, size_t ws_bytes, moe_stream stream) {
-    using namespace moe;
-    const int st = router_check(T, H, E);
-    if (st != MOE_OK) return st;
-    if (!w_r || !dw_r || (T > 0 && (!x || !dlogits || !dx))) return MOE_EINVAL;
-    if (misaligned(x) || misaligned(w_r) || misaligned(dlogits) || misaligned(dx) || misaligned(dw_r) ||
-        misaligned(ws))
-        return MOE_EALIGN;
-    const RouterPlan r = router_plan(T, H, E);
-    if (!ws || ws_bytes < r.bwd_bytes) return MOE_EWORKSPACE;
-    hipStream_t s = (hipStream_t)stream;
-    uint16_t* dl16 = (uint16_t*)ws;
-    float* part = (float*)((char*)ws + round256((size_t)T * E * 2));
-    int rc = moe_host::cast_f32_bf16(dlogits, (int64_t)T * E, dl16, s);
-    if (rc != MOE_OK) return rc;
-    // dx = bf16(dlogits) . W_r^T: W_r [H][E] is the [N][Kd] weight, contraction contiguous
-    GemmParams p{};
-    p.a = dl16;
-    p.lda = E;
-    p.w0 = w_r;
-    p.ldw = E;
-    p.dense_rows = T;
-    p.row_chunk = T;
-    p.e_local = 1;
-    p.cap = T;
-    p.N = H;
-    p.Kd = E;
-    p.c = dx;
-    p.ldc = H;
-    if (T > 0) {
-        rc = launch<LAY_KC, EPI_BF16, SCHED_ROWS>(p, s);
-        if (rc != MOE_OK) return rc;
-    }
-    // dW_r = x^T . bf16(dlogits): the token rows in chunks, one fp32 partial each
-    const bool split = r.bwd_chunks > 1;
-    GemmParams q{};
-    q.a = x;
-    q.lda = H;
-    q.b = dl16;
-    q.ldb = E;
-    q.dense_rows = T;
-    q.row_chunk = r.bwd_rows;
-    q.e_local = r.bwd_chunks;
-    q.cap = T;
-    q.M = H;
-    q.N = E;
-    q.cf = split ? part : dw_r;
-    rc = launch<LAY_MN, EPI_F32, SCHED_WGRAD>(q, s);
-    if (rc != MOE_OK || !split) return rc;
-    return moe_host::sum_partials(part, r.bwd_chunks, (int64_t)H * E, (int64_t)H * E, nullptr, E, dw_r, s);
-}
