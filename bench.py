@@ -65,6 +65,9 @@ def parse():
                          "rows x depth x width, as a vendor-library reference on this GPU")
     ap.add_argument("--copy-rows", action="store_true",
                     help="forward-only workloads: permute with the row copy instead of zero-copy dispatch")
+    ap.add_argument("--no-nb", action="store_true",
+                    help="skip timing the non-bitwise (two row chunks per expert) weight gradient beside the "
+                         "bitwise one on workloads with a backward")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration under rocprofv3)")
     return ap.parse_args()
@@ -355,6 +358,46 @@ def time_steps(steps, stream, n_steps, warmup):
     return dict(per=per, dom=steps[dom_i][0], dom_ms=dom_ms, ms_per_step=ms_per_step, one_step=one_step)
 
 
+def time_wgrad_modes(shape, buf, reps=5):
+    """The three weight-gradient GroupGEMMs of one step in the bitwise mode (one fixed-order pass over each
+    expert's rows) and in the non-bitwise mode with two row chunks per expert (fp32 partials added in chunk
+    order), each timed with HIP events over `reps` repetitions on the launch stream: UniEP's Table 7
+    comparison.  Returns ms per step of the three calls in each mode."""
+    import torch
+    from routing_permute_groupgemm_amd import _lib
+    H, F, EL, cap = shape.H, shape.F, shape.EL, buf.cap
+    ws = torch.empty(max(_lib.moe_wgrad_split_workspace_size(EL, H, F, 2),
+                         _lib.moe_wgrad_split_workspace_size(EL, F, H, 2)), dtype=torch.uint8, device="cuda")
+
+    def bw():
+        _lib.moe_wgrad(buf.x_perm, H, buf.dab, 2 * F, buf.offsets, EL, H, F, cap, dw=buf.dw_gate)
+        _lib.moe_wgrad(buf.x_perm, H, buf.dab, 2 * F, buf.offsets, EL, H, F, cap, dw=buf.dw_up, b_col0=F)
+        _lib.moe_wgrad(buf.h, F, buf.dy_perm, H, buf.offsets, EL, F, H, cap, dw=buf.dw_down)
+
+    def nb():
+        _lib.moe_wgrad_split(buf.x_perm, H, buf.dab, 2 * F, buf.offsets, EL, H, F, cap, 2, dw=buf.dw_gate, ws=ws)
+        _lib.moe_wgrad_split(buf.x_perm, H, buf.dab, 2 * F, buf.offsets, EL, H, F, cap, 2, dw=buf.dw_up, ws=ws,
+                             b_col0=F)
+        _lib.moe_wgrad_split(buf.h, F, buf.dy_perm, H, buf.offsets, EL, F, H, cap, 2, dw=buf.dw_down, ws=ws)
+
+    stream = torch.cuda.current_stream()
+    out = {}
+    for name, fn in (("bw", bw), ("nb", nb), ("bw_again", bw)):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out[name] = e0.elapsed_time(e1) / reps
+    del ws
+    bw_ms = (out["bw"] + out["bw_again"]) / 2
+    return dict(bw_ms=round(bw_ms, 4), nb_ms=round(out["nb"], 4), nb_splits=2,
+                nb_vs_bw=round(out["nb"] / bw_ms, 4), reps=reps)
+
+
 def routing_stats(buf):
     offsets = buf.offsets.cpu().numpy()
     counts = np.diff(offsets)
@@ -411,6 +454,9 @@ def run_workload(name, args, n_steps, warmup, log):
     )
     if rs["status"] != 0:
         summ["warning"] = "row capacity overflow: rows were dropped"
+    if shape.backward and not args.no_nb:
+        log(f"{shape.name}: weight gradient, bitwise vs non-bitwise")
+        summ["wgrad_bw_vs_nb"] = time_wgrad_modes(shape, buf)
     state = dict(shape=shape, inp=inp, dev=dev, buf=buf, steps=steps, t=t, work=work, rs=rs, zero_copy=zero_copy,
                  stream=stream)
     return summ, state
@@ -500,6 +546,8 @@ def main():
         "hbm_frac": summ["hbm_frac"],
         "step_ms": summ["step_ms"],
     }
+    if "wgrad_bw_vs_nb" in summ:
+        result["wgrad_bw_vs_nb"] = summ["wgrad_bw_vs_nb"]
     if graph_ms is not None:
         result["graph_ms_per_step"] = round(graph_ms, 4)
     if args.dense_reference:

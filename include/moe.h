@@ -281,6 +281,28 @@ int moe_wgrad(const moe_bf16* a, int lda, const moe_bf16* b, int ldb,
               float* dw, moe_stream stream);
 
 /*
+ * The non-bitwise variant of moe_wgrad (UniEP evaluation, "Performance Cost
+ * of Bitwise Reproducibility" and Table 7: splitting the weight gradient's
+ * reduction over tokens gives more parallel work but changes the summation
+ * tree).  Each expert's rows are cut into `splits` fixed chunks (every chunk
+ * but the last a whole number of 32-row steps); each chunk is summed as in
+ * moe_wgrad into an fp32 partial in ws, and the partials are added in chunk
+ * order:
+ *   dw[j] = sum over chunks c ascending of (a_jc^T . b_jc)
+ * Identical bits from run to run, within the fp32 rounding of moe_wgrad, but
+ * not the same bits.  splits == 1 is moe_wgrad itself (ws unused).
+ *   Arguments as moe_wgrad, plus splits (1 <= splits, e_local*splits <= 512)
+ *   and ws: device workspace of at least
+ *   moe_wgrad_split_workspace_size(e_local, M, N, splits) bytes
+ *   (e_local*splits fp32 [M,N] partials and the chunk offsets).
+ * Errors as moe_wgrad; MOE_EWORKSPACE if ws is NULL or too small.
+ */
+size_t moe_wgrad_split_workspace_size(int e_local, int M, int N, int splits);
+int moe_wgrad_split(const moe_bf16* a, int lda, const moe_bf16* b, int ldb,
+                    const int32_t* offsets, int e_local, int M, int N, int cap_rows,
+                    int splits, float* dw, void* ws, size_t ws_bytes, moe_stream stream);
+
+/*
  * Router projection (UniEP "MoE workflow": the router network produces each
  * token's scores over the experts, from which routing takes the top-k):
  *   logits[t,e] = sum_i x[t,i] * w_r[i,e]  (+ bias[e])      fp32 accumulate

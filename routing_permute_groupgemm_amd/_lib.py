@@ -34,6 +34,8 @@ SIGNATURES = {
     "moe_grouped_gemm": ([_p, _i, _p, _p, _i, _p, _i, _i, _i, _i, _i, _p, _p, _i, _p], _i),
     "moe_combine": ([_p, _p, _p, _i, _i, _i, _p, _p], _i),
     "moe_wgrad": ([_p, _i, _p, _i, _p, _i, _i, _i, _i, _p, _p], _i),
+    "moe_wgrad_split_workspace_size": ([_i, _i, _i, _i], _z),
+    "moe_wgrad_split": ([_p, _i, _p, _i, _p, _i, _i, _i, _i, _i, _p, _p, _z, _p], _i),
     "moe_router_workspace_size": ([_i, _i, _i], _z),
     "moe_router_logits": ([_p, _i, _i, _p, _i, _p, _p, _p, _z, _p], _i),
     "moe_router_backward": ([_p, _i, _i, _p, _i, _p, _p, _p, _p, _z, _p], _i),
@@ -365,6 +367,36 @@ def moe_wgrad(a, lda, b, ldb, offsets, e_local, M, N, cap_rows, dw=None, a_col0=
     pb = b.data_ptr() + 2 * b_col0
     _check(load().moe_wgrad(pa, lda, pb, ldb, _ptr(offsets), e_local, M, N, cap_rows, _ptr(dw),
                             _stream(stream)))
+    return dw
+
+
+def moe_wgrad_split_workspace_size(e_local, M, N, splits) -> int:
+    return int(load().moe_wgrad_split_workspace_size(e_local, M, N, splits))
+
+
+def moe_wgrad_split(a, lda, b, ldb, offsets, e_local, M, N, cap_rows, splits, dw=None, ws=None, a_col0=0,
+                    b_col0=0, stream=None):
+    """moe_wgrad with each expert's rows in `splits` fixed chunks whose fp32 partials are added in chunk
+    order (ws: device workspace, allocated here if not given or too small)."""
+    _need(a, torch.bfloat16, "a")
+    _need(b, torch.bfloat16, "b")
+    _need(offsets, torch.int32, "offsets")
+    if dw is None:
+        dw = torch.empty((e_local, M, N), dtype=torch.float32, device=a.device)
+    _need(dw, torch.float32, "dw")
+    _shape(dw, (e_local, M, N), "dw")
+    if offsets.numel() < e_local + 1:
+        raise MoeError(f"offsets: expected {e_local + 1} entries, got {offsets.numel()}")
+    for t, ld, c0, w, name in ((a, lda, a_col0, M, "a"), (b, ldb, b_col0, N, "b")):
+        if cap_rows > 0 and t.numel() < (cap_rows - 1) * ld + c0 + w:
+            raise MoeError(f"{name}: too small for {cap_rows} rows at stride {ld} from column {c0}")
+    need = moe_wgrad_split_workspace_size(e_local, M, N, splits)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=a.device)
+    pa = a.data_ptr() + 2 * a_col0
+    pb = b.data_ptr() + 2 * b_col0
+    _check(load().moe_wgrad_split(pa, lda, pb, ldb, _ptr(offsets), e_local, M, N, cap_rows, splits, _ptr(dw),
+                                  _ptr(ws), ws.numel(), _stream(stream)))
     return dw
 
 

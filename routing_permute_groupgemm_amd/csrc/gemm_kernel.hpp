@@ -535,7 +535,23 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
     // into LDS slot `slot`.  With live == false (no tile left) it loads from
     // the out-of-range offset: zeros, no memory traffic, and the same number
     // of loads per stage, so the vmcnt bookkeeping stays fixed.
-    auto load_one = [&](int kt, int slot, int u, bool live) {
+    // Weight gradient: the buffer descriptors of one stage (its BK rows of A
+    // and of B, cut at the group's last row, so rows past it load zeros),
+    // built once per stage rather than once per load.
+    struct StageSrd {
+        i32x4 a, b;
+    };
+    auto stage_srd = [&](int kt) {
+        StageSrd r{};
+        if constexpr (SCHED == SCHED_WGRAD) {
+            const int k0 = kt * BK;
+            const uint32_t rows = (uint32_t)max(0, min(BK, ic.valid - k0));
+            r.a = make_srd((const uint16_t*)c_rowA + (int64_t)k0 * p.lda, rows * (uint32_t)(p.lda * 2));
+            r.b = make_srd((const uint16_t*)c_rowB + (int64_t)k0 * p.ldb, rows * (uint32_t)(p.ldb * 2));
+        }
+        return r;
+    };
+    auto load_one = [&](int kt, int slot, int u, bool live, const StageSrd& ss) {
         const uint32_t sA = lds_addr(smem) + slot * TL::kStage;
         const uint32_t sB = sA + TL::kABytes;
         const int k0 = kt * BK;
@@ -575,20 +591,16 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
                     }
                     lds_load16(c_srdA, sA + q * 1024, live ? voff : kOOB);
                 } else {
-                    const i32x4 r = make_srd((const uint16_t*)c_rowA + (int64_t)k0 * p.lda,
-                                             (uint32_t)(max(0, min(BK, ic.valid - k0)) * p.lda * 2));
                     const int col = ic.mi_w * BM + mn_sub(u) * 64;
                     const uint32_t voff = col < p.M ? la0 + (uint32_t)((mn_kr(u) * 8 * p.lda + col) * 2) : kOOB;
-                    lds_load16(r, sA + q * 1024, live ? voff : kOOB);
+                    lds_load16(ss.a, sA + q * 1024, live ? voff : kOOB);
                 }
             } else {
                 const int q = (u - LA) * TL::kWaves + wave;
                 if (SCHED == SCHED_WGRAD) {
-                    const i32x4 r = make_srd((const uint16_t*)c_rowB + (int64_t)k0 * p.ldb,
-                                             (uint32_t)(max(0, min(BK, ic.valid - k0)) * p.ldb * 2));
                     const int col = ic.ni * BN + mn_sub(u - LA) * 64;
                     const uint32_t voff = col < p.N ? lb0 + (uint32_t)((mn_kr(u - LA) * 8 * p.ldb + col) * 2) : kOOB;
-                    lds_load16(r, sB + q * 1024, live ? voff : kOOB);
+                    lds_load16(ss.b, sB + q * 1024, live ? voff : kOOB);
                 } else if (LB == LAY_MN) {
                     // weight [Kd][ldw], N contiguous: [BK][64] sub-tiles
                     const int sub = mn_sub(u - LA);
@@ -619,8 +631,9 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
         }
     };
     auto issue = [&](int kt, int slot, bool live) {
+        const StageSrd ss = stage_srd(kt);
 #pragma unroll
-        for (int u = 0; u < LPW; ++u) load_one(kt, slot, u, live);
+        for (int u = 0; u < LPW; ++u) load_one(kt, slot, u, live, ss);
     };
 
     f32x16 acc[MTW][NTW];
@@ -678,6 +691,7 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
         constexpr int kMfma = NB * NTW;
         const bool live = itile < n_tiles_total;
         const int kn = ik;  // the issue cursor's stage, loaded into the slot of gs-1
+        const StageSrd ss = stage_srd(kn);
         const int nslot = (int)((gs + S - 1) % S);
         const int slot = (int)(gs % S), slot1 = (int)((gs + 1) % S);
 #pragma unroll
@@ -695,7 +709,7 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
                 const int lo = kk * LPW / KK, n = (kk + 1) * LPW / KK - lo;
 #pragma unroll
                 for (int i = 0; i < LPW; ++i)
-                    if (i < n && i * NB / n == mt) load_one(kn, nslot, lo + i, live);
+                    if (i < n && i * NB / n == mt) load_one(kn, nslot, lo + i, live, ss);
             }
             // each MFMA followed by its share of the LDS reads (at most one
             // per MFMA when there are more MFMAs than reads)
@@ -753,6 +767,7 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
             for (int kt = 0; kt < KT; ++kt, ++gs) {
                 const bool live = itile < n_tiles_total;
                 const int kn = ik;  // the issue cursor's stage, loaded into the slot of gs-1
+                const StageSrd ss = stage_srd(kn);
                 const int nslot = (int)((gs + S - 1) % S);
                 const int slot = (int)(gs % S), slot1 = (int)((gs + 1) % S);
 #pragma unroll
@@ -770,7 +785,7 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
                         const int lo = kk * LPW / KK, n = (kk + 1) * LPW / KK - lo;
 #pragma unroll
                         for (int i = 0; i < LPW; ++i)
-                            if (i < n && i * MTW / n == mt) load_one(kn, nslot, lo + i, live);
+                            if (i < n && i * MTW / n == mt) load_one(kn, nslot, lo + i, live, ss);
                     }
                     constexpr int kPer = (kReads + kMfma - 1) / kMfma;
 #pragma unroll

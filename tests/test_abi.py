@@ -231,3 +231,15 @@ def test_permute_noalloc_rejects_on_the_host():
                                    None) == -1
     assert lib.moe_permute_noalloc(MIS, 64, 2, 0, 8, FAKE, 64, 128, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                    None) == -3
+
+
+def test_wgrad_split_rejects_on_the_host():
+    lib = _lib.load()
+    assert lib.moe_wgrad_split_workspace_size(8, 128, 128, 1) == 0
+    assert lib.moe_wgrad_split_workspace_size(8, 128, 128, 2) >= 16 * 128 * 128 * 4
+    assert lib.moe_wgrad_split_workspace_size(300, 128, 128, 2) == 0  # more than 512 chunk groups
+    # splits < 1, too many chunk groups, no workspace, a misaligned workspace
+    assert lib.moe_wgrad_split(FAKE, 128, FAKE, 128, FAKE, 8, 128, 128, 64, 0, FAKE, FAKE, 1 << 30, None) == -1
+    assert lib.moe_wgrad_split(FAKE, 128, FAKE, 128, FAKE, 300, 128, 128, 64, 2, FAKE, FAKE, 1 << 30, None) == -1
+    assert lib.moe_wgrad_split(FAKE, 128, FAKE, 128, FAKE, 8, 128, 128, 64, 2, FAKE, None, 0, None) == -4
+    assert lib.moe_wgrad_split(FAKE, 128, FAKE, 128, FAKE, 8, 128, 128, 64, 2, FAKE, MIS, 1 << 30, None) == -3

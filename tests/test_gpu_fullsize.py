@@ -212,6 +212,31 @@ def test_wgrad_sampled(case, which):
         assert_close(f"dw[{j}]", got[j][:, cols], ref[j][:, cols])
 
 
+def test_wgrad_split_sampled(case):
+    """The non-bitwise weight gradient (two row chunks per expert) at full size: sampled experts and
+    columns against the oracle's serial sum, and a bitwise rerun."""
+    c = case
+    _bwd_only(c)
+    s = c.shape
+    M, N, lda, ldb = s.H, s.F, s.H, 2 * s.F
+    A = synth.operand_bf16((s.cap, s.H), seed=0, tag=6)
+    B = synth.operand_bf16((s.cap, 2 * s.F), seed=0, tag=7, std=0.1)
+    d = pipeline.to_device(dict(A=A, B=B))
+    ws = torch.empty(_lib.moe_wgrad_split_workspace_size(s.EL, M, N, 2), dtype=torch.uint8, device="cuda")
+    dw = _lib.moe_wgrad_split(d["A"], lda, d["B"], ldb, c.buf.offsets, s.EL, M, N, s.cap, 2, ws=ws)
+    dw2 = _lib.moe_wgrad_split(d["A"], lda, d["B"], ldb, c.buf.offsets, s.EL, M, N, s.cap, 2, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(dw.view(torch.int32), dw2.view(torch.int32)), "split wgrad rerun differs"
+    counts = c.ref_pm["counts"]
+    groups = np.unique([int(np.argmax(counts)), int(np.argmin(counts)), 1]).astype(np.int32)
+    cols = np.unique(np.concatenate([[0, N - 1], c.rng.integers(0, N, 10)])).astype(np.int32)
+    ref = np.zeros((s.EL, M, N), np.float32)
+    oracle.wgrad(A, lda, B, ldb, c.ref_pm["offsets"], M, N, s.cap, groups=groups, cols=cols, out=ref)
+    got = dw.cpu().numpy()
+    for j in groups:
+        assert_close(f"dw[{j}]", got[j][:, cols], ref[j][:, cols])
+
+
 def test_gate_grad_and_route_backward_full(case):
     """Router backward at full size: dgates for every token from the same seeded d_out and y on both
     sides, the fused kernel's dy_perm equal to moe_gather's, and dlogits for every token from the same
