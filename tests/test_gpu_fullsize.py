@@ -50,7 +50,11 @@ def case(request):
     torch.cuda.empty_cache()
 
 
-def sample_rows(c, n_random=24):
+def sample_rows(c, n_random=24, whole_tiles=False):
+    """Rows at the ends and middle of the first, last, largest and smallest experts plus random rows;
+    with whole_tiles, also every row of two whole 256-row GEMM tiles: the largest expert's first tile
+    and the last expert's last (ragged) tile, so that every lane, MFMA row block and epilogue row of
+    those tiles is compared element by element."""
     off = c.ref_pm["offsets"]
     counts = np.diff(off)
     nz = np.nonzero(counts)[0]
@@ -61,6 +65,13 @@ def sample_rows(c, n_random=24):
         if lo < hi:
             rows |= {lo, hi - 1, (lo + hi) // 2}
     rows |= set(c.rng.integers(0, c.R, n_random).tolist())
+    if whole_tiles:
+        j = nz[np.argmax(counts[nz])]
+        lo, hi = int(off[j]), int(min(off[j + 1], c.shape.cap))
+        rows |= set(range(lo, min(hi, lo + 256)))
+        j = nz[-1]
+        lo, hi = int(off[j]), int(min(off[j + 1], c.shape.cap))
+        rows |= set(range(lo + (hi - lo - 1) // 256 * 256, hi))
     return np.array(sorted(r for r in rows if r < c.R), np.int64)
 
 
@@ -86,7 +97,7 @@ def test_permute_full(case):
 
 def test_expert_up_sampled_rows(case):
     c = case
-    rows = sample_rows(c)
+    rows = sample_rows(c, whole_tiles=True)
     h, ab = oracle.expert_up(c.ref_pm["x_perm"], c.inp["w_gate"], c.inp["w_up"], c.ref_pm["offsets"],
                              c.shape.cap, rows=rows, want_ab=True)
     assert_close("h", bits(c.buf.h)[rows], h[rows])
@@ -118,7 +129,7 @@ def test_expert_down_sampled_rows(case):
     y = torch.empty((s.cap, s.H), dtype=torch.bfloat16, device="cuda")
     _lib.moe_grouped_gemm(dh, c.dev["w_down"], None, 0, c.buf.offsets, s.F, s.H, s.cap, y)
     torch.cuda.synchronize()
-    rows = sample_rows(c)
+    rows = sample_rows(c, whole_tiles=True)
     ref = oracle.expert_down(hin, c.inp["w_down"], c.ref_pm["offsets"], s.cap, rows=rows)
     assert_close("y", bits(y)[rows], ref[rows])
 
@@ -165,7 +176,7 @@ def test_dgrad_down_swiglu_sampled_rows(case):
     _lib.moe_grouped_gemm(d["dy"], c.dev["w_down"], None, 1, c.buf.offsets, s.H, s.F, s.cap, dab,
                           epilogue=_lib.MOE_EPI_SWIGLU_BWD, ab=d["ab"])
     torch.cuda.synchronize()
-    rows = sample_rows(c)
+    rows = sample_rows(c, whole_tiles=True)
     ref = oracle.bwd_down(dy, c.inp["w_down"], ab, c.ref_pm["offsets"], s.cap, rows=rows)
     assert_close("dab", bits(dab)[rows], ref[rows])
 
@@ -179,7 +190,7 @@ def test_dgrad_up_sampled_rows(case):
     dx = torch.empty((s.cap, s.H), dtype=torch.bfloat16, device="cuda")
     _lib.moe_grouped_gemm(d["dab"], c.dev["w_gate"], c.dev["w_up"], 1, c.buf.offsets, s.F, s.H, s.cap, dx)
     torch.cuda.synchronize()
-    rows = sample_rows(c)
+    rows = sample_rows(c, whole_tiles=True)
     ref = oracle.bwd_up(dabin, c.inp["w_gate"], c.inp["w_up"], c.ref_pm["offsets"], s.cap, rows=rows)
     assert_close("dx_perm", bits(dx)[rows], ref[rows])
 

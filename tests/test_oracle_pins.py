@@ -255,6 +255,50 @@ def test_row_subset_matches_full():
     assert np.array_equal(hs[rows], h[rows]) and np.array_equal(abs_[rows], ab[rows])
 
 
+def test_subset_modes_match_full_results():
+    """Every oracle mode that fills only some rows, tokens or groups (used at full size, where the full
+    result is out of reach) writes exactly what the full call writes there, and zeros elsewhere: a
+    subset path that indexed outputs by position in the subset rather than by the true row, token or
+    group would fail."""
+    inp, fwd, bwd, cap = _small_layer()
+    offsets = fwd["offsets"]
+    R = int(offsets[-1])
+    rows = np.array([0, 1, R // 3, R // 2, R - 1], np.int64)
+    others = np.setdiff1d(np.arange(cap), rows)
+    # expert_down, bwd_down, bwd_up on a row subset
+    y_s = oracle.expert_down(fwd["h"], inp["w_down"], offsets, cap, rows=rows)
+    dab_s = oracle.bwd_down(bwd["dy_perm"], inp["w_down"], fwd["ab"], offsets, cap, rows=rows)
+    dxp_s = oracle.bwd_up(bwd["dab"], inp["w_gate"], inp["w_up"], offsets, cap, rows=rows)
+    for name, sub, full in (("y", y_s, fwd["y"]), ("dab", dab_s, bwd["dab"]), ("dx_perm", dxp_s, bwd["dx_perm"])):
+        assert np.array_equal(sub[rows], full[rows]), name
+        assert not sub[others].any(), name
+    # combine on a token subset (gated forward and the ungated combine-gradient)
+    T = fwd["pos"].shape[0]
+    toks = np.array([0, 3, T // 2, T - 1], np.int64)
+    rest = np.setdiff1d(np.arange(T), toks)
+    out_s = oracle.combine(fwd["y"], fwd["pos"], fwd["gates"], tokens=toks)
+    dx_s = oracle.combine(bwd["dx_perm"], fwd["pos"], None, tokens=toks)
+    for name, sub, full in (("out", out_s, fwd["out"]), ("dx", dx_s, bwd["dx"])):
+        assert np.array_equal(sub[toks], full[toks]), name
+        assert not sub[rest].any(), name
+    # wgrad on a group subset, also with a column subset
+    H = inp["w_gate"].shape[1]
+    F = inp["w_gate"].shape[2]
+    EL = len(offsets) - 1
+    groups = np.array([EL - 1, 0], np.int32)
+    g_s = oracle.wgrad(fwd["x_perm"], H, bwd["dab"], 2 * F, offsets, H, F, cap, groups=groups)
+    for j in range(EL):
+        if j in groups:
+            assert np.array_equal(g_s[j].view(np.uint32), bwd["dw_gate"][j].view(np.uint32)), j
+        else:
+            assert not g_s[j].any(), j
+    cols = np.array([F - 1, 2], np.int32)
+    gc = oracle.wgrad(fwd["x_perm"], H, bwd["dab"], 2 * F, offsets, H, F, cap, groups=groups, cols=cols)
+    for j in groups:
+        assert np.array_equal(gc[j][:, cols].view(np.uint32), bwd["dw_gate"][j][:, cols].view(np.uint32))
+        assert not np.delete(gc[j], cols, axis=1).any()
+
+
 # ---------------------------------------------------------------- combine
 
 def test_combine_identity_expert_k1_is_bit_exact():
