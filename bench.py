@@ -103,6 +103,8 @@ def algorithmic_work(shape, R, T_act, n_active, zero_copy=False, router=False):
         w["bwd_combine"] = dict(bytes=2 * H * R + 4 * T * K + 2 * H * T, flops=0)
         for name, (m, n) in (("wgrad_gate", (H, F)), ("wgrad_up", (H, F)), ("wgrad_down", (F, H))):
             w[name] = dict(bytes=2 * R * m + 2 * R * n + 4 * EL * m * n, flops=2 * R * m * n)
+        # dW_gate and dW_up in one pass over x_perm and [da | db]
+        w["wgrad_gate_up"] = dict(bytes=2 * R * H + 2 * R * 2 * F + 4 * EL * H * 2 * F, flops=2 * R * H * 2 * F)
     return w
 
 
@@ -245,8 +247,7 @@ def measured_mfma_tflops(stream, target_ms=20.0):
 # (depth, width) of each GroupGEMM step as one dense product over all routed rows
 def dense_dims(name, shape):
     H, F = shape.H, shape.F
-    return {"expert_up": (H, 2 * F), "expert_down": (F, H), "bwd_down_dgrad": (H, F), "bwd_up_dgrad": (2 * F, H),
-            "wgrad_gate": None, "wgrad_up": None, "wgrad_down": None}.get(name)
+    return {"expert_up": (H, 2 * F), "expert_down": (F, H), "bwd_down_dgrad": (H, F), "bwd_up_dgrad": (2 * F, H)}.get(name)
 
 
 def dense_reference(M, Kd, N, steps):
@@ -270,7 +271,8 @@ def dense_reference(M, Kd, N, steps):
                 frac=round(tf / MFMA_BF16_PEAK_TFS, 4))
 
 
-GEMM_STEPS = ("expert_up", "expert_down", "bwd_down_dgrad", "bwd_up_dgrad", "wgrad_gate", "wgrad_up", "wgrad_down")
+GEMM_STEPS = ("expert_up", "expert_down", "bwd_down_dgrad", "bwd_up_dgrad", "wgrad_gate_up", "wgrad_gate", "wgrad_up",
+              "wgrad_down")
 HBM_STEPS = ("route", "permute", "combine", "bwd_gather", "route_bwd", "bwd_combine")
 
 
@@ -304,10 +306,8 @@ def layer_steps(shape, dev, buf, router):
             ("bwd_up_dgrad", lambda: _lib.moe_grouped_gemm(buf.dab, dev["w_gate"], dev["w_up"], 1, buf.offsets, F,
                                                            H, cap, buf.dx_perm)),
             ("bwd_combine", lambda: _lib.moe_combine(buf.dx_perm, buf.pos, None, out=buf.dx)),
-            ("wgrad_gate", lambda: _lib.moe_wgrad(buf.x_perm, H, buf.dab, 2 * F, buf.offsets, EL, H, F, cap,
-                                                  dw=buf.dw_gate)),
-            ("wgrad_up", lambda: _lib.moe_wgrad(buf.x_perm, H, buf.dab, 2 * F, buf.offsets, EL, H, F, cap,
-                                                dw=buf.dw_up, b_col0=F)),
+            ("wgrad_gate_up", lambda: _lib.moe_wgrad_gate_up(buf.x_perm, buf.dab, buf.offsets, EL, cap,
+                                                             dw_gate=buf.dw_gate, dw_up=buf.dw_up)),
             ("wgrad_down", lambda: _lib.moe_wgrad(buf.h, F, buf.dy_perm, H, buf.offsets, EL, F, H, cap,
                                                   dw=buf.dw_down)),
         ]

@@ -281,6 +281,21 @@ int moe_wgrad(const moe_bf16* a, int lda, const moe_bf16* b, int ldb,
               float* dw, moe_stream stream);
 
 /*
+ * dW_gate and dW_up in one transposed GroupGEMM (UniEP "MoE workflow",
+ * backward: the weight gradients reduce over the token dimension): both
+ * contract the same rows of x_perm, against the two halves of dab, so one pass
+ * over [da | db] reads x_perm once instead of twice.  For expert j:
+ *   dw_gate[j] = x_perm_j^T . dab_j[:, 0:F],  dw_up[j] = x_perm_j^T . dab_j[:, F:2F]
+ * bitwise equal to moe_wgrad(x_perm, H, dab, 2F, ..., M=H, N=F) and to the
+ * same call on dab + F (the same fixed order per output element).
+ *   x_perm bf16 [cap_rows,H];  dab bf16 [cap_rows,2F];  offsets as moe_wgrad;
+ *   dw_gate, dw_up fp32 [e_local,H,F] out.  H, F multiples of 64.
+ */
+int moe_wgrad_gate_up(const moe_bf16* x_perm, int H, const moe_bf16* dab, int F,
+                      const int32_t* offsets, int e_local, int cap_rows,
+                      float* dw_gate, float* dw_up, moe_stream stream);
+
+/*
  * The non-bitwise variant of moe_wgrad (UniEP evaluation, "Performance Cost
  * of Bitwise Reproducibility" and Table 7: splitting the weight gradient's
  * reduction over tokens gives more parallel work but changes the summation

@@ -34,6 +34,7 @@ SIGNATURES = {
     "moe_grouped_gemm": ([_p, _i, _p, _p, _i, _p, _i, _i, _i, _i, _i, _p, _p, _i, _p], _i),
     "moe_combine": ([_p, _p, _p, _i, _i, _i, _p, _p], _i),
     "moe_wgrad": ([_p, _i, _p, _i, _p, _i, _i, _i, _i, _p, _p], _i),
+    "moe_wgrad_gate_up": ([_p, _i, _p, _i, _p, _i, _i, _p, _p, _p], _i),
     "moe_wgrad_split_workspace_size": ([_i, _i, _i, _i], _z),
     "moe_wgrad_split": ([_p, _i, _p, _i, _p, _i, _i, _i, _i, _i, _p, _p, _z, _p], _i),
     "moe_router_workspace_size": ([_i, _i, _i], _z),
@@ -368,6 +369,31 @@ def moe_wgrad(a, lda, b, ldb, offsets, e_local, M, N, cap_rows, dw=None, a_col0=
     _check(load().moe_wgrad(pa, lda, pb, ldb, _ptr(offsets), e_local, M, N, cap_rows, _ptr(dw),
                             _stream(stream)))
     return dw
+
+
+def moe_wgrad_gate_up(x_perm, dab, offsets, e_local, cap_rows, dw_gate=None, dw_up=None, stream=None):
+    """(dw_gate, dw_up) = x_perm_j^T . [da_j | db_j] per expert, in one pass over x_perm."""
+    _need(x_perm, torch.bfloat16, "x_perm")
+    _need(dab, torch.bfloat16, "dab")
+    _need(offsets, torch.int32, "offsets")
+    H = x_perm.shape[1]
+    F = dab.shape[1] // 2
+    if dab.dim() != 2 or dab.shape[1] != 2 * F:
+        raise MoeError(f"dab: expected [rows, 2F], got {tuple(dab.shape)}")
+    _rows(x_perm, cap_rows, H, "x_perm")
+    _rows(dab, cap_rows, 2 * F, "dab")
+    if offsets.numel() < e_local + 1:
+        raise MoeError(f"offsets: expected {e_local + 1} entries, got {offsets.numel()}")
+    out = []
+    for t, name in ((dw_gate, "dw_gate"), (dw_up, "dw_up")):
+        if t is None:
+            t = torch.empty((e_local, H, F), dtype=torch.float32, device=x_perm.device)
+        _need(t, torch.float32, name)
+        _shape(t, (e_local, H, F), name)
+        out.append(t)
+    _check(load().moe_wgrad_gate_up(_ptr(x_perm), H, _ptr(dab), F, _ptr(offsets), e_local, cap_rows, _ptr(out[0]),
+                                    _ptr(out[1]), _stream(stream)))
+    return out[0], out[1]
 
 
 def moe_wgrad_split_workspace_size(e_local, M, N, splits) -> int:

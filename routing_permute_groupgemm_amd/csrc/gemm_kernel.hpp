@@ -81,7 +81,9 @@ struct GemmParams {
     int64_t ldc;
     uint16_t* c2;         // SWIGLU: ab_save [rows, 2F]
     const uint16_t* ab;   // SWIGLU_BWD: saved [a | b], row stride 2N
-    float* cf;            // WGRAD: fp32 out [e_local, M, N]
+    float* cf;            // WGRAD: fp32 out [e_local, M, n_split]: the columns n < n_split
+    float* cf2;           // WGRAD: the columns n >= n_split, out [e_local, M, N - n_split] (NULL: n_split = N)
+    int n_split;
     const int32_t* src;   // ROWS gather: row r of the tile reads a[src[r] / topk]
     int topk;
     uint32_t topk_rcp;    // floor((2^32 - 1) / topk): src / topk without a divide
@@ -881,7 +883,14 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
                         } else if (SCHED == SCHED_WGRAD) {
                             const int m = mi_w * BM + mloc;
                             const int n = ni * BN + wn * (BN / WN) + 32 * np + 4 * c;
-                            if (m < p.M && n < p.N) *(u32x4*)(p.cf + ((int64_t)j * p.M + m) * p.N + n) = v;
+                            if (m < p.M && n < p.N) {
+                                // a plain store: L2 merges the pieces of a row into whole
+                                // lines (a non-temporal store doubled the HBM write traffic)
+                                const bool second = n >= p.n_split;
+                                float* base = second ? p.cf2 : p.cf;
+                                const int nn = second ? n - p.n_split : n;
+                                *(u32x4*)(base + ((int64_t)j * p.M + m) * p.n_split + nn) = v;
+                            }
                         } else {
                             // row-tiled fp32 output: one partial per contraction chunk
                             const int n = ni * BN + wn * (BN / WN) + 32 * np + 4 * c;
@@ -905,26 +914,6 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
 #pragma unroll
         for (int mt = 0; mt < MTW; ++mt) {
             const int mloc = row_base(mt) + (lane & 31);
-            if (SCHED == SCHED_WGRAD) {
-                const int m = mi_w * BM + mloc;
-                if (m >= p.M) continue;
-                float* orow = p.cf + ((int64_t)j * p.M + m) * p.N;
-#pragma unroll
-                for (int nt = 0; nt < NTW; ++nt)
-#pragma unroll
-                    for (int j4 = 0; j4 < 4; ++j4) {
-                        const int n = ni * BN + col_of(nt) + 8 * j4 + cq;
-                        if (n < p.N) {
-                            f32x4 v = {acc[mt][nt][4 * j4], acc[mt][nt][4 * j4 + 1], acc[mt][nt][4 * j4 + 2],
-                                       acc[mt][nt][4 * j4 + 3]};
-                            // a plain store: L2 merges the 32-byte pieces of a row
-                            // into whole lines (a non-temporal store doubled the
-                            // HBM write traffic)
-                            *(f32x4*)(orow + n) = v;
-                        }
-                    }
-                continue;
-            }
             if (mloc >= valid) continue;
             const int64_t row = row0 + mloc;
             if (EPI == EPI_SWIGLU) {

@@ -149,6 +149,7 @@ extern "C" int moe_router_backward(const moe_bf16* x, int T, int H, const moe_bf
     q.M = H;
     q.N = E;
     q.cf = split ? part : dw_r;
+    q.n_split = E;
     rc = launch_wgrad(q, s);
     if (rc != MOE_OK || !split) return rc;
     return moe_host::sum_partials(part, r.bwd_chunks, (int64_t)H * E, (int64_t)H * E, nullptr, E, dw_r, s);

@@ -71,6 +71,35 @@ extern "C" int moe_wgrad(const moe_bf16* a, int lda, const moe_bf16* b, int ldb,
     p.M = M;
     p.N = N;
     p.cf = dw;
+    p.n_split = N;
+    return launch_wgrad(p, (hipStream_t)stream);
+}
+
+extern "C" int moe_wgrad_gate_up(const moe_bf16* x_perm, int H, const moe_bf16* dab, int F, const int32_t* offsets,
+                                 int e_local, int cap_rows, float* dw_gate, float* dw_up, moe_stream stream) {
+    using namespace moe;
+    if (e_local < 0 || e_local > kMaxGroups || H < 0 || F < 0 || cap_rows < 0) return MOE_EINVAL;
+    if (H % 64 || F % 64) return MOE_ESHAPE;
+    if (!offsets) return MOE_EINVAL;
+    if (e_local == 0 || H == 0 || F == 0) return MOE_OK;
+    if (!dw_gate || !dw_up || (cap_rows > 0 && (!x_perm || !dab))) return MOE_EINVAL;
+    if (misaligned(x_perm) || misaligned(dab) || misaligned(offsets) || misaligned(dw_gate) || misaligned(dw_up))
+        return MOE_EALIGN;
+    if ((int64_t)64 * H * 2 >= (1ll << 31) || (int64_t)64 * 2 * F * 2 >= (1ll << 31)) return MOE_EINVAL;
+    // one transposed GroupGEMM over [da | db]: output columns n < F are dW_gate, the rest dW_up
+    GemmParams p{};
+    p.a = x_perm;
+    p.lda = H;
+    p.b = dab;
+    p.ldb = 2 * F;
+    p.offsets = offsets;
+    p.e_local = e_local;
+    p.cap = cap_rows;
+    p.M = H;
+    p.N = 2 * F;
+    p.cf = dw_gate;
+    p.cf2 = dw_up;
+    p.n_split = F;
     return launch_wgrad(p, (hipStream_t)stream);
 }
 
@@ -115,6 +144,7 @@ extern "C" int moe_wgrad_split(const moe_bf16* a, int lda, const moe_bf16* b, in
     p.M = M;
     p.N = N;
     p.cf = part;
+    p.n_split = N;
     rc = launch_wgrad(p, s);
     if (rc != MOE_OK) return rc;
     const int64_t mn4 = (int64_t)M * N / 4;

@@ -123,8 +123,7 @@ def backward(buf: MoeBuffers, inp: dict):
                           epilogue=_lib.MOE_EPI_SWIGLU_BWD, ab=buf.ab)
     _lib.moe_grouped_gemm(buf.dab, inp["w_gate"], inp["w_up"], 1, buf.offsets, F, H, cap, buf.dx_perm)
     _lib.moe_combine(buf.dx_perm, buf.pos, None, out=buf.dx)
-    _lib.moe_wgrad(buf.x_perm, H, buf.dab, 2 * F, buf.offsets, EL, H, F, cap, dw=buf.dw_gate)
-    _lib.moe_wgrad(buf.x_perm, H, buf.dab, 2 * F, buf.offsets, EL, H, F, cap, dw=buf.dw_up, b_col0=F)
+    _lib.moe_wgrad_gate_up(buf.x_perm, buf.dab, buf.offsets, EL, cap, dw_gate=buf.dw_gate, dw_up=buf.dw_up)
     _lib.moe_wgrad(buf.h, F, buf.dy_perm, H, buf.offsets, EL, F, H, cap, dw=buf.dw_down)
     return buf.dx
 

@@ -243,3 +243,12 @@ def test_wgrad_split_rejects_on_the_host():
     assert lib.moe_wgrad_split(FAKE, 128, FAKE, 128, FAKE, 300, 128, 128, 64, 2, FAKE, FAKE, 1 << 30, None) == -1
     assert lib.moe_wgrad_split(FAKE, 128, FAKE, 128, FAKE, 8, 128, 128, 64, 2, FAKE, None, 0, None) == -4
     assert lib.moe_wgrad_split(FAKE, 128, FAKE, 128, FAKE, 8, 128, 128, 64, 2, FAKE, MIS, 1 << 30, None) == -3
+
+
+def test_wgrad_gate_up_rejects_on_the_host():
+    lib = _lib.load()
+    assert lib.moe_wgrad_gate_up(FAKE, 100, FAKE, 64, FAKE, 4, 64, FAKE, FAKE, None) == -2   # H % 64
+    assert lib.moe_wgrad_gate_up(FAKE, 128, FAKE, 64, FAKE, 4, 64, FAKE, None, None) == -1   # no dw_up
+    assert lib.moe_wgrad_gate_up(FAKE, 128, FAKE, 64, None, 4, 64, FAKE, FAKE, None) == -1   # no offsets
+    assert lib.moe_wgrad_gate_up(FAKE, 128, FAKE, 64, FAKE, 4, 64, FAKE, MIS, None) == -3
+    assert lib.moe_wgrad_gate_up(FAKE, 128, FAKE, 64, FAKE, 600, 64, FAKE, FAKE, None) == -1  # e_local > 512

@@ -1,8 +1,10 @@
-"""The non-bitwise weight gradient (moe_wgrad_split: each expert's rows in
-fixed chunks whose fp32 partials are added in chunk order) against the oracle
+"""The weight-gradient entry points beside moe_wgrad.  The non-bitwise weight
+gradient (moe_wgrad_split: each expert's rows in fixed chunks whose fp32
+partials are added in chunk order) against the oracle
 element by element, its run-to-run determinism, and its chunk semantics:
 it equals, bit for bit, moe_wgrad over the refined row groups followed by
-fp32 adds in chunk order.  Every call goes through the C ABI."""
+fp32 adds in chunk order.  The paired dW_gate/dW_up pass (moe_wgrad_gate_up)
+against two moe_wgrad calls, bit for bit.  Every call goes through the C ABI."""
 import numpy as np
 import pytest
 import torch
@@ -79,3 +81,26 @@ def test_split_one_is_the_bitwise_path():
     want = _lib.moe_wgrad(dev["a"], M, dev["b"], N, dev["offsets"], EL, M, N, R)
     torch.cuda.synchronize()
     assert torch.equal(got.view(torch.int32), want.view(torch.int32))
+
+
+@pytest.mark.parametrize("H,F", [(192, 64), (128, 192), (320, 128)])
+def test_gate_up_pair_is_two_bitwise_wgrads(H, F):
+    """dW_gate and dW_up from one pass over [da | db] equal the two separate weight gradients bit for bit
+    (same fixed order per output element), including the empty experts' zeros; and the oracle within
+    tolerance."""
+    print(f"[wgrad_gate_up] H={H} F={F}", flush=True)
+    a, dab, offsets, R = operands(H, 2 * F, seed=H + F)
+    dev = pipeline.to_device(dict(a=a, dab=dab, offsets=offsets))
+    EL = len(COUNTS)
+    g0 = torch.full((EL, H, F), float("nan"), dtype=torch.float32, device="cuda")
+    u0 = torch.full_like(g0, float("nan"))
+    g, u = _lib.moe_wgrad_gate_up(dev["a"], dev["dab"], dev["offsets"], EL, R, dw_gate=g0, dw_up=u0)
+    wg = _lib.moe_wgrad(dev["a"], H, dev["dab"], 2 * F, dev["offsets"], EL, H, F, R)
+    wu = _lib.moe_wgrad(dev["a"], H, dev["dab"], 2 * F, dev["offsets"], EL, H, F, R, b_col0=F)
+    torch.cuda.synchronize()
+    assert torch.equal(g.view(torch.int32), wg.view(torch.int32)), "dW_gate differs from moe_wgrad"
+    assert torch.equal(u.view(torch.int32), wu.view(torch.int32)), "dW_up differs from moe_wgrad"
+    ref_g = oracle.wgrad(a, H, dab, 2 * F, offsets, H, F, R)
+    ref_u = oracle.wgrad(a, H, np.ascontiguousarray(dab[:, F:]), F, offsets, H, F, R)
+    assert_close("dw_gate", g.cpu().numpy(), ref_g)
+    assert_close("dw_up", u.cpu().numpy(), ref_u)
