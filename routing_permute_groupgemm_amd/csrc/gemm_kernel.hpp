@@ -56,6 +56,9 @@ constexpr int kGroupM = 4;  // row-tiled GEMMs: m-tiles per group of the tile or
 constexpr int kGroupN = 4;  // weight gradient: n-tiles per group of the tile order
 constexpr int kMaxGroups = 512;
 constexpr int kLdsBudget = 128 * 1024;  // LDS per workgroup for the stage ring
+#ifndef MOE_GEMM_MFMA16
+#define MOE_GEMM_MFMA16 1  // the down dgrad's 256 x 256 body computes with 16x16x32 MFMAs (0: 32x32x16)
+#endif
 
 enum : int { LAY_KC = 0, LAY_MN = 1 };
 enum : int { EPI_BF16 = 0, EPI_SWIGLU = 1, EPI_SWIGLU_BWD = 2, EPI_F32 = 3 };
@@ -202,6 +205,31 @@ struct Lay {
         u32x4 v = {l2[0], l2[1], h2[0], h2[1]};
         return __builtin_bit_cast(bf16x8, v);
     }
+    // Fragments of v_mfma_f32_16x16x32_bf16 (one 32-deep step per stage, BK = 32):
+    // lane holds row rb + l%16 and k values 8*(l/16) + 0..7
+    __device__ static __forceinline__ bf16x8 frag_kc16(const uint8_t* tile, int rb, int lane) {
+        static_assert(BK == 32, "one 32-deep MFMA step per stage");
+        const int row = rb + (lane & 15);
+        const int ch = (lane >> 4) ^ swz_kc(row);
+        u32x4 v = *(const MOE_LDS u32x4*)(tile + row * kRowBytes + (ch << 4));
+        return __builtin_bit_cast(bf16x8, v);
+    }
+    // lane holds column cb + l%16 (cb a multiple of 16) and k values 8*(l/16) + 0..7:
+    // each group of 16 lanes reads a 4 k-row x 16 column patch twice (k-rows
+    // 8g..8g+3, then 8g+4..8g+7) and the transposing read gives lane q column q
+    __device__ static __forceinline__ bf16x8 frag_mn16(const uint8_t* tile, int cb, int lane) {
+        static_assert(BK == 32, "one 32-deep MFMA step per stage");
+        const int g = lane >> 4, q = lane & 15;
+        const int krow = 8 * g + (q >> 2);
+        const int col = (cb & 63) + 4 * (q & 3);
+        const uint8_t* sub = tile + (cb >> 6) * kSubBytes;
+        const int off = ((col >> 3) ^ swz_mn(krow)) * 16 + (col & 7) * 2;
+        s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS s16x4*)(sub + krow * 128 + off));
+        s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS s16x4*)(sub + (krow + 4) * 128 + off));
+        u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        u32x4 v = {l2[0], l2[1], h2[0], h2[1]};
+        return __builtin_bit_cast(bf16x8, v);
+    }
     // per-lane byte offset of an LDS-direct load into a KC tile: load q fills
     // rows q*kRowsPerLoad + l/kChunks; `v` is q's part of the swizzle period
     __device__ static __forceinline__ uint32_t lane_kc(int lane, int v, int64_t ld) {
@@ -264,6 +292,22 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
     constexpr int MTW = TL::kMTW, NTW = TL::kNTW, LPW = TL::kLoadsPerWave, S = TL::kStages, KK = TL::kKK;
     constexpr int LA = TL::kALoads / TL::kWaves;  // A loads per wave and stage
     static_assert(!GATHER || (SCHED == SCHED_ROWS && EPI == EPI_SWIGLU), "gathered A rows: gate/up GEMM only");
+    // The 256 x 256 body of the down dgrad (SwiGLU-backward epilogue) computes
+    // with v_mfma_f32_16x16x32_bf16: its 128 x 128 wave tile is 8 x 8 blocks of
+    // 16 x 16, one 32-deep MFMA step per stage.  Each lane then holds 4
+    // consecutive output columns of 16 rows, so the epilogue's loads of the
+    // saved (a, b) pairs and its stores of (da, db) cover 32 bytes of a row per
+    // group of 4 lanes instead of 16, and this GEMM ran 5-8% faster (A/B on one
+    // box: 3.55 against 3.75 ms for T = 131072, H = 7168; 0.64 against 0.69 ms
+    // for T = 16384, H = 2048).  The other GEMMs ran as fast or faster with
+    // 32x32x16, although back-to-back 16x16x32 MFMAs on random operands reach
+    // 14% more flops on this chip: their time is set by the loads, not the
+    // MFMA rate.  The smaller bodies keep 32x32x16, whose 32-row blocks their
+    // idle-row scheme is built on.
+    constexpr bool kMf16 = MOE_GEMM_MFMA16 && EPI == EPI_SWIGLU_BWD && BM == 256 && BN == 256 && WM == 2 &&
+                           WN == 2 && BK == 32;
+    constexpr int MB16 = kMf16 ? BM / WM / 16 : 1;  // 16-row blocks per wave
+    constexpr int NB16 = kMf16 ? BN / WN / 16 : 1;  // 16-column blocks per wave
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
@@ -741,6 +785,141 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
     for (int tile = tile0; tile < n_tiles_total; tile += G) {
         const TileDesc cd = decode(tile);
         const int j = cd.j, row0 = cd.row0, valid = cd.valid, ni = cd.ni, mi_w = cd.mi_w, KT = cd.KT, ks = cd.ks;
+
+        if constexpr (kMf16) {
+            // ---- the 256 x 256 body on 16x16x32 MFMAs ----
+            f32x4 acc16[MB16][NB16];
+#pragma unroll
+            for (int a = 0; a < MB16; ++a)
+#pragma unroll
+                for (int b = 0; b < NB16; ++b) acc16[a][b] = f32x4{};
+            // first row / column (within the tile) of the wave's 16-row block m and
+            // 16-column block n
+            auto row16 = [&](int m) { return wm * (BM / WM) + 16 * m; };
+            auto col16 = [&](int n) { return wn * (BN / WN) + 16 * n; };
+            auto frag_a = [&](int slot, int m) { return LY::frag_kc16(smem + slot * TL::kStage, row16(m), lane); };
+            auto frag_b = [&](int slot, int n) {
+                const uint8_t* sB = smem + slot * TL::kStage + TL::kABytes;
+                return LB == LAY_KC ? LY::frag_kc16(sB, col16(n), lane) : LY::frag_mn16(sB, col16(n), lane);
+            };
+            // Each stage runs in two column halves: rows 0..MB16-1 against B blocks
+            // 0..NB16/2-1, then against the other half.  All A fragments of the stage
+            // stay in registers; the B fragments of the second half are read early in
+            // the first half (from this stage's slot), and in the second half each A
+            // fragment is read again for the next stage right after its last use, and
+            // the next stage's first-half B fragments early on.  Every fragment is
+            // thus read at least 4 rows of MFMAs before its first use,
+            // with as many fragment registers as the 32x32x16 bodies (16 of 4).  The
+            // next stage's fragments come from its slot, published by the barrier
+            // that ended the stage before.
+            constexpr int NH = NB16 / 2;
+            bf16x8 a16[MB16], b16[NB16];
+            if (KT > 0) {
+                const int slot = (int)(gs % S);
+#pragma unroll
+                for (int m = 0; m < MB16; ++m) a16[m] = frag_a(slot, m);
+#pragma unroll
+                for (int n = 0; n < NH; ++n) b16[n] = frag_b(slot, n);
+            }
+            for (int kt = 0; kt < KT; ++kt, ++gs) {
+                const bool live = itile < n_tiles_total;
+                const int kn = ik;  // the issue cursor's stage, loaded into the slot of gs-1
+                const StageSrd ss = stage_srd(kn);
+                const int nslot = (int)((gs + S - 1) % S);
+                const int slot = (int)(gs % S), slot1 = (int)((gs + 1) % S);
+                // first half: this stage's second-half B fragments are read along the way
+#pragma unroll
+                for (int m = 0; m < MB16; ++m) {
+#pragma unroll
+                    for (int n = 0; n < NH; ++n)
+                        acc16[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b16[n], a16[m], acc16[m][n], 0, 0, 0);
+                    if (m < NH) b16[NH + m] = frag_b(slot, NH + m);
+#pragma unroll
+                    for (int i = 0; i < LPW; ++i)
+                        if (i * 2 * MB16 / LPW == m) load_one(kn, nslot, i, live, ss);
+                }
+                // the halves stay apart: mixed, some first-half MFMAs would wait for the
+                // second half's B fragments, read moments before
+                __builtin_amdgcn_sched_barrier(0);
+                // second half: the next stage's A fragments, and its first-half B ones
+#pragma unroll
+                for (int m = 0; m < MB16; ++m) {
+#pragma unroll
+                    for (int n = NH; n < NB16; ++n)
+                        acc16[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b16[n], a16[m], acc16[m][n], 0, 0, 0);
+                    a16[m] = frag_a(slot1, m);
+                    if (m < NH) b16[m] = frag_b(slot1, m);
+#pragma unroll
+                    for (int i = 0; i < LPW; ++i)
+                        if (i * 2 * MB16 / LPW == MB16 + m) load_one(kn, nslot, i, live, ss);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                advance();
+                if (GATHER && pf_issued) {
+                    pf_issued = false;
+                    wait_vmcnt<kWaitLoads + LA>();
+                } else {
+                    wait_vmcnt<kWaitLoads>();
+                }
+                __syncthreads();
+            }
+
+            // ---- epilogue: lane holds row l%16 and columns 4*(l/16) + 0..3 of each 16 x 16 block ----
+            static_assert(EPI == EPI_SWIGLU_BWD && SCHED == SCHED_ROWS, "16x16x32 body: the down dgrad only");
+            {  // the accumulators are dh
+                const int cq = 4 * (lane >> 4);
+#pragma unroll
+                for (int mp = 0; mp < MB16 / 2; ++mp) {
+                    // two 16-row blocks at a time: their saved (a, b) pairs are all
+                    // loaded before any of their results is stored
+                    u32x2 aw[2][NB16], bw[2][NB16];
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2) {
+                        const int mloc = row16(2 * mp + h2) + (lane & 15);
+                        const int64_t row = row0 + mloc;
+#pragma unroll
+                        for (int nb = 0; nb < NB16; ++nb) {
+                            const int n = ni * BN + col16(nb) + cq;
+                            aw[h2][nb] = bw[h2][nb] = u32x2{0u, 0u};
+                            if (mloc < valid && n < p.N) {
+                                aw[h2][nb] = *(const u32x2*)(p.ab + row * 2 * p.N + n);
+                                bw[h2][nb] = *(const u32x2*)(p.ab + row * 2 * p.N + p.N + n);
+                            }
+                        }
+                    }
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                        for (int nb = 0; nb < NB16; ++nb) asm volatile("" ::"v"(aw[h2][nb]), "v"(bw[h2][nb]));
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2) {
+                        const int mloc = row16(2 * mp + h2) + (lane & 15);
+                        if (mloc >= valid) continue;
+                        const int64_t row = row0 + mloc;
+#pragma unroll
+                        for (int nb = 0; nb < NB16; ++nb) {
+                            const int n = ni * BN + col16(nb) + cq;
+                            if (n >= p.N) continue;
+                            float da[4], db[4];
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const float v = acc16[2 * mp + h2][nb][i];
+                                float a = (i & 1) ? bf_hi(aw[h2][nb][i >> 1]) : bf_lo(aw[h2][nb][i >> 1]);
+                                float b = (i & 1) ? bf_hi(bw[h2][nb][i >> 1]) : bf_lo(bw[h2][nb][i >> 1]);
+                                float sg = sigmoid_f(a);
+                                da[i] = v * b * sg * (1.0f + a * (1.0f - sg));
+                                db[i] = v * a * sg;
+                            }
+                            u32x2 dw = {pack_bf2(da[0], da[1]), pack_bf2(da[2], da[3])};
+                            u32x2 ew = {pack_bf2(db[0], db[1]), pack_bf2(db[2], db[3])};
+                            *(u32x2*)(p.c + row * p.ldc + n) = dw;
+                            *(u32x2*)(p.c + row * p.ldc + p.N + n) = ew;
+                        }
+                    }
+                }
+            }
+            continue;
+        }
 #pragma unroll
         for (int a = 0; a < MTW; ++a)
 #pragma unroll

@@ -270,8 +270,8 @@ EDGE_COUNTS = [1, 31, 32, 33, 63, 64, 65, 95, 96, 97, 127, 128, 129, 159, 160, 1
 
 @pytest.mark.parametrize("tile", ["0", "256", "192", "128"])
 def test_gemms_at_row_block_edges(tile, monkeypatch):
-    """Gate/up (copy and zero-copy) and down GroupGEMMs on experts whose row counts sit at every
-    row-block and tile edge, element by element against the oracle, in each tile configuration
+    """Gate/up (copy and zero-copy), down and down-dgrad GroupGEMMs on experts whose row counts sit at
+    every row-block and tile edge, element by element against the oracle, in each tile configuration
     (0: the automatic choice)."""
     monkeypatch.setenv("MOE_GEMM_TILE", tile)
     counts = np.array(EDGE_COUNTS, np.int32)
@@ -292,7 +292,22 @@ def test_gemms_at_row_block_edges(tile, monkeypatch):
     _lib.moe_grouped_gemm_swiglu_gather(dev["x"], dev["src"], K, dev["wg"], dev["wu"], dev["off"], R, h=hz)
     y = torch.empty((R, H), dtype=torch.bfloat16, device="cuda")
     _lib.moe_grouped_gemm(dev["h"], dev["wd"], None, 0, dev["off"], F, H, R, y)
+    # down dgrad with the SwiGLU-backward epilogue: W_down read transposed ([N][Kd], the layer's
+    # backward) and, through the same entry point, a weight stored [Kd][N]
+    dy = synth.operand_bf16((R, H), seed=31, tag=6, std=0.125)
+    abin = synth.operand_bf16((R, 2 * F), seed=31, tag=7)
+    wdT = np.ascontiguousarray(np.transpose(wd, (0, 2, 1)))
+    d2 = pipeline.to_device(dict(dy=dy, ab=abin, wdT=wdT))
+    dab = torch.empty((R, 2 * F), dtype=torch.bfloat16, device="cuda")
+    dab2 = torch.empty_like(dab)
+    _lib.moe_grouped_gemm(d2["dy"], dev["wd"], None, 1, dev["off"], H, F, R, dab, epilogue=_lib.MOE_EPI_SWIGLU_BWD,
+                          ab=d2["ab"])
+    _lib.moe_grouped_gemm(d2["dy"], d2["wdT"], None, 0, dev["off"], H, F, R, dab2,
+                          epilogue=_lib.MOE_EPI_SWIGLU_BWD, ab=d2["ab"])
     torch.cuda.synchronize()
+    ref_dab = oracle.bwd_down(dy, wd, abin, offsets, R)
+    assert_close("dab (W_down transposed)", bits(dab), ref_dab)
+    assert_close("dab (weight [Kd][N])", bits(dab2), ref_dab)
     ref_h, ref_ab = oracle.expert_up(x_perm, wg, wu, offsets, R, want_ab=True)
     assert_close("h", bits(h), ref_h)
     assert_close("ab_save", bits(ab), ref_ab)
