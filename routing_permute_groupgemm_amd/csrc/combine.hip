@@ -82,12 +82,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ 
     float g[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-        // the same in every lane: keep them in scalar registers
+        // the same in every lane: read from lane k into scalar registers
         const int k = m ? __builtin_ctzll(m) : 0;
-        rows[r] = __builtin_amdgcn_readfirstlane(__shfl(my_pos, k, 64));
-        g[r] = GATED ? __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
-                           __builtin_bit_cast(int, __shfl(my_g, k, 64))))
-                     : 1.0f;
+        rows[r] = __builtin_amdgcn_readlane(my_pos, k);
+        g[r] = GATED ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_g), k)) : 1.0f;
         m &= m - 1;
     }
     const int nv = H >> 3;
@@ -182,12 +180,10 @@ __global__ __launch_bounds__(256) void gather_kernel(const u32x4* __restrict__ d
     float g[16], dot[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-        // the same in every lane: keep them in scalar registers
+        // the same in every lane: read from lane k into scalar registers
         const int k = m ? __builtin_ctzll(m) : 0;
-        rows[r] = __builtin_amdgcn_readfirstlane(__shfl(my_pos, k, 64));
-        g[r] = GATED ? __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
-                           __builtin_bit_cast(int, __shfl(my_g, k, 64))))
-                     : 1.0f;
+        rows[r] = __builtin_amdgcn_readlane(my_pos, k);
+        g[r] = GATED ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_g), k)) : 1.0f;
         dot[r] = 0.0f;
         m &= m - 1;
     }

@@ -300,7 +300,7 @@ __global__ __launch_bounds__(256) void perm_copy_kernel(const u32x4* __restrict_
             if (v < nv) buf[u] = __builtin_nontemporal_load(xr + v);
         }
         for (int k = 0; k < K; ++k) {
-            int r = __shfl(my_pos, k, 64);
+            const int r = __builtin_amdgcn_readlane(my_pos, k);  // uniform: lane k's destination row
             if (r < 0) continue;
             u32x4* dst = x_perm + (int64_t)r * nv;
 #pragma unroll

@@ -115,8 +115,12 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
 // Router backward: one wave per token.  The gates are the softmax of the
 // chosen scores, so with g, dg the token's gates and gate gradients the
 // score gradient is g_k * (dg_k - sum_j g_j dg_j) at the chosen experts and 0
-// elsewhere.  The sum runs over j ascending; each lane then writes its
-// experts lane, lane + 64, ... so the row is written once, coalesced.
+// elsewhere.  The sum runs over j ascending.  The K chosen experts and their
+// values are wave-uniform: lane k holds choice k, and readlane copies them
+// into scalar registers once.  Each lane then writes its experts lane,
+// lane + 64, ..., selecting its value among the K choices, so the row is
+// written once, coalesced.
+template <int KMAX>
 __global__ __launch_bounds__(256) void route_backward_kernel(const int32_t* __restrict__ topk_idx,
                                                              const float* __restrict__ gates,
                                                              const float* __restrict__ dgates, int T, int E, int K,
@@ -128,19 +132,29 @@ __global__ __launch_bounds__(256) void route_backward_kernel(const int32_t* __re
     const float my_g = lane < K ? gates[t * K + lane] : 0.0f;
     const float my_dg = lane < K ? dgates[t * K + lane] : 0.0f;
     float sum = 0.0f;
-    for (int j = 0; j < K; ++j) sum += __shfl(my_g, j, 64) * __shfl(my_dg, j, 64);
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+        if (j < K) {
+            const float gj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_g), j));
+            const float dgj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_dg), j));
+            sum += gj * dgj;
+        }
+    }
     const float my_val = my_g * (my_dg - sum);
+    int ik[KMAX];
+    float vk[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        ik[k] = k < K ? __builtin_amdgcn_readlane(my_idx, k) : -1;
+        vk[k] = k < K ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_val), k)) : 0.0f;
+    }
     float* row = dlogits + t * E;
     for (int e0 = 0; e0 < E; e0 += 64) {
         const int e = e0 + lane;
         float v = 0.0f;
-        for (int k = 0; k < K; ++k) {
-            // both shuffles run on the whole wave (a shuffle under a lane-varying
-            // condition would read from inactive source lanes)
-            const int ik = __shfl(my_idx, k, 64);
-            const float vk = __shfl(my_val, k, 64);
-            if (ik == e) v = vk;
-        }
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k)
+            if (ik[k] == e) v = vk[k];
         if (e < E) row[e] = v;
     }
 }
@@ -184,8 +198,10 @@ extern "C" int moe_route_backward(const int32_t* topk_idx, const float* gates, c
     if (moe_host::misaligned(topk_idx) || moe_host::misaligned(gates) || moe_host::misaligned(dgates) ||
         moe_host::misaligned(dlogits))
         return MOE_EALIGN;
-    route_backward_kernel<<<(T + 3) / 4, 256, 0, (hipStream_t)stream>>>(topk_idx, gates, dgates, T, E, K,
-                                                                         dlogits);
+    const dim3 grid((T + 3) / 4), block(256);
+    hipStream_t s = (hipStream_t)stream;
+    if (K <= 8) route_backward_kernel<8><<<grid, block, 0, s>>>(topk_idx, gates, dgates, T, E, K, dlogits);
+    else route_backward_kernel<16><<<grid, block, 0, s>>>(topk_idx, gates, dgates, T, E, K, dlogits);
     return moe_host::launch_status();
 }
 
