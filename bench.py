@@ -218,22 +218,26 @@ def measured_copy_gbps(stream):
     return round(2 * n / (ms * 1e-3) / 1e9, 1)
 
 
-def measured_mfma_tflops(stream, target_ms=20.0):
+def measured_mfma_tflops(stream, target_ms=20.0, shape=32):
     """TFLOP/s that back-to-back bf16 MFMAs reach on this GPU with N(0,1) operands held in registers
-    (libmoe's probe, one workgroup of four waves per CU): the practical ceiling of an MFMA-bound kernel
-    on real data, since the clock the chip holds under MFMA load depends on the operand bits."""
+    (libmoe's probe, one workgroup of four waves per CU; shape 32: v_mfma_f32_32x32x16_bf16, 16:
+    v_mfma_f32_16x16x32_bf16): the practical ceiling of an MFMA-bound kernel on real data, since the
+    clock the chip holds under MFMA load depends on the operand bits."""
     import torch
     from routing_permute_groupgemm_amd import _lib
     blocks = torch.cuda.get_device_properties(0).multi_processor_count
     gen = torch.Generator(device="cuda").manual_seed(7)
-    ops = torch.randn((blocks * 4, 8, 64, 8), device="cuda", generator=gen).to(torch.bfloat16)
+    nfrag = 8 if shape == 32 else 16
+    ops = torch.randn((blocks * 4, nfrag, 64, 8), device="cuda", generator=gen).to(torch.bfloat16)
     out = torch.empty((blocks * 4, 64), dtype=torch.float32, device="cuda")
-    flop_per_iter = blocks * 4 * 16 * 2 * 32 * 32 * 16
+    # per wave and iteration: 16 MFMAs of 32x32x16, or 64 of 16x16x32
+    flop_per_iter = blocks * 4 * (16 * 2 * 32 * 32 * 16 if shape == 32 else 64 * 2 * 16 * 16 * 32)
+    probe = _lib.moe_probe_mfma if shape == 32 else _lib.moe_probe_mfma16
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
     def run(iters):
         e0.record(stream)
-        _lib.moe_probe_mfma(ops, iters, out=out)
+        probe(ops, iters, out=out)
         e1.record(stream)
         torch.cuda.synchronize()
         return e0.elapsed_time(e1)
@@ -492,6 +496,7 @@ def main():
     else:
         # likewise the rate back-to-back MFMAs on random operands reach on this GPU
         rl["measured_mfma_tflops"] = measured_mfma_tflops(stream)
+        rl["measured_mfma16_tflops"] = measured_mfma_tflops(stream, shape=16)
     graph_ms = None
     if args.graph:
         one_step = t["one_step"]

@@ -369,6 +369,20 @@ int moe_router_backward(const moe_bf16* x, int T, int H, const moe_bf16* w_r, in
  */
 int moe_probe_mfma(const moe_bf16* operands, int blocks, int iters, float* out, moe_stream stream);
 
+/*
+ * The same measurement aid on the other bf16 MFMA shape,
+ * v_mfma_f32_16x16x32_bf16: each wave runs iters rounds of an 8 x 8 block of
+ * independent 16x16x32 MFMAs (the same 16 * 32768 flop per round and wave).
+ *   operands  bf16 [blocks*4][16][64][8]: fragments 0..7 of wave w are its A
+ *             operands, 8..15 its B operands; lane l of a fragment holds row
+ *             (or column) l%16 and contraction index 8*(l/16) + 0..7.
+ *   out       fp32 [blocks*4*64].
+ * For each wave the sum of out over its 64 lanes equals
+ *   iters * sum_{m,n<8} sum_{g<4, j<8} (sum_{l in group g} A_m[l][j]) * (sum_{l in group g} B_n[l][j])
+ * (lanes 16g .. 16g+15 form group g).  Limits and errors as moe_probe_mfma.
+ */
+int moe_probe_mfma16(const moe_bf16* operands, int blocks, int iters, float* out, moe_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -41,6 +41,7 @@ SIGNATURES = {
     "moe_router_logits": ([_p, _i, _i, _p, _i, _p, _p, _p, _z, _p], _i),
     "moe_router_backward": ([_p, _i, _i, _p, _i, _p, _p, _p, _p, _z, _p], _i),
     "moe_probe_mfma": ([_p, _i, _i, _p, _p], _i),
+    "moe_probe_mfma16": ([_p, _i, _i, _p, _p], _i),
 }
 
 MOE_EPI_NONE = 0
@@ -493,4 +494,19 @@ def moe_probe_mfma(operands, iters, out=None, stream=None):
     _need(out, torch.float32, "out")
     _shape(out, (waves, 64), "out")
     _check(load().moe_probe_mfma(_ptr(operands), waves // 4, iters, _ptr(out), _stream(stream)))
+    return out
+
+
+def moe_probe_mfma16(operands, iters, out=None, stream=None):
+    """The probe on 16x16x32 MFMAs: operands bf16 [blocks*4, 16, 64, 8] (per wave: 8 A then 8 B fragments)
+    -> out fp32 [blocks*4, 64]."""
+    _need(operands, torch.bfloat16, "operands")
+    if operands.dim() != 4 or tuple(operands.shape[1:]) != (16, 64, 8) or operands.shape[0] % 4:
+        raise MoeError(f"operands: expected shape (4*blocks, 16, 64, 8), got {tuple(operands.shape)}")
+    waves = operands.shape[0]
+    if out is None:
+        out = torch.empty((waves, 64), dtype=torch.float32, device=operands.device)
+    _need(out, torch.float32, "out")
+    _shape(out, (waves, 64), "out")
+    _check(load().moe_probe_mfma16(_ptr(operands), waves // 4, iters, _ptr(out), _stream(stream)))
     return out

@@ -33,8 +33,10 @@ def _run(cmd):
 
 
 def build_library(verbose: bool = False) -> str:
+    """MOE_HIPCC_FLAGS (environment) adds compiler flags, e.g. -DMOE_GEMM_MFMA16=0 to build the down dgrad
+    on 32x32x16 MFMAs for an A/B comparison of the same sources."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    inc = ["-I", os.path.join(ROOT, "include")]
+    inc = ["-I", os.path.join(ROOT, "include")] + os.environ.get("MOE_HIPCC_FLAGS", "").split()
     with tempfile.TemporaryDirectory(prefix="moe_build_") as tmpdir:
         objs, cmds = [], []
         for src in sources():

@@ -7,7 +7,9 @@
 // caller's operands: every wave keeps four A and four B fragments in
 // registers and runs a 4 x 4 block of independent 32x32x16 bf16 MFMAs, the
 // accumulator footprint of the GroupGEMM's 128 x 128 wave tile, with no
-// memory traffic inside the loop.
+// memory traffic inside the loop.  The second kernel does the same with
+// 16x16x32 bf16 MFMAs (an 8 x 8 block, eight A and eight B fragments), the
+// other MFMA shape of the same bf16 rate on paper.
 #include "moe_common.hpp"
 
 namespace moe {
@@ -45,11 +47,54 @@ __global__ __launch_bounds__(256) void mfma_probe_kernel(const bf16x8* __restric
     out[w * 64 + lane] = s;
 }
 
+// The same 128 x 128 accumulator footprint on v_mfma_f32_16x16x32_bf16: fragments
+// 0..7 of a wave are A, 8..15 B; lane l holds row / column l%16 and k values
+// 8*(l/16) + 0..7 of its fragment.
+__global__ __launch_bounds__(256) void mfma16_probe_kernel(const bf16x8* __restrict__ ops, int iters,
+                                                           float* __restrict__ out) {
+    const int lane = threadIdx.x & 63;
+    const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const bf16x8* o = ops + w * 16 * 64 + lane;
+    bf16x8 a[8], b[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        a[i] = o[i * 64];
+        b[i] = o[(8 + i) * 64];
+    }
+    f32x4 acc[8][8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int n = 0; n < 8; ++n) acc[m][n] = f32x4{};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+            for (int n = 0; n < 8; ++n)
+                acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m], b[n], acc[m][n], 0, 0, 0);
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int n = 0; n < 8; ++n)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s += acc[m][n][i];
+    out[w * 64 + lane] = s;
+}
+
 }  // namespace moe
 
 extern "C" int moe_probe_mfma(const moe_bf16* operands, int blocks, int iters, float* out, moe_stream stream) {
     if (blocks < 1 || blocks > (1 << 20) || iters < 0 || !operands || !out) return MOE_EINVAL;
     if (moe_host::misaligned(operands) || moe_host::misaligned(out)) return MOE_EALIGN;
     moe::mfma_probe_kernel<<<blocks, 256, 0, (hipStream_t)stream>>>((const moe::bf16x8*)operands, iters, out);
+    return moe_host::launch_status();
+}
+
+extern "C" int moe_probe_mfma16(const moe_bf16* operands, int blocks, int iters, float* out, moe_stream stream) {
+    if (blocks < 1 || blocks > (1 << 20) || iters < 0 || !operands || !out) return MOE_EINVAL;
+    if (moe_host::misaligned(operands) || moe_host::misaligned(out)) return MOE_EALIGN;
+    moe::mfma16_probe_kernel<<<blocks, 256, 0, (hipStream_t)stream>>>((const moe::bf16x8*)operands, iters, out);
     return moe_host::launch_status();
 }

@@ -39,3 +39,22 @@ def test_probe_zero_iterations_writes_zeros():
     _lib.moe_probe_mfma(ops, 0, out=out)
     torch.cuda.synchronize()
     assert torch.count_nonzero(out).item() == 0
+
+
+def expected_wave_sums16(ops, iters):
+    """ops int [waves, 16, 64, 8]: fragments 0..7 are A, 8..15 are B; lanes in groups of 16 share a k-set."""
+    o = ops.astype(np.float64).reshape(ops.shape[0], 16, 4, 16, 8)  # [w, frag, group, lane%16, j]
+    col = o.sum(axis=3)                                               # [w, frag, group, j]
+    a, b = col[:, :8], col[:, 8:]
+    return iters * np.einsum("wmgj,wngj->w", a, b)
+
+
+@pytest.mark.parametrize("blocks,iters", [(1, 1), (3, 7), (256, 64)])
+def test_probe16_matches_closed_form(blocks, iters):
+    rng = np.random.default_rng(blocks * 1000 + iters + 1)
+    ops = rng.integers(-1, 2, size=(blocks * 4, 16, 64, 8))
+    dev = torch.from_numpy(ops.astype(np.float32)).to(torch.bfloat16).cuda()
+    out = _lib.moe_probe_mfma16(dev, iters)
+    torch.cuda.synchronize()
+    got = out.double().sum(dim=1).cpu().numpy()
+    np.testing.assert_array_equal(got, expected_wave_sums16(ops, iters))
