@@ -448,6 +448,8 @@ def run_workload(name, args, n_steps, warmup, log):
         pass_="fwd+bwd" if shape.backward else "fwd",
         dispatch="zero-copy" if zero_copy else "row copy",
         routed_rows=rs["R"],
+        tokens_active=rs["T_act"],
+        experts_active=rs["n_active"],
         maxvio=round(synth.maxvio(rs["counts"], shape.T, shape.K, shape.E), 3),
         dominant=t["dom"],
         dominant_frac=roofline(work[t["dom"]], t["dom_ms"])["frac"],
@@ -537,7 +539,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": shape.name, "T": shape.T, "H": shape.H, "F": shape.F, "E": shape.E, "K": shape.K,
                    "e_local": shape.EL, "cap_rows": buf.cap, "pass": summ["pass_"], "dispatch": summ["dispatch"],
-                   "router_projection": args.router, "routed_rows": summ["routed_rows"], "maxvio": summ["maxvio"],
+                   "router_projection": args.router, "routed_rows": summ["routed_rows"],
+                   "tokens_active": summ["tokens_active"], "experts_active": summ["experts_active"], "maxvio": summ["maxvio"],
                    "seed": args.seed, "parallelism": "single GPU"},
         "roofline": rl,
         "groupgemm_mfma_frac": summ["groupgemm_mfma_frac"],

@@ -101,6 +101,8 @@ struct GemmParams {
     int kchunk;
     int64_t part_stride;
     const float* bias;    // ROWS EPI_F32: added to every row, [N]
+    int stagger_ticks;    // start delay step of the workgroups (100 MHz ticks; 0: none)
+    int stagger_phases;
 };
 
 typedef __attribute__((ext_vector_type(4))) int i32x4;
@@ -1227,6 +1229,21 @@ void gg_kernel(GemmParams p) {
     // 1 KiB of slack behind them
     __shared__ int s_idx[GATHER ? 2 * TL::kALoads * 64 + 256 : 1];
     __shared__ int s_maxrows;
+    // Start stagger, a measurement knob (off unless MOE_GEMM_STAGGER_P > 1 and
+    // MOE_GEMM_STAGGER_NS are set): workgroup b waits ((b / 8) % P) * NS
+    // before it starts, so that the persistent workgroups reach their tile
+    // epilogues, and issue their stores, at different times.  With P = 2..8
+    // and steps of 3.75-30 us no GEMM of the layer ran faster (the delay
+    // itself was the only change), so the workgroups' stores landing at once
+    // do not set the epilogue's cost.
+    if (p.stagger_ticks > 0) {
+        const int phase = (int)((blockIdx.x >> 3) % (unsigned)p.stagger_phases);
+        if (phase) {
+            const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+            const uint64_t wait = (uint64_t)phase * (uint64_t)p.stagger_ticks;
+            while (__builtin_amdgcn_s_memrealtime() - t0 < wait) __builtin_amdgcn_s_sleep(2);
+        }
+    }
     if (threadIdx.x == 0) s_maxrows = 0;
     __syncthreads();
     for (int j = threadIdx.x; j <= p.e_local; j += TL::kThreads) {
@@ -1304,7 +1321,10 @@ static int launch_cfg(const GemmParams& p, hipStream_t s) {
     int64_t g = std::min<int64_t>(total_upper, (int64_t)moe_host::num_cus() * per_cu);
     const int grid = (int)((g + 7) / 8 * 8);
     if (grid == 0) return MOE_OK;
-    gg_kernel<BM, BN, BK, WM, WN, LB, EPI, SCHED, LDSB, ALT, GATHER><<<grid, TL::kThreads, 0, s>>>(p);
+    GemmParams q = p;
+    q.stagger_phases = std::max(1, env_int("MOE_GEMM_STAGGER_P", 1));
+    q.stagger_ticks = q.stagger_phases > 1 ? env_int("MOE_GEMM_STAGGER_NS", 0) / 10 : 0;
+    gg_kernel<BM, BN, BK, WM, WN, LB, EPI, SCHED, LDSB, ALT, GATHER><<<grid, TL::kThreads, 0, s>>>(q);
     return moe_host::launch_status();
 }
 

@@ -1,0 +1,276 @@
+"""Turn rocprofv3 CSV output of a bench.py run into the short text summaries kept beside the code.
+
+Two subcommands, both run on the host after the profiled bench run:
+
+  stats     <dir>/<name>_kernel_trace.csv and _kernel_stats.csv of a `--kernel-trace --stats` run
+            -> a markdown table of per-step kernel time (every dispatch is labelled with the layer
+               step it belongs to) and the profiler's own per-kernel-name table
+  counters  <dir>/<tag>_p<i>/p_counter_collection.csv of one `--pmc` run per counter group, and
+            <dir>/calib_p3, calib_p4 of a plain device copy under FETCH_SIZE and WRITE_SIZE
+            -> a markdown table of derived counter figures per GroupGEMM, and the HBM bytes per
+               launch of each GroupGEMM merged into a JSON file that bench.py reads for its
+               roofline's traffic figure
+
+Dispatches are labelled by kernel name; the GroupGEMM template's layout / epilogue / schedule
+arguments name its step.  The two weight-gradient launches of a step share one template
+instance and are told apart by their order inside the step (dW_gate|dW_up first, dW_down second).
+A step starts at each router top-k dispatch.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import json
+import os
+import re
+import sys
+
+REPO = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# (layout, epilogue, schedule) template arguments of the GroupGEMM -> step
+GG_STEPS = {(1, 1, 0): "expert_up", (1, 0, 0): "expert_down", (0, 2, 0): "bwd_down_dgrad",
+            (0, 0, 0): "bwd_up_dgrad", (1, 3, 0): "router_fwd"}
+WGRAD_ORDER = ("wgrad_gate_up", "wgrad_down")
+OTHER = [("route_kernel", "route"), ("perm_count_kernel", "permute (count)"), ("perm_scan_kernel", "permute (scan)"),
+         ("perm_rank_kernel", "permute (rank)"), ("perm_copy_kernel", "permute (row copy)"),
+         ("gather_kernel", "bwd_gather"), ("route_backward_kernel", "route_bwd"),
+         ("combine_kernel<true", "combine"), ("combine_kernel<false", "bwd_combine"),
+         ("mfma16_probe_kernel", "MFMA probe 16x16x32 (after the timed steps)"),
+         ("mfma_probe_kernel", "MFMA probe 32x32x16 (after the timed steps)"),
+         ("split_offsets_kernel", "wgrad split (offsets)"), ("sum_split_kernel", "wgrad split (sum)"),
+         ("copyBuffer", "runtime copy"), ("at::native", "torch (input set-up)")]
+STEP_ORDER = ["router_fwd", "route", "permute (count)", "permute (scan)", "permute (rank)", "permute (row copy)",
+              "expert_up", "expert_down", "combine", "bwd_gather", "route_bwd", "bwd_down_dgrad", "bwd_up_dgrad",
+              "bwd_combine", "wgrad_gate_up", "wgrad_down"]
+GG_RE = re.compile(r"gg_kernel<(\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (\w+)>")
+
+
+def label_dispatches(rows):
+    """rows: dicts with Dispatch_Id and Kernel_Name.  Returns {dispatch id: step label}."""
+    out = {}
+    wg_in_step = 0
+    for r in sorted(rows, key=lambda r: int(r["Dispatch_Id"])):
+        name, d = r["Kernel_Name"], int(r["Dispatch_Id"])
+        if "route_kernel" in name:
+            wg_in_step = 0
+        m = GG_RE.search(name)
+        if m:
+            key = (int(m.group(6)), int(m.group(7)), int(m.group(8)))
+            if key == (1, 3, 1):
+                out[d] = WGRAD_ORDER[wg_in_step] if wg_in_step < len(WGRAD_ORDER) else "wgrad (outside a step)"
+                wg_in_step += 1
+            else:
+                step = GG_STEPS.get(key, "GroupGEMM " + m.group(0))
+                out[d] = step + (" (gathered rows)" if m.group(11) == "true" else "")
+            continue
+        for pat, lab in OTHER:
+            if pat in name:
+                out[d] = lab
+                break
+        else:
+            out[d] = name[:60]
+    return out
+
+
+def bench_json(path):
+    """The bench's JSON line (its last line that parses as a JSON object)."""
+    res = None
+    with open(path) as fh:
+        for line in fh:
+            line = line.strip()
+            if line.startswith("{"):
+                try:
+                    res = json.loads(line)
+                except ValueError:
+                    pass
+    if res is None:
+        raise SystemExit(f"no bench JSON line in {path}")
+    return res
+
+
+def work_of(bj):
+    """Algorithmic bytes and flops per launch of every step of the bench's headline workload."""
+    sys.path.insert(0, REPO)
+    import bench
+    from routing_permute_groupgemm_amd import synth
+    c = bj["config"]
+    shape = synth.WORKLOADS[c["workload"]]
+    return bench.algorithmic_work(shape, c["routed_rows"], c["tokens_active"], c["experts_active"],
+                                  c["dispatch"] == "zero-copy", c.get("router_projection", False)), bench.src_hash()
+
+
+def cmd_stats(a):
+    trace = list(csv.DictReader(open(os.path.join(a.dir, f"{a.name}_kernel_trace.csv"))))
+    labels = label_dispatches(trace)
+    dur = collections.defaultdict(list)
+    kname = {}
+    for r in trace:
+        lab = labels[int(r["Dispatch_Id"])]
+        dur[lab].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
+        kname.setdefault(lab, r["Kernel_Name"])
+    total = sum(sum(v) for v in dur.values())
+    bj = bench_json(a.bench_log)
+    order = [s for s in STEP_ORDER if s in dur] + sorted(s for s in dur if s not in STEP_ORDER)
+    L = [f"# Kernel time per step, {bj['config']['workload']}\n",
+         "Command (MI355X, ROCm 7.2, from the repository root):\n",
+         f"`{a.command}`\n",
+         "Every dispatch of the run labelled with the layer step it belongs to (the two weight-gradient launches "
+         "of a step share one kernel and are told apart by their order in the step). Durations in µs.\n",
+         "| step | kernel | dispatches | avg µs | min µs | max µs | share |", "|---|---|---|---|---|---|---|"]
+    for s in order:
+        v = dur[s]
+        kn = kname[s].replace("|", "\\|")
+        kn = kn if len(kn) <= 72 else kn[:72] + "…"
+        L.append(f"| {s} | `{kn}` | {len(v)} | {sum(v) / len(v):.1f} | {min(v):.1f} | {max(v):.1f} | "
+                 f"{100 * sum(v) / total:.1f}% |")
+    rl = bj["roofline"]
+    L.append("")
+    L.append(f"Bench line of the same run: {bj['value']:.0f} {bj['unit']}, {bj['ms_per_step']} ms/step; roofline kernel "
+             f"{rl['kernel']}: {rl['launch_ms']} ms per launch between HIP events, {rl['achieved']} {rl['unit']} = "
+             f"{rl['frac']} of {rl['peak']}.")
+    sp = os.path.join(a.dir, f"{a.name}_kernel_stats.csv")
+    if os.path.exists(sp):
+        L.append("\nThe profiler's own `--stats` table (per kernel name; the weight-gradient row mixes both launches):\n")
+        L.append("| kernel | calls | avg µs | min µs | max µs | % |")
+        L.append("|---|---|---|---|---|---|")
+        for r in list(csv.DictReader(open(sp)))[:a.top]:
+            kn = r["Name"].replace("|", "\\|")
+            kn = kn if len(kn) <= 72 else kn[:72] + "…"
+            L.append(f"| `{kn}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+                     f"{float(r['MaxNs']) / 1e3:.1f} | {r['Percentage']} |")
+    open(a.out, "w").write("\n".join(L) + "\n")
+    print("\n".join(L))
+
+
+COUNTER_GROUPS = {
+    1: "SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_WAIT_INST_LDS SQ_VALU_MFMA_BUSY_CYCLES "
+       "SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS",
+    2: "SQ_INSTS_VALU SQ_INSTS_LDS SQ_INSTS_SALU SQ_INSTS_MFMA SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_INSTS_SMEM "
+       "SQ_CYCLES",
+    3: "FETCH_SIZE",
+    4: "WRITE_SIZE",
+    5: "TCC_HIT_sum TCC_MISS_sum GRBM_GUI_ACTIVE GRBM_COUNT",
+}
+
+
+def load_pass(path):
+    rows = list(csv.DictReader(open(path)))
+    labels = label_dispatches(list({r["Dispatch_Id"]: r for r in rows}.values()))
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    dur = {}
+    for r in rows:
+        d = int(r["Dispatch_Id"])
+        per[d][r["Counter_Name"]] += float(r["Counter_Value"])
+        dur[d] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    agg = collections.defaultdict(lambda: collections.defaultdict(list))
+    for d, cs in per.items():
+        for c, v in cs.items():
+            agg[labels[d]][c].append(v)
+        agg[labels[d]]["_dur"].append(dur[d])
+    return {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in agg.items()}, \
+        {k: len(v["_dur"]) for k, v in agg.items()}
+
+
+def calib_factor(path, counter):
+    """Counted KiB per KiB moved by the 1 GiB device copy of `bench.py --calib-copy`."""
+    vals = collections.defaultdict(float)
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] == counter:
+            vals[r["Dispatch_Id"]] += float(r["Counter_Value"])
+    big = [v for v in vals.values() if v > 1e5]
+    if not big:
+        raise SystemExit(f"no copy dispatch in {path}")
+    return sum(big) / len(big) / (1 << 20)
+
+
+def cmd_counters(a):
+    bj = bench_json(a.bench_log)
+    wl = bj["config"]["workload"]
+    work, sha = work_of(bj)
+    ff = calib_factor(os.path.join(a.dir, "calib_p3", "p_counter_collection.csv"), "FETCH_SIZE")
+    wf = calib_factor(os.path.join(a.dir, "calib_p4", "p_counter_collection.csv"), "WRITE_SIZE")
+    res = collections.defaultdict(dict)
+    ndisp, durs = {}, collections.defaultdict(list)
+    for i in COUNTER_GROUPS:
+        r, n = load_pass(os.path.join(a.dir, f"{a.tag}_p{i}", "p_counter_collection.csv"))
+        for k, cs in r.items():
+            durs[k].append(cs.pop("_dur"))
+            res[k].update(cs)
+            ndisp[k] = n[k]
+    gemms = [s for s in STEP_ORDER if s in res and s in work and work[s]["flops"]]
+    L = [f"# Counters of the GroupGEMMs, {wl}\n",
+         f"One rocprofv3 counter run per group (MI355X, ROCm 7.2), every GroupGEMM dispatch of the run:\n",
+         f"`{a.command}`\n", "with `<group>` one of:\n"]
+    L += [f"{i}. `{g}`" for i, g in COUNTER_GROUPS.items()]
+    L.append("\nHBM bytes: `FETCH_SIZE` and `WRITE_SIZE` (KiB per dispatch) divided by what the same counter reads for "
+             f"a plain 1 GiB device copy (`{a.calib_command}`, once per counter): fetch factor {ff:.4f}, write "
+             f"factor {wf:.4f} counted KiB per KiB moved. Values are means over the dispatches of each step.\n")
+    L.append("Derived: clock = (`GRBM_GUI_ACTIVE`/8) / dispatch time; MFMA busy = `SQ_VALU_MFMA_BUSY_CYCLES` / "
+             "(`GRBM_GUI_ACTIVE`/8 x 1024 SIMDs); wait shares = `SQ_WAIT_INST_ANY` (`SQ_WAIT_INST_LDS`) / "
+             "`SQ_WAVE_CYCLES`; L2 hit = `TCC_HIT_sum` / (`TCC_HIT_sum` + `TCC_MISS_sum`); per-MFMA instruction "
+             "ratios from `SQ_INSTS_*`; HBM read / write the scaled `FETCH_SIZE` / `WRITE_SIZE` against the step's "
+             "algorithmic bytes.\n")
+    L.append("| GEMM | dispatches | µs (pass 5) | clock GHz | MFMA busy | wait share | LDS-wait share | SALU/MFMA | "
+             "VALU/MFMA | LDS/MFMA | L2 hit | LDS bank conflict / active | HBM read GB | HBM write GB | "
+             "algorithmic GB | (read+write)/algorithmic |")
+    L.append("|" + "---|" * 16)
+    try:
+        traffic = json.load(open(a.traffic))
+    except (OSError, ValueError):
+        traffic = {}
+    for s in gemms:
+        c = res[s]
+        dur = durs[s][4]
+        gui = c["GRBM_GUI_ACTIVE"] / 8
+        mf = c["SQ_INSTS_MFMA"]
+        rd = c["FETCH_SIZE"] * 1024 / ff / 1e9
+        wr = c["WRITE_SIZE"] * 1024 / wf / 1e9
+        alg = work[s]["bytes"] / 1e9
+        L.append(f"| {s} | {ndisp[s]} | {dur * 1e6:.0f} | {gui / dur / 1e9:.2f} | "
+                 f"{c['SQ_VALU_MFMA_BUSY_CYCLES'] / (gui * 1024):.3f} | {c['SQ_WAIT_INST_ANY'] / c['SQ_WAVE_CYCLES']:.3f} | "
+                 f"{c['SQ_WAIT_INST_LDS'] / c['SQ_WAVE_CYCLES']:.3f} | {c['SQ_INSTS_SALU'] / mf:.2f} | "
+                 f"{(c['SQ_INSTS_VALU'] - mf) / mf:.2f} | {c['SQ_INSTS_LDS'] / mf:.2f} | "
+                 f"{c['TCC_HIT_sum'] / (c['TCC_HIT_sum'] + c['TCC_MISS_sum']):.3f} | "
+                 f"{c['SQ_LDS_BANK_CONFLICT'] / max(c['SQ_LDS_IDX_ACTIVE'], 1):.3f} | {rd:.2f} | {wr:.2f} | "
+                 f"{alg:.2f} | {(rd + wr) / alg:.2f} |")
+        traffic[f"{s}@{wl}"] = dict(gemm_src_sha=sha, traffic_bytes_per_launch=int((rd + wr) * 1e9),
+                                    fetch_kib=round(c["FETCH_SIZE"], 1), write_kib=round(c["WRITE_SIZE"], 1),
+                                    fetch_factor=round(ff, 6), write_factor=round(wf, 6), dispatches=ndisp[s])
+    L.append("\nRaw means per dispatch:\n")
+    cn = sorted({c for s in gemms for c in res[s]})
+    L.append("| counter | " + " | ".join(gemms) + " |")
+    L.append("|---|" + "---|" * len(gemms))
+    for c in cn:
+        L.append(f"| `{c}` | " + " | ".join(f"{res[s].get(c, float('nan')):.4g}" for s in gemms) + " |")
+    open(a.out, "w").write("\n".join(L) + "\n")
+    with open(a.traffic, "w") as fh:
+        json.dump(dict(sorted(traffic.items())), fh, indent=1)
+        fh.write("\n")
+    print("\n".join(L[:20 + len(gemms)]))
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(prog="python -m routing_permute_groupgemm_amd.profsum")
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("--dir", required=True)
+    s.add_argument("--name", default="kt", help="rocprofv3 -o name")
+    s.add_argument("--bench-log", required=True, help="stdout of the profiled bench run")
+    s.add_argument("--command", required=True, help="the profiled command, quoted in the summary")
+    s.add_argument("--out", required=True)
+    s.add_argument("--top", type=int, default=20)
+    c = sub.add_parser("counters")
+    c.add_argument("--dir", required=True)
+    c.add_argument("--tag", required=True, help="counter runs are <dir>/<tag>_p1 ... _p5")
+    c.add_argument("--bench-log", required=True, help="stdout of one of the counter runs")
+    c.add_argument("--command", required=True)
+    c.add_argument("--calib-command", required=True)
+    c.add_argument("--out", required=True)
+    c.add_argument("--traffic", default=os.path.join(REPO, "profiles", "traffic.json"))
+    a = ap.parse_args(argv)
+    (cmd_stats if a.cmd == "stats" else cmd_counters)(a)
+
+
+if __name__ == "__main__":
+    main()
