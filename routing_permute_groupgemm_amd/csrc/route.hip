@@ -8,21 +8,23 @@
 // chosen probabilities renormalised over the K choices; the softmax
 // normaliser cancels, so g_k = exp(s_k - s_max) / sum_k' exp(s_k' - s_max).
 //
-// One wave64 per token.  Lane l holds the scores of experts l, l+64, ... as
-// order-preserving 32-bit keys.  Each of the K rounds takes the lane's best
-// remaining key (the lowest slot wins a tie inside the lane: lowest expert
-// id), reduces the lane bests to the wave maximum with DPP row operations
-// (no LDS round trips), and, if several lanes hold that score, takes the
-// lowest expert id among them; the winner clears its key.  Row loads are
-// lane-strided and coalesced.
+// A wave64 takes one token at a time.  Lane l holds the scores of experts l,
+// l+64, ... as order-preserving 32-bit keys (row loads are lane-strided and
+// coalesced).  The top K are found by a threshold and a rank count over the
+// few candidates above it (route_kernel, below); tokens with too many
+// candidates take K rounds of a wave maximum instead: each round takes the
+// lane's best remaining key (the lowest slot wins a tie inside the lane:
+// lowest expert id), reduces the lane bests to the wave maximum with DPP row
+// operations, and, if several lanes hold that score, takes the lowest expert
+// id among them; the winner clears its key.
 #include "moe_common.hpp"
 
 namespace moe {
 
 __device__ __forceinline__ uint32_t score_key(float s) {
-    if (s == 0.0f) s = 0.0f;  // -0 and +0 compare equal: canonicalise to +0
-    uint32_t u = __float_as_uint(s);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);  // > 0 for every non-NaN score
+    // -0 and +0 compare equal: s + 0 is +0 for both (and s for every other s)
+    const uint32_t u = __float_as_uint(s + 0.0f);
+    return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);  // negative: ~u; else u | sign; > 0 unless NaN
 }
 
 __device__ __forceinline__ float key_score(uint32_t u) {
@@ -53,22 +55,15 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
+// The K rounds above, for one token whose lane l holds the keys of experts
+// l, l + 64, ... (0: absent or taken).  On return lane k < K holds choice k
+// (its expert id and score); s_max is the best score.
 template <int EPL>
-__global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int T, int E, int K,
-                                                    int32_t* __restrict__ topk_idx,
-                                                    float* __restrict__ gates) {
-    const int lane = threadIdx.x & 63;
-    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= T) return;
-    const float* row = logits + t * E;
-    uint32_t key[EPL];  // 0 = absent or taken (below every score's key)
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-        const int e = i * 64 + lane;
-        key[i] = e < E ? score_key(__builtin_nontemporal_load(row + e)) : 0u;
-    }
-    int my_idx = 0;
-    float my_score = 0.0f, s_max = 0.0f;
+__device__ __forceinline__ void select_rounds(uint32_t (&key)[EPL], int K, int lane, int& my_idx, float& my_score,
+                                              float& s_max) {
+    my_idx = 0;
+    my_score = 0.0f;
+    s_max = 0.0f;
     for (int k = 0; k < K; ++k) {
         // the lane's best remaining key; strict > keeps the lowest slot on a tie
         uint32_t best = key[0];
@@ -95,67 +90,217 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
             for (int i = 0; i < EPL; ++i)
                 if (i == (e_win >> 6)) key[i] = 0u;
         }
-        const float s = key_score(m);
-        if (k == 0) s_max = s;
+        const float sc = key_score(m);
+        if (k == 0) s_max = sc;
         if (lane == k) {
             my_idx = e_win;
-            my_score = s;
+            my_score = sc;
         }
-    }
-    // gates: lanes 0..K-1 hold one choice each; the sum runs over k ascending
-    float ex = lane < K ? expf(my_score - s_max) : 0.0f;
-    float z = 0.0f;
-    for (int k = 0; k < K; ++k) z += __shfl(ex, k, 64);
-    if (lane < K) {
-        topk_idx[t * K + lane] = my_idx;
-        gates[t * K + lane] = ex / z;
     }
 }
 
-// Router backward: one wave per token.  The gates are the softmax of the
-// chosen scores, so with g, dg the token's gates and gate gradients the
-// score gradient is g_k * (dg_k - sum_j g_j dg_j) at the chosen experts and 0
-// elsewhere.  The sum runs over j ascending.  The K chosen experts and their
-// values are wave-uniform: lane k holds choice k, and readlane copies them
-// into scalar registers once.  Each lane then writes its experts lane,
-// lane + 64, ..., selecting its value among the K choices, so the row is
-// written once, coalesced.
-template <int KMAX>
+// Top-K by a threshold and a rank count.  Split the lanes into G >= K groups
+// (8 groups of 8 lanes for K <= 8, 16 of 4 for K <= 16): the G group maxima
+// are G distinct experts, so the K-th best key is at least theta, the
+// smallest group maximum, and every expert of the top K has a key >= theta.
+// Those candidates (about 20 of 256 on the router scores of the layer's
+// workloads) are compacted into LDS as 64-bit words key << 32 | ~id, whose
+// unsigned order is (score descending, id ascending); lane c then counts the
+// candidates above candidate c, which is its rank, and ranks 0..K-1 are the
+// choices.  Tokens with more than 64 candidates (ties, or flat scores) take
+// the K rounds instead.  Both paths give the same choices.
+//
+// A wave takes a batch of 64 / KP consecutive tokens (KP: the next power of
+// two >= K), one token at a time with the next row in flight.  The choices
+// (expert id and score - s_max) go to LDS, slot KP*token + rank; after the
+// batch, lane KP*i + k computes choice k of token i's gate,
+// exp(s_k - s_max) / sum_k' exp(s_k' - s_max) with the sum taken over k'
+// ascending, and the batch's ids and gates are written with one coalesced
+// store each.  FULL: E is a multiple of 64 (no absent lanes).
+template <int EPL, bool FULL>
+__global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int T, int E, int K,
+                                                    int kp_log2, int32_t* __restrict__ topk_idx,
+                                                    float* __restrict__ gates) {
+    __shared__ uint64_t s_cand[4][64];
+    __shared__ int s_bid[4][64];    // batch: chosen expert id, slot KP*token + rank
+    __shared__ float s_bsc[4][64];  // batch: chosen score - s_max, then exp of it
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tb_n = 64 >> kp_log2;  // tokens per batch
+    const int64_t n_batches = ((int64_t)T + tb_n - 1) / tb_n;
+    const int64_t stride = (int64_t)gridDim.x * 4;
+    uint64_t* cand = s_cand[wave];
+    int* bid = s_bid[wave];
+    float* bsc = s_bsc[wave];
+    float raw[EPL];
+    // branch-free row loads: lanes past E (and rows past T) load a valid
+    // address, and their values are discarded
+    auto load_row = [&](int64_t tt) {
+        const float* row = logits + min(tt, (int64_t)T - 1) * E;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            const int e = i * 64 + lane;
+            raw[i] = __builtin_nontemporal_load(row + (FULL || e < E ? e : 0));
+        }
+    };
+    int64_t b = (int64_t)blockIdx.x * 4 + wave;
+    load_row(b * tb_n);
+    for (; b < n_batches; b += stride) {
+        const int64_t t0 = b * tb_n;
+        const int nt = (int)min((int64_t)tb_n, (int64_t)T - t0);
+        for (int ti = 0; ti < nt; ++ti) {
+            uint32_t key[EPL];  // 0 = absent (below every score's key)
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) {
+                const uint32_t kv = score_key(raw[i]);
+                key[i] = FULL || i * 64 + lane < E ? kv : 0u;
+            }
+            // the next row: this batch's next token, or the next batch's first
+            load_row(ti + 1 < nt ? t0 + ti + 1 : (b + stride) * tb_n);
+
+            // theta: the smallest of the G group maxima
+            uint32_t gmax = key[0];
+#pragma unroll
+            for (int i = 1; i < EPL; ++i) gmax = max(gmax, key[i]);
+            gmax = max(gmax, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)gmax, 0xB1, 0xf, 0xf, false));  // quad [1,0,3,2]
+            gmax = max(gmax, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)gmax, 0x4E, 0xf, 0xf, false));  // quad [2,3,0,1]
+            if (K <= 8)
+                gmax = max(gmax, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)gmax, 0x141, 0xf, 0xf, false));  // half-row
+            const uint32_t theta = max(wave_min_u32(gmax), 1u);  // absent keys (0) are never candidates
+
+            uint64_t cm[EPL];
+            int n = 0;
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) {
+                cm[i] = __ballot(key[i] >= theta);
+                n += __popcll(cm[i]);
+            }
+            int my_idx = 0, rank = 64;
+            float my_score = 0.0f, s_max;
+            if (n <= 64) {
+                int off = 0;
+#pragma unroll
+                for (int i = 0; i < EPL; ++i) {
+                    if (key[i] >= theta) {
+                        const int pos = off + (int)__builtin_amdgcn_mbcnt_hi(
+                                                  (uint32_t)(cm[i] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)cm[i], 0u));
+                        *(MOE_LDS uint64_t*)(cand + pos) =
+                            ((uint64_t)key[i] << 32) | (uint32_t)~(uint32_t)(i * 64 + lane);
+                    }
+                    off += __popcll(cm[i]);
+                }
+                asm volatile("" ::: "memory");  // a wave's LDS accesses execute in order
+                const uint64_t v = lane < n ? *(const MOE_LDS uint64_t*)(cand + lane) : 0ull;
+                int r = 0;
+                for (int j = 0; j < n; ++j) r += *(const MOE_LDS uint64_t*)(cand + j) > v;
+                if (lane < n) rank = r;
+                const int top = __builtin_ctzll(__ballot(rank == 0));
+                s_max = key_score((uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), top));
+                my_score = key_score((uint32_t)(v >> 32));
+                my_idx = (int)~(uint32_t)v;
+            } else {
+                select_rounds<EPL>(key, K, lane, my_idx, my_score, s_max);
+                if (lane < K) rank = lane;
+            }
+            if (rank < K) {
+                *(MOE_LDS int*)(bid + (ti << kp_log2) + rank) = my_idx;
+                *(MOE_LDS float*)(bsc + (ti << kp_log2) + rank) = my_score - s_max;
+            }
+            asm volatile("" ::: "memory");  // this token's candidates are read before the next token's are written
+        }
+        // the batch's gates: lane KP*i + k holds choice k of token i
+        const int ti = lane >> kp_log2, k = lane & ((1 << kp_log2) - 1);
+        const bool valid = ti < nt && k < K;
+        const float ex = valid ? expf(*(const MOE_LDS float*)(bsc + lane)) : 0.0f;
+        asm volatile("" ::: "memory");
+        if (valid) *(MOE_LDS float*)(bsc + lane) = ex;
+        asm volatile("" ::: "memory");
+        float z = 0.0f;
+        const int base = lane & ~((1 << kp_log2) - 1);
+        for (int j = 0; j < K; ++j) z += *(const MOE_LDS float*)(bsc + base + j);
+        if (valid) {
+            const int64_t o = (t0 + ti) * K + k;
+            topk_idx[o] = *(const MOE_LDS int*)(bid + lane);
+            gates[o] = ex / z;
+        }
+        asm volatile("" ::: "memory");  // the batch's slots are read before the next batch writes them
+    }
+}
+
+// Router backward.  The gates are the softmax of the chosen scores, so with
+// g, dg a token's gates and gate gradients the score gradient is
+// g_k * (dg_k - sum_j g_j dg_j) at the chosen experts and 0 elsewhere; the
+// sum runs over j ascending (fused multiply-adds from 0).
+//
+// The output is a dense [T, E] fp32 array that is almost all zeros, so the
+// kernel is bound by its writes.  A wave takes a group of 8 tokens at a time
+// (4 when K > 8): with KP the next power of two >= K, lane KP*t + k holds
+// choice k of token t of the group.  The group's rows, contiguous in dlogits,
+// are built in the wave's slice of LDS (zeroed, then one scatter of the
+// chosen values; a wave's LDS accesses execute in order) and written with
+// 16-byte stores, 1 KiB per instruction.  Waves loop over token groups and
+// load the next group's inputs before they write the current one.
+// Precondition: a token's K experts are distinct (moe_route's output is).
+constexpr int kRbTok = 8;  // rows of a group (K <= 8; K > 8 uses 4)
+
+template <int EMAX>
 __global__ __launch_bounds__(256) void route_backward_kernel(const int32_t* __restrict__ topk_idx,
                                                              const float* __restrict__ gates,
                                                              const float* __restrict__ dgates, int T, int E, int K,
-                                                             float* __restrict__ dlogits) {
-    const int lane = threadIdx.x & 63;
-    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= T) return;
-    const int my_idx = lane < K ? topk_idx[t * K + lane] : -1;
-    const float my_g = lane < K ? gates[t * K + lane] : 0.0f;
-    const float my_dg = lane < K ? dgates[t * K + lane] : 0.0f;
-    float sum = 0.0f;
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-        if (j < K) {
-            const float gj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_g), j));
-            const float dgj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_dg), j));
-            sum += gj * dgj;
+                                                             int kp_log2, float* __restrict__ dlogits) {
+    __shared__ __attribute__((aligned(16))) float s_rows[4][kRbTok * EMAX];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    float* rows = s_rows[wave];
+    const int KP = 1 << kp_log2;
+    const int tpw = min(kRbTok, 64 >> kp_log2);  // tokens per group
+    const int tj = lane >> kp_log2, k = lane & (KP - 1);
+    const int64_t n_groups = ((int64_t)T + tpw - 1) / tpw;
+    const int64_t stride = (int64_t)gridDim.x * 4;
+    auto load = [&](int64_t grp, int& idx, float& g, float& dg) {
+        const int64_t t = grp * tpw + tj;
+        idx = -1;
+        g = dg = 0.0f;
+        if (tj < tpw && k < K && t < T) {
+            idx = topk_idx[t * K + k];
+            g = gates[t * K + k];
+            dg = dgates[t * K + k];
         }
-    }
-    const float my_val = my_g * (my_dg - sum);
-    int ik[KMAX];
-    float vk[KMAX];
-#pragma unroll
-    for (int k = 0; k < KMAX; ++k) {
-        ik[k] = k < K ? __builtin_amdgcn_readlane(my_idx, k) : -1;
-        vk[k] = k < K ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_val), k)) : 0.0f;
-    }
-    float* row = dlogits + t * E;
-    for (int e0 = 0; e0 < E; e0 += 64) {
-        const int e = e0 + lane;
-        float v = 0.0f;
-#pragma unroll
-        for (int k = 0; k < KMAX; ++k)
-            if (ik[k] == e) v = vk[k];
-        if (e < E) row[e] = v;
+    };
+    int64_t grp = (int64_t)blockIdx.x * 4 + wave;
+    int idx;
+    float g, dg;
+    load(grp, idx, g, dg);
+    for (; grp < n_groups; grp += stride) {
+        int n_idx;
+        float n_g, n_dg;
+        load(grp + stride, n_idx, n_g, n_dg);
+        // the token's sum over its choices: lanes of the token read them in turn
+        float sum = 0.0f;
+        const int base = (tj << kp_log2) & 63;
+        for (int j = 0; j < K; ++j) {
+            const float gj = __shfl(g, base + j, 64);
+            const float dgj = __shfl(dg, base + j, 64);
+            sum = __builtin_fmaf(gj, dgj, sum);
+        }
+        const float val = g * (dg - sum);
+        asm volatile("" ::: "memory");  // the previous group's rows are read before they are cleared
+        const int64_t t0 = grp * tpw;
+        const int nf = (int)min((int64_t)tpw, (int64_t)T - t0) * E;  // floats of the group's rows
+        const int nq = (nf + 3) >> 2;
+#pragma unroll 4
+        for (int q = lane; q < nq; q += 64) *(MOE_LDS f32x4*)(rows + 4 * q) = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        asm volatile("" ::: "memory");
+        if (idx >= 0 && idx < E) *(MOE_LDS float*)(rows + tj * E + idx) = val;
+        asm volatile("" ::: "memory");
+        float* dst = dlogits + t0 * E;
+        if ((nf & 3) == 0) {
+#pragma unroll 4
+            for (int q = lane; q < nq; q += 64) *(f32x4*)(dst + 4 * q) = *(const MOE_LDS f32x4*)(rows + 4 * q);
+        } else {
+            for (int f = lane; f < nf; f += 64) dst[f] = *(const MOE_LDS float*)(rows + f);
+        }
+        idx = n_idx;
+        g = n_g;
+        dg = n_dg;
     }
 }
 
@@ -172,18 +317,31 @@ extern "C" int moe_route(const float* logits, int T, int E, int K, int32_t* topk
     if (moe_host::misaligned(logits) || moe_host::misaligned(topk_idx) || moe_host::misaligned(gates))
         return MOE_EALIGN;
     hipStream_t s = (hipStream_t)stream;
-    dim3 grid((T + 3) / 4), block(256);
-    int epl = (E + 63) / 64;
+    // waves loop over batches of 64 / KP tokens (KP: the next power of two >= K)
+    int kp = 1;
+    while (kp < K) kp <<= 1;
+    const int64_t batches = ((int64_t)T + 64 / kp - 1) / (64 / kp);
+    const dim3 grid((unsigned)std::min<int64_t>((batches + 3) / 4, (int64_t)moe_host::num_cus() * 8)), block(256);
+    int kp_log2 = 0;
+    while ((1 << kp_log2) < K) ++kp_log2;
+    const int epl = (E + 63) / 64;
+    const bool full = E % 64 == 0;
+#define MOE_ROUTE_CASE(N)                                                                                  \
+    case N:                                                                                                \
+        if (full) route_kernel<N, true><<<grid, block, 0, s>>>(logits, T, E, K, kp_log2, topk_idx, gates); \
+        else route_kernel<N, false><<<grid, block, 0, s>>>(logits, T, E, K, kp_log2, topk_idx, gates);     \
+        break;
     switch (epl) {
-        case 1: route_kernel<1><<<grid, block, 0, s>>>(logits, T, E, K, topk_idx, gates); break;
-        case 2: route_kernel<2><<<grid, block, 0, s>>>(logits, T, E, K, topk_idx, gates); break;
-        case 3: route_kernel<3><<<grid, block, 0, s>>>(logits, T, E, K, topk_idx, gates); break;
-        case 4: route_kernel<4><<<grid, block, 0, s>>>(logits, T, E, K, topk_idx, gates); break;
-        case 5: route_kernel<5><<<grid, block, 0, s>>>(logits, T, E, K, topk_idx, gates); break;
-        case 6: route_kernel<6><<<grid, block, 0, s>>>(logits, T, E, K, topk_idx, gates); break;
-        case 7: route_kernel<7><<<grid, block, 0, s>>>(logits, T, E, K, topk_idx, gates); break;
-        default: route_kernel<8><<<grid, block, 0, s>>>(logits, T, E, K, topk_idx, gates); break;
+        MOE_ROUTE_CASE(1)
+        MOE_ROUTE_CASE(2)
+        MOE_ROUTE_CASE(3)
+        MOE_ROUTE_CASE(4)
+        MOE_ROUTE_CASE(5)
+        MOE_ROUTE_CASE(6)
+        MOE_ROUTE_CASE(7)
+        default: MOE_ROUTE_CASE(8)
     }
+#undef MOE_ROUTE_CASE
     return moe_host::launch_status();
 }
 
@@ -198,10 +356,17 @@ extern "C" int moe_route_backward(const int32_t* topk_idx, const float* gates, c
     if (moe_host::misaligned(topk_idx) || moe_host::misaligned(gates) || moe_host::misaligned(dgates) ||
         moe_host::misaligned(dlogits))
         return MOE_EALIGN;
-    const dim3 grid((T + 3) / 4), block(256);
     hipStream_t s = (hipStream_t)stream;
-    if (K <= 8) route_backward_kernel<8><<<grid, block, 0, s>>>(topk_idx, gates, dgates, T, E, K, dlogits);
-    else route_backward_kernel<16><<<grid, block, 0, s>>>(topk_idx, gates, dgates, T, E, K, dlogits);
+    int kp_log2 = 0;
+    while ((1 << kp_log2) < K) ++kp_log2;
+    const int tpw = std::min(kRbTok, 64 >> kp_log2);
+    const int64_t groups = ((int64_t)T + tpw - 1) / tpw;
+    // LDS: 4 waves x 8 rows x EMAX floats per workgroup (32 or 64 KiB)
+    const int per_cu = E <= 256 ? 4 : 2;
+    const int64_t blocks = std::min<int64_t>((groups + 3) / 4, (int64_t)moe_host::num_cus() * per_cu);
+    const dim3 grid((unsigned)blocks), block(256);
+    if (E <= 256) route_backward_kernel<256><<<grid, block, 0, s>>>(topk_idx, gates, dgates, T, E, K, kp_log2, dlogits);
+    else route_backward_kernel<512><<<grid, block, 0, s>>>(topk_idx, gates, dgates, T, E, K, kp_log2, dlogits);
     return moe_host::launch_status();
 }
 

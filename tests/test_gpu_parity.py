@@ -223,6 +223,46 @@ def test_route_ties_and_signed_zeros(E, K):
     assert_close("gates", bits(g), ref_g)
 
 
+def _threshold_rows(E, rng):
+    """Router scores that exercise both ways the route kernel selects: rows of distinct N(0,1) scores
+    (a few candidates above the threshold), flat rows and rows with 64 or 65 experts tied at the top
+    (64 candidates: the rank count over all ties; 65: the K rounds), and a row of signed zeros."""
+    rows = [rng.standard_normal(E).astype(np.float32) for _ in range(40)]
+    rows.append(np.full(E, 0.5, np.float32))
+    for n_top in (64, 65, E // 2, E - 1):
+        if 0 < n_top <= E:
+            r = (rng.standard_normal(E) - 5.0).astype(np.float32)
+            r[rng.permutation(E)[:n_top]] = 3.0
+            r2 = r.copy()
+            r2[:] = -3.0
+            r2[:n_top] = 3.0
+            rows += [r, r2]
+    z = np.zeros(E, np.float32)
+    z[::2] = -0.0
+    rows.append(z)
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("E,K", [(8, 8), (64, 8), (65, 1), (128, 9), (256, 8), (256, 16), (512, 8), (512, 13)])
+def test_route_threshold_and_rounds(E, K):
+    """Choices exactly the oracle's (score desc, id asc) on rows that take the threshold-and-rank path and
+    rows that take the K rounds, interleaved so that one wave meets both; gates within tolerance; a rerun
+    bitwise identical."""
+    rng = np.random.default_rng(E * 7 + K)
+    block = _threshold_rows(E, rng)
+    logits = np.concatenate([block[rng.permutation(len(block))] for _ in range(40)])
+    T = len(logits)
+    print(f"[route paths] E={E} K={K} T={T}", flush=True)
+    d = torch.from_numpy(logits).cuda()
+    idx, g = _lib.moe_route(d, K)
+    idx2, g2 = _lib.moe_route(d, K)
+    torch.cuda.synchronize()
+    ref_idx, ref_g = oracle.route(logits, K)
+    assert_equal("topk_idx", bits(idx), ref_idx)
+    assert_close("gates", bits(g), ref_g)
+    assert torch.equal(idx, idx2) and torch.equal(g.view(torch.int32), g2.view(torch.int32))
+
+
 # (T, K, local experts): the permute's three schedules.  64-token blocks with the scan done inside the
 # rank kernel (at most 256 blocks; 256 exactly for T=16384), 64-token blocks with the one-block scan
 # (313 blocks), and 256-token blocks (blocks x local experts above 8192).

@@ -121,3 +121,33 @@ def test_router_full_size_sampled(name):
     rdx, rdw = oracle.router_backward(inp["x"], inp["w_router"], dl, rows=rows, cols=cols)
     assert_close("dx", bits(dx)[rows], rdx[rows])
     assert_close("dw_r", bits(dw)[:, cols], rdw[:, cols])
+
+
+# (T, E, K): K of 1..16 (lanes per token 1, 2, 4, 8, 16; K not a power of two), E not a multiple of 4,
+# E past 256 (the larger LDS slice), T ragged against the 8- and 4-token groups and past one pass of the grid
+RB_CASES = [(1, 8, 1), (7, 8, 2), (13, 100, 3), (4099, 256, 8), (1001, 257, 5), (333, 320, 16), (2050, 512, 13),
+            (65537, 128, 8), (9, 7, 4), (300000, 64, 2)]
+
+
+@pytest.mark.parametrize("T,E,K", RB_CASES)
+def test_route_backward_shapes(T, E, K):
+    """dlogits from distinct top-K experts, gates and gate gradients against the oracle: zeros exactly where no
+    expert was chosen, the chosen entries within tolerance; a rerun is bitwise identical."""
+    print(f"[route_backward] T={T} E={E} K={K}", flush=True)
+    rng = np.random.default_rng(T * 7 + E * 3 + K)
+    idx = np.argsort(rng.random((T, E)), axis=1)[:, :K].astype(np.int32)
+    g = rng.random((T, K)).astype(np.float32)
+    g /= g.sum(axis=1, keepdims=True)
+    dg = rng.standard_normal((T, K)).astype(np.float32)
+    d_idx, d_g, d_dg = (torch.from_numpy(a).cuda() for a in (idx, g, dg))
+    dl = _lib.moe_route_backward(d_idx, d_g, d_dg, E)
+    torch.cuda.synchronize()
+    got = dl.cpu().numpy()
+    ref = oracle.route_backward(idx, g, dg, E)
+    chosen = np.zeros((T, E), bool)
+    np.put_along_axis(chosen, idx, True, axis=1)
+    assert np.all(got[~chosen] == 0.0), "non-zero score gradient at an expert that was not chosen"
+    assert_close("dlogits", got, ref)
+    again = _lib.moe_route_backward(d_idx, d_g, d_dg, E)
+    torch.cuda.synchronize()
+    assert np.array_equal(again.cpu().numpy().view(np.uint32), got.view(np.uint32))
