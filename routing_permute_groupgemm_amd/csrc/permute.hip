@@ -17,9 +17,12 @@
 //  1. count:   per block of TB tokens, an LDS histogram of local experts
 //              (integer adds commute, so the result has no order dependence);
 //              written expert-major to the workspace: ws[j*nblk + b].
-//  2. scan:    one block scans ws in place (exclusive, expert-major), so
-//              ws[j*nblk+b] becomes the first row of expert j owned by block b;
-//              also writes counts, offsets and the overflow status.
+//  2. scan:    one block per expert scans its row of ws in place
+//              (exclusive), so ws[j*nblk+b] becomes the rows of expert j owned
+//              by the blocks before b, and writes the expert's total to
+//              counts[j]; the rank blocks add the experts' offsets (a prefix
+//              over counts), and the first of them writes offsets and the
+//              overflow status.
 //  3. rank:    each block ranks its pairs inside each expert with wave
 //              ballots (a match of equal expert ids, then a popcount of the
 //              lower lanes) and per-wave running counters in LDS, processed
@@ -81,60 +84,50 @@ __device__ __forceinline__ int block_inclusive_scan_1024(int v, int* sh_wave /*[
     return v + add;
 }
 
-__global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t* __restrict__ ws, int e_local, int nblk,
-                                                         int64_t cap_rows, int32_t* __restrict__ counts,
-                                                         int32_t* __restrict__ offsets,
-                                                         int32_t* __restrict__ status) {
+// Step 2 when the rank kernel does not scan: block j scans row j of the
+// count matrix (expert j's counts over the token blocks) in place, exclusive,
+// and writes the row total to counts[j].  The experts' offsets (a prefix over
+// these totals) are then formed by each rank block from counts.
+__global__ __launch_bounds__(1024) void perm_rowscan_kernel(int32_t* __restrict__ ws, int nblk,
+                                                            int32_t* __restrict__ counts) {
     __shared__ int sh_wave[16];
     __shared__ int sh_carry;
-    const int64_t n = (int64_t)e_local * nblk;
-    if (n == 0) {  // no tokens or no local experts: every count and offset is 0
-        for (int j = threadIdx.x; j <= e_local; j += 1024) {
-            offsets[j] = 0;
-            if (j < e_local) counts[j] = 0;
-        }
-        if (threadIdx.x == 0) status[0] = 0;
-        return;
-    }
+    int32_t* row = ws + (int64_t)blockIdx.x * nblk;
     if (threadIdx.x == 0) sh_carry = 0;
     __syncthreads();
     // chunks of 1024*ITEMS, each thread owns ITEMS consecutive entries
-    constexpr int ITEMS = 8;
-    for (int64_t base = 0; base < n; base += 1024 * ITEMS) {
+    constexpr int ITEMS = 4;
+    for (int base = 0; base < nblk; base += 1024 * ITEMS) {
         int vals[ITEMS];
         int sum = 0;
-        const int64_t my0 = base + (int64_t)threadIdx.x * ITEMS;
+        const int my0 = base + threadIdx.x * ITEMS;
 #pragma unroll
         for (int i = 0; i < ITEMS; ++i) {
-            vals[i] = (my0 + i < n) ? ws[my0 + i] : 0;
+            vals[i] = my0 + i < nblk ? row[my0 + i] : 0;
             sum += vals[i];
         }
-        int incl = block_inclusive_scan_1024(sum, sh_wave);
+        const int incl = block_inclusive_scan_1024(sum, sh_wave);
         int run = sh_carry + incl - sum;
 #pragma unroll
         for (int i = 0; i < ITEMS; ++i) {
-            if (my0 + i < n) {
-                ws[my0 + i] = run;
-                // the first block of expert j holds offsets[j]
-                int64_t q = my0 + i;
-                if (q % nblk == 0) offsets[q / nblk] = run;
-            }
+            if (my0 + i < nblk) row[my0 + i] = run;
             run += vals[i];
         }
         __syncthreads();
         if (threadIdx.x == 1023) sh_carry = run;
         __syncthreads();
     }
-    const int total = sh_carry;
-    if (threadIdx.x == 0) {
-        offsets[e_local] = total;
-        status[0] = (int64_t)total > cap_rows ? 1 : 0;
+    if (threadIdx.x == 0) counts[blockIdx.x] = sh_carry;
+}
+
+// No pairs to place (no tokens or no local experts): every count and offset is 0.
+__global__ void perm_empty_kernel(int e_local, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                  int32_t* __restrict__ status) {
+    for (int j = threadIdx.x; j <= e_local; j += blockDim.x) {
+        offsets[j] = 0;
+        if (j < e_local) counts[j] = 0;
     }
-    __syncthreads();
-    for (int j = threadIdx.x; j < e_local; j += 1024) {
-        int hi = (j + 1 < e_local) ? ws[(int64_t)(j + 1) * nblk] : total;
-        counts[j] = hi - ws[(int64_t)j * nblk];
-    }
+    if (threadIdx.x == 0) status[0] = 0;
 }
 
 // Lanes whose key equals this lane's key (keys < 2^nbits; inactive lanes excluded).
@@ -154,11 +147,12 @@ __device__ __forceinline__ uint64_t match_key(int key, bool active, int nbits) {
 constexpr int kFusedScanBlocks = 256;
 
 // KMAX: an upper bound of the rounds of 64 pairs per wave (tb/4 tokens * K pairs).
-// FUSED: ws holds the raw per-(expert, block) counts and every block derives
-// its own first row per expert from them (the expert's offset, an exclusive
-// scan of the totals over experts, plus the counts of the blocks before it);
-// block 0 also writes counts, offsets and status.  Otherwise ws holds those
-// first rows already (the scan kernel's output).
+// Every block derives its own first row per expert: the expert's offset (an
+// exclusive scan of the expert totals) plus the counts of the token blocks
+// before it.  FUSED: ws holds the raw per-(expert, block) counts and the
+// block adds them up itself, and block 0 also writes counts.  Otherwise the
+// rows of ws are already scanned per expert and counts holds the totals
+// (perm_rowscan_kernel's output).  Block 0 writes offsets and status.
 template <int KMAX, bool FUSED>
 __global__ __launch_bounds__(256) void perm_rank_kernel(const int32_t* __restrict__ idx, int T, int K,
                                                         int e_begin, int e_local, int nbits, int nblk, int tb,
@@ -167,23 +161,30 @@ __global__ __launch_bounds__(256) void perm_rank_kernel(const int32_t* __restric
                                                         int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                         int32_t* __restrict__ status) {
     __shared__ int cnt[4][kMaxLocal];
-    __shared__ int s_base[FUSED ? kMaxLocal : 1];   // FUSED: this block's first row per expert
-    __shared__ int s_tot[FUSED ? kMaxLocal : 1];
+    __shared__ int s_base[kMaxLocal];  // this block's first row per expert
+    __shared__ int s_tot[kMaxLocal];
     __shared__ int s_wsum[4];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     for (int j = lane; j < e_local; j += 64) cnt[wave][j] = 0;
-    if constexpr (FUSED) {
-        for (int j = threadIdx.x; j < e_local; j += 256) s_base[j] = s_tot[j] = 0;
-        __syncthreads();
-        // per expert: the total over all blocks and the part before this block
-        // (integer adds, so the order of the LDS atomics does not matter)
-        const int64_t n = (int64_t)e_local * nblk;
-        for (int64_t q = threadIdx.x; q < n; q += 256) {
-            const int c = ws[q];
-            const int j = (int)(q / nblk), b = (int)(q - (int64_t)j * nblk);
-            if (c) {
-                atomicAdd(&s_tot[j], c);
-                if (b < (int)blockIdx.x) atomicAdd(&s_base[j], c);
+    {
+        if constexpr (FUSED) {
+            for (int j = threadIdx.x; j < e_local; j += 256) s_base[j] = s_tot[j] = 0;
+            __syncthreads();
+            // per expert: the total over all blocks and the part before this block
+            // (integer adds, so the order of the LDS atomics does not matter)
+            const int64_t n = (int64_t)e_local * nblk;
+            for (int64_t q = threadIdx.x; q < n; q += 256) {
+                const int c = ws[q];
+                const int j = (int)(q / nblk), b = (int)(q - (int64_t)j * nblk);
+                if (c) {
+                    atomicAdd(&s_tot[j], c);
+                    if (b < (int)blockIdx.x) atomicAdd(&s_base[j], c);
+                }
+            }
+        } else {
+            for (int j = threadIdx.x; j < e_local; j += 256) {
+                s_tot[j] = counts[j];
+                s_base[j] = ws[(int64_t)j * nblk + blockIdx.x];
             }
         }
         __syncthreads();
@@ -205,11 +206,11 @@ __global__ __launch_bounds__(256) void perm_rank_kernel(const int32_t* __restric
         if (j0 + 1 < e_local) s_base[j0 + 1] += off0 + t0;
         if (blockIdx.x == 0) {
             if (j0 < e_local) {
-                counts[j0] = t0;
+                if (FUSED) counts[j0] = t0;
                 offsets[j0] = off0;
             }
             if (j0 + 1 < e_local) {
-                counts[j0 + 1] = t1;
+                if (FUSED) counts[j0 + 1] = t1;
                 offsets[j0 + 1] = off0 + t0;
             }
             if (threadIdx.x == 0) {
@@ -267,7 +268,7 @@ __global__ __launch_bounds__(256) void perm_rank_kernel(const int32_t* __restric
                 int j = jj[it];
                 int row = -1;
                 if (j >= 0) {
-                    const int first = FUSED ? s_base[j] : ws[(int64_t)j * nblk + blockIdx.x];
+                    const int first = s_base[j];
                     int64_t r = (int64_t)first + cnt[wave][j] + rk[it];
                     if (r < cap_rows) {
                         row = (int)r;
@@ -364,7 +365,11 @@ static int permute_launch(const int32_t* topk_idx, int T, int K, int e_begin, in
     const bool fused = tb == 64 && nblk > 0 && nblk <= kFusedScanBlocks;
     if (nblk > 0 && e_local > 0)
         perm_count_kernel<<<nblk, 256, 0, s>>>(topk_idx, T, K, e_begin, e_local, nblk, tb, w);
-    if (!fused) perm_scan_kernel<<<1, 1024, 0, s>>>(w, e_local, nblk, cap_rows, counts, offsets, status);
+    if (nblk == 0 || e_local == 0) {
+        perm_empty_kernel<<<1, 256, 0, s>>>(e_local, counts, offsets, status);
+    } else if (!fused) {
+        perm_rowscan_kernel<<<e_local, 1024, 0, s>>>(w, nblk, counts);
+    }
     if (nblk > 0) {
 #define MOE_RANK(KM, FU)                                                                                    \
     perm_rank_kernel<KM, FU><<<nblk, 256, 0, s>>>(topk_idx, T, K, e_begin, e_local, nbits, nblk, tb, w, cap_rows, \

@@ -263,10 +263,12 @@ def test_route_threshold_and_rounds(E, K):
     assert torch.equal(idx, idx2) and torch.equal(g.view(torch.int32), g2.view(torch.int32))
 
 
-# (T, K, local experts): the permute's three schedules.  64-token blocks with the scan done inside the
-# rank kernel (at most 256 blocks; 256 exactly for T=16384), 64-token blocks with the one-block scan
-# (313 blocks), and 256-token blocks (blocks x local experts above 8192).
-@pytest.mark.parametrize("T,K,EL", [(8192, 8, 40), (8193, 8, 40), (16384, 4, 16), (20000, 4, 16), (20000, 4, 40)])
+# (T, K, local experts): the permute's schedules.  64-token blocks with the scan done inside the rank
+# kernel (at most 256 blocks; 256 exactly for T=16384), 64-token blocks with the per-expert row scan
+# (313 blocks), and 256-token blocks (blocks x local experts above 8192) with the row scan, up to
+# 782 blocks per expert.
+@pytest.mark.parametrize("T,K,EL", [(8192, 8, 40), (8193, 8, 40), (16384, 4, 16), (20000, 4, 16), (20000, 4, 40),
+                                    (131072, 2, 32), (200000, 2, 40)])
 def test_permute_local_share_and_capacity(T, K, EL):
     """A local share (experts 8.. of 64) at several thousand tokens: counts, offsets, pos, src and
     x_perm exactly as the oracle's, with the expected capacity and with half of it (rows dropped)."""
