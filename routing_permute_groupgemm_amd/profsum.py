@@ -14,7 +14,8 @@ Two subcommands, both run on the host after the profiled bench run:
 Dispatches are labelled by kernel name; the GroupGEMM template's layout / epilogue / schedule
 arguments name its step.  The two weight-gradient launches of a step share one template
 instance and are told apart by their order inside the step (dW_gate|dW_up first, dW_down second).
-A step starts at each router top-k dispatch.
+A step starts at each router top-k dispatch, or (in traces filtered to the GroupGEMMs) at the
+second launch of the router projection or of the gate/up GroupGEMM since the last start.
 """
 from __future__ import annotations
 
@@ -28,41 +29,46 @@ import sys
 
 REPO = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
-# (layout, epilogue, schedule) template arguments of the GroupGEMM -> step
-GG_STEPS = {(1, 1, 0): "expert_up", (1, 0, 0): "expert_down", (0, 2, 0): "bwd_down_dgrad",
-            (0, 0, 0): "bwd_up_dgrad", (1, 3, 0): "router_fwd"}
-WGRAD_ORDER = ("wgrad_gate_up", "wgrad_down")
-OTHER = [("route_kernel", "route"), ("perm_count_kernel", "permute (count)"), ("perm_scan_kernel", "permute (scan)"),
+# (layout, epilogue, schedule) template arguments of the GroupGEMM -> the steps that launch that
+# instance, in their order inside a layer step
+GG_STEPS = {(1, 1, 0): ("expert_up",), (1, 0, 0): ("expert_down",), (0, 2, 0): ("bwd_down_dgrad",),
+            (0, 0, 0): ("bwd_up_dgrad", "router_bwd (dx)"), (1, 3, 0): ("router_fwd",),
+            (1, 3, 1): ("wgrad_gate_up", "wgrad_down", "router_bwd (dW_r)")}
+OTHER = [("route_kernel", "route"), ("perm_count_kernel", "permute (count)"), ("perm_rowscan_kernel", "permute (scan)"),
+         ("perm_empty_kernel", "permute (no pairs)"),
          ("perm_rank_kernel", "permute (rank)"), ("perm_copy_kernel", "permute (row copy)"),
          ("gather_kernel", "bwd_gather"), ("route_backward_kernel", "route_bwd"),
          ("combine_kernel<true", "combine"), ("combine_kernel<false", "bwd_combine"),
          ("mfma16_probe_kernel", "MFMA probe 16x16x32 (after the timed steps)"),
          ("mfma_probe_kernel", "MFMA probe 32x32x16 (after the timed steps)"),
          ("split_offsets_kernel", "wgrad split (offsets)"), ("sum_split_kernel", "wgrad split (sum)"),
+         ("cast_bf16_kernel", "router_bwd (cast)"), ("sum_partials_kernel", "router_bwd (dW_r sum)"),
          ("copyBuffer", "runtime copy"), ("at::native", "torch (input set-up)")]
 STEP_ORDER = ["router_fwd", "route", "permute (count)", "permute (scan)", "permute (rank)", "permute (row copy)",
               "expert_up", "expert_down", "combine", "bwd_gather", "route_bwd", "bwd_down_dgrad", "bwd_up_dgrad",
-              "bwd_combine", "wgrad_gate_up", "wgrad_down"]
+              "bwd_combine", "wgrad_gate_up", "wgrad_down", "router_bwd (cast)", "router_bwd (dx)",
+              "router_bwd (dW_r)", "router_bwd (dW_r sum)"]
 GG_RE = re.compile(r"gg_kernel<(\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (\w+)>")
 
 
 def label_dispatches(rows):
     """rows: dicts with Dispatch_Id and Kernel_Name.  Returns {dispatch id: step label}."""
     out = {}
-    wg_in_step = 0
+    seen = collections.Counter()  # GroupGEMM instances launched so far in this layer step
     for r in sorted(rows, key=lambda r: int(r["Dispatch_Id"])):
         name, d = r["Kernel_Name"], int(r["Dispatch_Id"])
         if "route_kernel" in name:
-            wg_in_step = 0
+            seen.clear()
         m = GG_RE.search(name)
         if m:
             key = (int(m.group(6)), int(m.group(7)), int(m.group(8)))
-            if key == (1, 3, 1):
-                out[d] = WGRAD_ORDER[wg_in_step] if wg_in_step < len(WGRAD_ORDER) else "wgrad (outside a step)"
-                wg_in_step += 1
-            else:
-                step = GG_STEPS.get(key, "GroupGEMM " + m.group(0))
-                out[d] = step + (" (gathered rows)" if m.group(11) == "true" else "")
+            if key in ((1, 3, 0), (1, 1, 0)) and seen[key]:
+                seen.clear()  # a new step (traces filtered to the GroupGEMMs have no route dispatch)
+            steps = GG_STEPS.get(key, ("GroupGEMM " + m.group(0),))
+            i = seen[key]
+            seen[key] += 1
+            step = steps[i] if i < len(steps) else steps[-1] + " (extra launch)"
+            out[d] = step + (" (gathered rows)" if m.group(11) == "true" else "")
             continue
         for pat, lab in OTHER:
             if pat in name:
@@ -198,7 +204,9 @@ def cmd_counters(a):
             durs[k].append(cs.pop("_dur"))
             res[k].update(cs)
             ndisp[k] = n[k]
-    gemms = [s for s in STEP_ORDER if s in res and s in work and work[s]["flops"]]
+    base = lambda lab: lab.replace(" (gathered rows)", "")  # noqa: E731  the step a label belongs to
+    order = {n: i for i, n in enumerate(STEP_ORDER)}
+    gemms = sorted((s for s in res if base(s) in work and work[base(s)]["flops"]), key=lambda s: order.get(base(s), 99))
     L = [f"# Counters of the GroupGEMMs, {wl}\n",
          f"One rocprofv3 counter run per group (MI355X, ROCm 7.2), every GroupGEMM dispatch of the run:\n",
          f"`{a.command}`\n", "with `<group>` one of:\n"]
@@ -226,7 +234,7 @@ def cmd_counters(a):
         mf = c["SQ_INSTS_MFMA"]
         rd = c["FETCH_SIZE"] * 1024 / ff / 1e9
         wr = c["WRITE_SIZE"] * 1024 / wf / 1e9
-        alg = work[s]["bytes"] / 1e9
+        alg = work[base(s)]["bytes"] / 1e9
         L.append(f"| {s} | {ndisp[s]} | {dur * 1e6:.0f} | {gui / dur / 1e9:.2f} | "
                  f"{c['SQ_VALU_MFMA_BUSY_CYCLES'] / (gui * 1024):.3f} | {c['SQ_WAIT_INST_ANY'] / c['SQ_WAVE_CYCLES']:.3f} | "
                  f"{c['SQ_WAIT_INST_LDS'] / c['SQ_WAVE_CYCLES']:.3f} | {c['SQ_INSTS_SALU'] / mf:.2f} | "
@@ -234,7 +242,7 @@ def cmd_counters(a):
                  f"{c['TCC_HIT_sum'] / (c['TCC_HIT_sum'] + c['TCC_MISS_sum']):.3f} | "
                  f"{c['SQ_LDS_BANK_CONFLICT'] / max(c['SQ_LDS_IDX_ACTIVE'], 1):.3f} | {rd:.2f} | {wr:.2f} | "
                  f"{alg:.2f} | {(rd + wr) / alg:.2f} |")
-        traffic[f"{s}@{wl}"] = dict(gemm_src_sha=sha, traffic_bytes_per_launch=int((rd + wr) * 1e9),
+        traffic[f"{base(s)}@{wl}"] = dict(gemm_src_sha=sha, traffic_bytes_per_launch=int((rd + wr) * 1e9),
                                     fetch_kib=round(c["FETCH_SIZE"], 1), write_kib=round(c["WRITE_SIZE"], 1),
                                     fetch_factor=round(ff, 6), write_factor=round(wf, 6), dispatches=ndisp[s])
     L.append("\nRaw means per dispatch:\n")
