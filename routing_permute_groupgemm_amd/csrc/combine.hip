@@ -70,7 +70,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4* __restrict__ 
                                                       const float* __restrict__ gates, int T, int K, int H,
                                                       u32x4* __restrict__ out) {
     const int lane = threadIdx.x & 63;
-    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t t = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (t >= T) return;
     const int my_pos = lane < K ? pos[t * K + lane] : -1;
     float my_g = 1.0f;
@@ -168,7 +168,7 @@ __global__ __launch_bounds__(256) void gather_kernel(const u32x4* __restrict__ d
                                                      int T, int K, int H, u32x4* __restrict__ dy_perm,
                                                      float* __restrict__ dgates) {
     const int lane = threadIdx.x & 63;
-    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t t = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (t >= T) return;
     const int my_pos = lane < K ? pos[t * K + lane] : -1;
     float my_g = 1.0f;

@@ -287,7 +287,7 @@ __global__ __launch_bounds__(256) void perm_copy_kernel(const u32x4* __restrict_
                                                         const int32_t* __restrict__ pos,
                                                         u32x4* __restrict__ x_perm) {
     const int lane = threadIdx.x & 63;
-    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t t = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (t >= T) return;
     const int my_pos = lane < K ? pos[t * K + lane] : -1;
     if (__ballot(my_pos >= 0) == 0ull) return;  // no local pair

@@ -21,6 +21,8 @@
 
 namespace moe {
 
+typedef __attribute__((ext_vector_type(2))) unsigned long long u64x2;
+
 __device__ __forceinline__ uint32_t score_key(float s) {
     // -0 and +0 compare equal: s + 0 is +0 for both (and s for every other s)
     const uint32_t u = __float_as_uint(s + 0.0f);
@@ -121,10 +123,11 @@ template <int EPL, bool FULL>
 __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int T, int E, int K,
                                                     int kp_log2, int32_t* __restrict__ topk_idx,
                                                     float* __restrict__ gates) {
-    __shared__ uint64_t s_cand[4][64];
+    __shared__ __attribute__((aligned(16))) uint64_t s_cand[4][72];  // 64 candidates and 8 zero words
     __shared__ int s_bid[4][64];    // batch: chosen expert id, slot KP*token + rank
     __shared__ float s_bsc[4][64];  // batch: chosen score - s_max, then exp of it
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar loop control
     const int tb_n = 64 >> kp_log2;  // tokens per batch
     const int64_t n_batches = ((int64_t)T + tb_n - 1) / tb_n;
     const int64_t stride = (int64_t)gridDim.x * 4;
@@ -188,10 +191,19 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
                     }
                     off += __popcll(cm[i]);
                 }
+                // zeros past the last candidate: they rank below every key, so
+                // the count below runs over whole groups of 8 words
+                if (lane < 8) *(MOE_LDS uint64_t*)(cand + n + lane) = 0ull;
                 asm volatile("" ::: "memory");  // a wave's LDS accesses execute in order
                 const uint64_t v = lane < n ? *(const MOE_LDS uint64_t*)(cand + lane) : 0ull;
                 int r = 0;
-                for (int j = 0; j < n; ++j) r += *(const MOE_LDS uint64_t*)(cand + j) > v;
+                for (int j0 = 0; j0 < n; j0 += 8) {
+                    u64x2 c[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) c[q] = *(const MOE_LDS u64x2*)(cand + j0 + 2 * q);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) r += (int)(c[q][0] > v) + (int)(c[q][1] > v);
+                }
                 if (lane < n) rank = r;
                 const int top = __builtin_ctzll(__ballot(rank == 0));
                 s_max = key_score((uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), top));
@@ -248,7 +260,8 @@ __global__ __launch_bounds__(256) void route_backward_kernel(const int32_t* __re
                                                              const float* __restrict__ dgates, int T, int E, int K,
                                                              int kp_log2, float* __restrict__ dlogits) {
     __shared__ __attribute__((aligned(16))) float s_rows[4][kRbTok * EMAX];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar loop control
     float* rows = s_rows[wave];
     const int KP = 1 << kp_log2;
     const int tpw = min(kRbTok, 64 >> kp_log2);  // tokens per group
