@@ -59,6 +59,9 @@ constexpr int kLdsBudget = 128 * 1024;  // LDS per workgroup for the stage ring
 #ifndef MOE_GEMM_MFMA16
 #define MOE_GEMM_MFMA16 1  // the down dgrad's 256 x 256 body computes with 16x16x32 MFMAs (0: 32x32x16)
 #endif
+#ifndef MOE_GEMM_MFMA16_WGRAD
+#define MOE_GEMM_MFMA16_WGRAD 0  // 1: the weight gradient's too (measured 5% slower, so off)
+#endif
 
 enum : int { LAY_KC = 0, LAY_MN = 1 };
 enum : int { EPI_BF16 = 0, EPI_SWIGLU = 1, EPI_SWIGLU_BWD = 2, EPI_F32 = 3 };
@@ -305,9 +308,13 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
     // 32x32x16, although back-to-back 16x16x32 MFMAs on random operands reach
     // 14% more flops on this chip: their time is set by the loads, not the
     // MFMA rate.  The smaller bodies keep 32x32x16, whose 32-row blocks their
-    // idle-row scheme is built on.
-    constexpr bool kMf16 = MOE_GEMM_MFMA16 && EPI == EPI_SWIGLU_BWD && BM == 256 && BN == 256 && WM == 2 &&
-                           WN == 2 && BK == 32;
+    // idle-row scheme is built on.  The weight gradient can use the same body
+    // (MOE_GEMM_MFMA16_WGRAD=1: MN-layout A fragments, and each lane stores its
+    // 16 bytes of fp32 dW straight from the accumulators); it ran 5% slower
+    // than its 32x32x16 body, whose staged epilogue stores whole lines.
+    constexpr bool kMf16 = ((MOE_GEMM_MFMA16 && EPI == EPI_SWIGLU_BWD && SCHED == SCHED_ROWS) ||
+                            (MOE_GEMM_MFMA16_WGRAD && EPI == EPI_F32 && SCHED == SCHED_WGRAD)) &&
+                           BM == 256 && BN == 256 && WM == 2 && WN == 2 && BK == 32;
     constexpr int MB16 = kMf16 ? BM / WM / 16 : 1;  // 16-row blocks per wave
     constexpr int NB16 = kMf16 ? BN / WN / 16 : 1;  // 16-column blocks per wave
 
@@ -799,7 +806,10 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
             // 16-column block n
             auto row16 = [&](int m) { return wm * (BM / WM) + 16 * m; };
             auto col16 = [&](int n) { return wn * (BN / WN) + 16 * n; };
-            auto frag_a = [&](int slot, int m) { return LY::frag_kc16(smem + slot * TL::kStage, row16(m), lane); };
+            auto frag_a = [&](int slot, int m) {
+                const uint8_t* sA = smem + slot * TL::kStage;
+                return SCHED == SCHED_ROWS ? LY::frag_kc16(sA, row16(m), lane) : LY::frag_mn16(sA, row16(m), lane);
+            };
             auto frag_b = [&](int slot, int n) {
                 const uint8_t* sB = smem + slot * TL::kStage + TL::kABytes;
                 return LB == LAY_KC ? LY::frag_kc16(sB, col16(n), lane) : LY::frag_mn16(sB, col16(n), lane);
@@ -867,8 +877,29 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
             }
 
             // ---- epilogue: lane holds row l%16 and columns 4*(l/16) + 0..3 of each 16 x 16 block ----
-            static_assert(EPI == EPI_SWIGLU_BWD && SCHED == SCHED_ROWS, "16x16x32 body: the down dgrad only");
-            {  // the accumulators are dh
+            if constexpr (SCHED == SCHED_WGRAD) {
+                // fp32 dW: each lane stores its 4 columns of a row (16 bytes); a
+                // store instruction covers 64 bytes of each of 16 rows, and L2
+                // merges the pieces of a line before it writes it back
+                const int cq = 4 * (lane >> 4);
+#pragma unroll
+                for (int m = 0; m < MB16; ++m) {
+                    const int mrow = mi_w * BM + row16(m) + (lane & 15);
+                    if (mrow >= p.M) continue;
+#pragma unroll
+                    for (int nb = 0; nb < NB16; ++nb) {
+                        const int n = ni * BN + col16(nb) + cq;
+                        if (n >= p.N) continue;
+                        const bool second = n >= p.n_split;
+                        float* base = second ? p.cf2 : p.cf;
+                        const int nn = second ? n - p.n_split : n;
+                        *(f32x4*)(base + ((int64_t)j * p.M + mrow) * p.n_split + nn) = acc16[m][nb];
+                    }
+                }
+                continue;
+            }
+            static_assert(EPI == EPI_SWIGLU_BWD || SCHED == SCHED_WGRAD, "16x16x32 body: the down dgrad or dW");
+            if constexpr (EPI == EPI_SWIGLU_BWD) {  // the accumulators are dh
                 const int cq = 4 * (lane >> 4);
 #pragma unroll
                 for (int mp = 0; mp < MB16 / 2; ++mp) {
