@@ -1,6 +1,6 @@
 """Turn rocprofv3 CSV output of a bench.py run into the short text summaries kept beside the code.
 
-Two subcommands, both run on the host after the profiled bench run:
+Three subcommands, all run on the host after the profiled bench run:
 
   stats     <dir>/<name>_kernel_trace.csv and _kernel_stats.csv of a `--kernel-trace --stats` run
             -> a markdown table of per-step kernel time (every dispatch is labelled with the layer
@@ -10,12 +10,14 @@ Two subcommands, both run on the host after the profiled bench run:
             -> a markdown table of derived counter figures per GroupGEMM, and the HBM bytes per
                launch of each GroupGEMM merged into a JSON file that bench.py reads for its
                roofline's traffic figure
+  kernels   <run dir>/p_counter_collection.csv of one `--pmc` run per counter group
+            -> a markdown table of instruction counts and waits per kernel name
 
 Dispatches are labelled by kernel name; the GroupGEMM template's layout / epilogue / schedule
 arguments name its step.  The two weight-gradient launches of a step share one template
 instance and are told apart by their order inside the step (dW_gate|dW_up first, dW_down second).
-A step starts at each router top-k dispatch, or (in traces filtered to the GroupGEMMs) at the
-second launch of the router projection or of the gate/up GroupGEMM since the last start.
+A step starts at each router top-k dispatch and at each router projection, or (in traces filtered
+to the GroupGEMMs) at the second launch of the gate/up GroupGEMM since the last start.
 """
 from __future__ import annotations
 
@@ -32,8 +34,9 @@ REPO = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 # (layout, epilogue, schedule) template arguments of the GroupGEMM -> the steps that launch that
 # instance, in their order inside a layer step
 GG_STEPS = {(1, 1, 0): ("expert_up",), (1, 0, 0): ("expert_down",), (0, 2, 0): ("bwd_down_dgrad",),
-            (0, 0, 0): ("bwd_up_dgrad", "router_bwd (dx)"), (1, 3, 0): ("router_fwd",),
-            (1, 3, 1): ("wgrad_gate_up", "wgrad_down", "router_bwd (dW_r)")}
+            (0, 0, 0): ("bwd_up_dgrad",), (1, 3, 0): ("router_fwd",), (1, 3, 1): ("wgrad_gate_up", "wgrad_down")}
+# the router's backward launches the same instances once more, after the layer's own launches
+GG_ROUTER = {(0, 0, 0): "router_bwd (dx)", (1, 3, 1): "router_bwd (dW_r)"}
 OTHER = [("route_kernel", "route"), ("perm_count_kernel", "permute (count)"), ("perm_rowscan_kernel", "permute (scan)"),
          ("perm_empty_kernel", "permute (no pairs)"),
          ("perm_rank_kernel", "permute (rank)"), ("perm_copy_kernel", "permute (row copy)"),
@@ -55,16 +58,24 @@ def label_dispatches(rows):
     """rows: dicts with Dispatch_Id and Kernel_Name.  Returns {dispatch id: step label}."""
     out = {}
     seen = collections.Counter()  # GroupGEMM instances launched so far in this layer step
+    has_router = router_pending = False
     for r in sorted(rows, key=lambda r: int(r["Dispatch_Id"])):
         name, d = r["Kernel_Name"], int(r["Dispatch_Id"])
         if "route_kernel" in name:
+            has_router, router_pending = router_pending, False
             seen.clear()
         m = GG_RE.search(name)
         if m:
             key = (int(m.group(6)), int(m.group(7)), int(m.group(8)))
-            if key in ((1, 3, 0), (1, 1, 0)) and seen[key]:
+            if key == (1, 3, 0):  # the router projection opens a step
+                seen.clear()
+                has_router = router_pending = True
+            elif key == (1, 1, 0) and seen[key]:
                 seen.clear()  # a new step (traces filtered to the GroupGEMMs have no route dispatch)
+                has_router = False
             steps = GG_STEPS.get(key, ("GroupGEMM " + m.group(0),))
+            if has_router and key in GG_ROUTER:
+                steps = steps + (GG_ROUTER[key],)
             i = seen[key]
             seen[key] += 1
             step = steps[i] if i < len(steps) else steps[-1] + " (extra launch)"
@@ -106,8 +117,20 @@ def work_of(bj):
                                   c["dispatch"] == "zero-copy", c.get("router_projection", False)), bench.src_hash()
 
 
+def headline_part(trace):
+    """The dispatches of the bench's headline workload: those before its first MFMA probe (the bench
+    measures the probes' rate after the headline's steps, then runs any other workloads)."""
+    trace = sorted(trace, key=lambda r: int(r["Dispatch_Id"]))
+    for i, r in enumerate(trace):
+        if "probe_kernel" in r["Kernel_Name"]:
+            return trace[:i]
+    return trace
+
+
 def cmd_stats(a):
     trace = list(csv.DictReader(open(os.path.join(a.dir, f"{a.name}_kernel_trace.csv"))))
+    if a.headline_only:
+        trace = headline_part(trace)
     labels = label_dispatches(trace)
     dur = collections.defaultdict(list)
     kname = {}
@@ -121,8 +144,11 @@ def cmd_stats(a):
     L = [f"# Kernel time per step, {bj['config']['workload']}\n",
          "Command (MI355X, ROCm 7.2, from the repository root):\n",
          f"`{a.command}`\n",
-         "Every dispatch of the run labelled with the layer step it belongs to (the two weight-gradient launches "
-         "of a step share one kernel and are told apart by their order in the step). Durations in µs.\n",
+         ("The headline workload's dispatches (those before the bench's first MFMA probe), each " if a.headline_only
+          else "Every dispatch of the run, ") +
+         "labelled with the layer step it belongs to (the two weight-gradient launches of a step share one "
+         "kernel and are told apart by their order in the step; launches after the last step, such as the "
+         "bitwise-vs-non-bitwise weight-gradient timing, are marked as extra). Durations in µs.\n",
          "| step | kernel | dispatches | avg µs | min µs | max µs | share |", "|---|---|---|---|---|---|---|"]
     for s in order:
         v = dur[s]
@@ -137,7 +163,9 @@ def cmd_stats(a):
              f"{rl['frac']} of {rl['peak']}.")
     sp = os.path.join(a.dir, f"{a.name}_kernel_stats.csv")
     if os.path.exists(sp):
-        L.append("\nThe profiler's own `--stats` table (per kernel name; the weight-gradient row mixes both launches):\n")
+        L.append("\nThe profiler's own `--stats` table (per kernel name over the whole run; the weight-gradient row "
+                 "mixes both launches" + (" and the other workloads' kernels share these names" if a.headline_only
+                                          else "") + "):\n")
         L.append("| kernel | calls | avg µs | min µs | max µs | % |")
         L.append("|---|---|---|---|---|---|")
         for r in list(csv.DictReader(open(sp)))[:a.top]:
@@ -258,6 +286,50 @@ def cmd_counters(a):
     print("\n".join(L[:20 + len(gemms)]))
 
 
+def cmd_kernels(a):
+    """Counter means per dispatch of every kernel in one or more counter runs, by kernel name."""
+    res = collections.defaultdict(dict)
+    durs = collections.defaultdict(list)
+    for d in a.runs:
+        per = collections.defaultdict(lambda: collections.defaultdict(float))
+        kn, dur = {}, {}
+        for r in csv.DictReader(open(os.path.join(d, "p_counter_collection.csv"))):
+            i = r["Dispatch_Id"]
+            per[i][r["Counter_Name"]] += float(r["Counter_Value"])
+            kn[i] = r["Kernel_Name"].split("(")[0].replace("void ", "")
+            dur[i] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3
+        agg = collections.defaultdict(lambda: collections.defaultdict(list))
+        for i, cs in per.items():
+            for c, v in cs.items():
+                agg[kn[i]][c].append(v)
+            durs[kn[i]].append(dur[i])
+        for k, cs in agg.items():
+            for c, v in cs.items():
+                res[k][c] = sum(v) / len(v)
+    L = [f"# {a.title}\n", "One rocprofv3 counter run per group (MI355X, ROCm 7.2):\n", f"`{a.command}`\n",
+         "with `<group>` one of:\n"]
+    L += [f"{i + 1}. `{g}`" for i, g in enumerate(a.groups)]
+    L.append(f"\nMeans per dispatch; per-unit figures divide by {a.per_name} = {a.per}. VALU busy = "
+             "4·`SQ_ACTIVE_INST_VALU` / (1024 SIMDs × `GRBM_GUI_ACTIVE`/8), the share of the SIMDs' cycles "
+             "spent issuing VALU instructions (a wave64 VALU instruction takes 4 cycles; `GRBM_GUI_ACTIVE` also "
+             "counts the cycles around a short dispatch, so this under-states it for short kernels).\n")
+    L.append(f"| kernel | µs | VALU / {a.per_name} | SALU / {a.per_name} | LDS / {a.per_name} | VALU busy | "
+             "wait share (`SQ_WAIT_INST_ANY` / `SQ_WAVE_CYCLES`) |")
+    L.append("|---|---|---|---|---|---|---|")
+    for k, c in res.items():
+        gui = c.get("GRBM_GUI_ACTIVE", float("nan")) / 8
+        L.append(f"| `{k}` | {sum(durs[k]) / len(durs[k]):.1f} | {c['SQ_INSTS_VALU'] / a.per:.0f} | "
+                 f"{c['SQ_INSTS_SALU'] / a.per:.0f} | {c['SQ_INSTS_LDS'] / a.per:.0f} | "
+                 f"{4 * c['SQ_ACTIVE_INST_VALU'] / (1024 * gui):.2f} | "
+                 f"{c['SQ_WAIT_INST_ANY'] / c['SQ_WAVE_CYCLES']:.2f} |")
+    L += ["", "Raw means per dispatch:", "", "| counter | " + " | ".join(f"`{k}`" for k in res) + " |",
+          "|---|" + "---|" * len(res)]
+    for cn in sorted({c for v in res.values() for c in v}):
+        L.append(f"| `{cn}` | " + " | ".join(f"{res[k].get(cn, float('nan')):.4g}" for k in res) + " |")
+    open(a.out, "w").write("\n".join(L) + "\n")
+    print("\n".join(L[:12 + len(res)]))
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(prog="python -m routing_permute_groupgemm_amd.profsum")
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -268,6 +340,8 @@ def main(argv=None):
     s.add_argument("--command", required=True, help="the profiled command, quoted in the summary")
     s.add_argument("--out", required=True)
     s.add_argument("--top", type=int, default=20)
+    s.add_argument("--headline-only", action="store_true",
+                   help="summarise only the headline workload of a default bench run (dispatches before the probes)")
     c = sub.add_parser("counters")
     c.add_argument("--dir", required=True)
     c.add_argument("--tag", required=True, help="counter runs are <dir>/<tag>_p1 ... _p5")
@@ -276,8 +350,16 @@ def main(argv=None):
     c.add_argument("--calib-command", required=True)
     c.add_argument("--out", required=True)
     c.add_argument("--traffic", default=os.path.join(REPO, "profiles", "traffic.json"))
+    k = sub.add_parser("kernels")
+    k.add_argument("--runs", nargs="+", required=True, help="rocprofv3 -d directories, one per counter group")
+    k.add_argument("--groups", nargs="+", required=True, help="the counter groups, quoted, in run order")
+    k.add_argument("--per", type=float, default=1.0)
+    k.add_argument("--per-name", default="dispatch")
+    k.add_argument("--title", required=True)
+    k.add_argument("--command", required=True)
+    k.add_argument("--out", required=True)
     a = ap.parse_args(argv)
-    (cmd_stats if a.cmd == "stats" else cmd_counters)(a)
+    {"stats": cmd_stats, "counters": cmd_counters, "kernels": cmd_kernels}[a.cmd](a)
 
 
 if __name__ == "__main__":

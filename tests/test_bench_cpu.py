@@ -72,3 +72,17 @@ def test_profile_summaries_label_every_step():
     # the zero-copy gate/up GEMM keeps its step name, marked
     assert profsum.label_dispatches([dict(Dispatch_Id="1", Kernel_Name=_gg(1, 1, 0, "true"))])[1] == \
         "expert_up (gathered rows)"
+
+
+def test_profile_summaries_mark_launches_after_the_last_step():
+    """Weight-gradient launches after a step without the router (the bench's bitwise-vs-non-bitwise timing)
+    are marked as extra launches, not taken for the router's; a headline-only summary stops at the probes."""
+    from routing_permute_groupgemm_amd import profsum
+    names = ["void moe::route_kernel<4, true>(float const*)", _gg(1, 1, 0), _gg(1, 3, 1), _gg(1, 3, 1),
+             _gg(1, 3, 1), "moe::split_offsets_kernel(int)", _gg(1, 3, 1), "moe::mfma_probe_kernel(int)",
+             "void moe::route_kernel<2, true>(float const*)"]
+    rows = [dict(Dispatch_Id=str(i + 1), Kernel_Name=k) for i, k in enumerate(names)]
+    lab = profsum.label_dispatches(rows)
+    assert [lab[i] for i in (3, 4, 5, 7)] == ["wgrad_gate_up", "wgrad_down", "wgrad_down (extra launch)",
+                                               "wgrad_down (extra launch)"]
+    assert len(profsum.headline_part(rows)) == 7
