@@ -92,6 +92,7 @@ int moe_route(const float* logits, int T, int E, int K,
  * chosen expert e = topk_idx[t,k]:
  *   dlogits[t,e] = gates[t,k] * (dgates[t,k] - sum_j gates[t,j]*dgates[t,j])
  * (sum over j ascending, fp32) and dlogits[t,e] = 0 for the other experts.
+ * A token's K experts must be distinct (those of moe_route are).
  * Linear in dgates, so per-GPU partial gate gradients give per-GPU partial
  * score gradients that sum to the full one.
  *   topk_idx int32 [T,K], gates fp32 [T,K] (from moe_route);
