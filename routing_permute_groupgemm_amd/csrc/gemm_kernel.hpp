@@ -1122,6 +1122,67 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
             __syncthreads();  // every wave is done with the slot before the next stage refills it
             continue;
         }
+        if constexpr (EPI == EPI_SWIGLU && NTW == 4 && !GATHER) {
+            // SwiGLU outputs go out through LDS as the bf16 ones do: each wave
+            // holds 64 columns of h (and of a and b) per 32-row block, one 4 KiB
+            // staging block of 32 rows x 128 bytes, stored as whole lines.  Stored
+            // straight from the MFMA layout, each store covers 16 bytes of 32
+            // rows, and the tile's h and ab stores took about twice as long.  The
+            // gathered-row bodies keep the direct stores: their extra per-lane row
+            // offsets leave no registers for the staged form, which spilled there.
+            uint8_t* stg = smem + ((gs + S - 1) % S) * TL::kStage + wave * 4096;
+            const int ln = lane_id_here();
+            const int r = ln & 31, hh = ln >> 5;
+            auto stage_addr = [&](int row, int chunk) {
+                return (MOE_LDS uint8_t*)(stg + row * 128 + ((chunk ^ (row & 7)) << 4));
+            };
+            const int hc0 = ni * (BN / 2) + wn * (BN / 2 / WN);  // the wave's first h column
+            // read the staged block back, 8 rows x 128 bytes per instruction
+            auto flush = [&](int mt, uint16_t* dst, int64_t ld, int col0) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int rr = 8 * i + (ln >> 3), c = ln & 7;
+                    const u32x4 v = *(const MOE_LDS u32x4*)stage_addr(rr, c);
+                    const int mloc = row_base(mt) + rr;
+                    const int n = hc0 + 8 * c;
+                    if (mloc < valid && n < p.N) *(u32x4*)(dst + (int64_t)(row0 + mloc) * ld + col0 + n) = v;
+                }
+            };
+            // lane (r, hh) holds columns 8*j4 + 4*hh + 0..3 of 32-column block i2 in row r
+            auto put = [&](int i2, int j4, u32x2 w) { *(MOE_LDS u32x2*)(stage_addr(r, 4 * i2 + j4) + 8 * hh) = w; };
+#pragma unroll
+            for (int mt = 0; mt < MTW; ++mt) {
+                if (row_base(mt) >= valid) continue;  // no valid row in this block (uniform)
+#pragma unroll
+                for (int i2 = 0; i2 < 2; ++i2) {
+                    const f32x16& ga = acc[mt][i2];
+                    const f32x16& ub = acc[mt][2 + i2];
+#pragma unroll
+                    for (int j4 = 0; j4 < 4; ++j4) {
+                        float hv[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) hv[i] = silu_f(ga[4 * j4 + i]) * ub[4 * j4 + i];
+                        put(i2, j4, u32x2{pack_bf2(hv[0], hv[1]), pack_bf2(hv[2], hv[3])});
+                    }
+                }
+                flush(mt, p.c, p.ldc, 0);
+                if (p.c2) {
+#pragma unroll
+                    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+                        for (int i2 = 0; i2 < 2; ++i2) {
+                            const f32x16& v = acc[mt][2 * half + i2];
+#pragma unroll
+                            for (int j4 = 0; j4 < 4; ++j4)
+                                put(i2, j4, u32x2{pack_bf2(v[4 * j4], v[4 * j4 + 1]), pack_bf2(v[4 * j4 + 2], v[4 * j4 + 3])});
+                        }
+                        flush(mt, p.c2, 2 * (int64_t)p.N, half * p.N);
+                    }
+                }
+            }
+            __syncthreads();  // every wave is done with the slot before the next stage refills it
+            continue;
+        }
         const int cq = 4 * (lane >> 5);
 #pragma unroll
         for (int mt = 0; mt < MTW; ++mt) {
