@@ -1035,17 +1035,20 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
             // store touches 32 rows).  The stage slot of the last stage (gs-1)
             // is free until the next stage issues its loads; each wave stages
             // 32 rows x 128 bytes at a time in its own 4 KiB of that slot, with
-            // 16-byte chunks XOR-swizzled by row.
+            // 16-byte chunks XOR-swizzled by row.  Where the slot has 8 KiB per
+            // wave (the 256-row body), two such blocks are written before either
+            // is read back, so each wait for LDS data covers two blocks.
             static_assert(TL::kStage / TL::kWaves >= 4096, "staging space per wave");
-            uint8_t* stg = smem + ((gs + S - 1) % S) * TL::kStage + wave * 4096;
+            constexpr int kBufs = TL::kStage / TL::kWaves >= 8192 ? 2 : 1;
+            uint8_t* stg = smem + ((gs + S - 1) % S) * TL::kStage + wave * (kBufs * 4096);
             // the addresses derived from the lane are rebuilt here, per tile,
             // instead of being hoisted out of the tile loop, where the 256-row
             // body has no registers left for them and spills them (each reload
             // then waits for every store issued before it)
             const int ln = lane_id_here();
             const int r = ln & 31, h = ln >> 5;
-            auto stage_addr = [&](int row, int chunk) {
-                return (MOE_LDS uint8_t*)(stg + row * 128 + ((chunk ^ (row & 7)) << 4));
+            auto stage_addr = [&](int buf, int row, int chunk) {
+                return (MOE_LDS uint8_t*)(stg + buf * 4096 + row * 128 + ((chunk ^ (row & 7)) << 4));
             };
             // column groups per round: 64 bf16 (two MFMA tiles) or 32 fp32 (one)
             constexpr int kTilesPerRound = EPI == EPI_BF16 ? 2 : 1;
@@ -1065,29 +1068,37 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
                     for (int np = 0; np < NTW; ++np) asm volatile("" ::"v"(bias_v[np]));
                 }
             }
+            constexpr int kRounds = NTW / kTilesPerRound;
+            static_assert(kRounds % kBufs == 0, "rounds in whole pairs");
 #pragma unroll
             for (int mt = 0; mt < MTW; ++mt) {
 #pragma unroll
-                for (int np = 0; np < NTW / kTilesPerRound; ++np) {
+                for (int np0 = 0; np0 < kRounds; np0 += kBufs) {
 #pragma unroll
-                    for (int q = 0; q < kTilesPerRound; ++q) {
-                        const f32x16& a = acc[mt][np * kTilesPerRound + q];
+                    for (int b = 0; b < kBufs; ++b) {
 #pragma unroll
-                        for (int j4 = 0; j4 < 4; ++j4) {
-                            if (EPI == EPI_BF16) {
-                                u32x2 w = {pack_bf2(a[4 * j4], a[4 * j4 + 1]), pack_bf2(a[4 * j4 + 2], a[4 * j4 + 3])};
-                                *(MOE_LDS u32x2*)(stage_addr(r, 4 * q + j4) + 8 * h) = w;
-                            } else {
-                                f32x4 w = {a[4 * j4], a[4 * j4 + 1], a[4 * j4 + 2], a[4 * j4 + 3]};
-                                *(MOE_LDS f32x4*)stage_addr(r, 2 * j4 + h) = w;
+                        for (int q = 0; q < kTilesPerRound; ++q) {
+                            const f32x16& a = acc[mt][(np0 + b) * kTilesPerRound + q];
+#pragma unroll
+                            for (int j4 = 0; j4 < 4; ++j4) {
+                                if (EPI == EPI_BF16) {
+                                    u32x2 w = {pack_bf2(a[4 * j4], a[4 * j4 + 1]), pack_bf2(a[4 * j4 + 2], a[4 * j4 + 3])};
+                                    *(MOE_LDS u32x2*)(stage_addr(b, r, 4 * q + j4) + 8 * h) = w;
+                                } else {
+                                    f32x4 w = {a[4 * j4], a[4 * j4 + 1], a[4 * j4 + 2], a[4 * j4 + 3]};
+                                    *(MOE_LDS f32x4*)stage_addr(b, r, 2 * j4 + h) = w;
+                                }
                             }
                         }
                     }
+#pragma unroll
+                    for (int b = 0; b < kBufs; ++b) {
+                    const int np = np0 + b;
                     // read back 8 rows x 128 bytes per instruction and store whole lines
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int rr = 8 * i + (ln >> 3), c = ln & 7;
-                        const u32x4 v = *(const MOE_LDS u32x4*)stage_addr(rr, c);
+                        const u32x4 v = *(const MOE_LDS u32x4*)stage_addr(b, rr, c);
                         const int mloc = row_base(mt) + rr;
                         if (EPI == EPI_BF16) {
                             const int n = ni * BN + wn * (BN / WN) + 64 * np + 8 * c;
@@ -1117,6 +1128,7 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
                             }
                         }
                     }
+                    }
                 }
             }
             __syncthreads();  // every wave is done with the slot before the next stage refills it
@@ -1130,26 +1142,39 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
             // rows, and the tile's h and ab stores took about twice as long.  The
             // gathered-row bodies keep the direct stores: their extra per-lane row
             // offsets leave no registers for the staged form, which spilled there.
-            uint8_t* stg = smem + ((gs + S - 1) % S) * TL::kStage + wave * 4096;
+            constexpr int kBufs = TL::kStage / TL::kWaves >= 8192 ? 2 : 1;
+            uint8_t* stg = smem + ((gs + S - 1) % S) * TL::kStage + wave * (kBufs * 4096);
             const int ln = lane_id_here();
             const int r = ln & 31, hh = ln >> 5;
-            auto stage_addr = [&](int row, int chunk) {
-                return (MOE_LDS uint8_t*)(stg + row * 128 + ((chunk ^ (row & 7)) << 4));
+            auto stage_addr = [&](int buf, int row, int chunk) {
+                return (MOE_LDS uint8_t*)(stg + buf * 4096 + row * 128 + ((chunk ^ (row & 7)) << 4));
             };
             const int hc0 = ni * (BN / 2) + wn * (BN / 2 / WN);  // the wave's first h column
             // read the staged block back, 8 rows x 128 bytes per instruction
-            auto flush = [&](int mt, uint16_t* dst, int64_t ld, int col0) {
+            auto flush = [&](int buf, int mt, uint16_t* dst, int64_t ld, int col0) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int rr = 8 * i + (ln >> 3), c = ln & 7;
-                    const u32x4 v = *(const MOE_LDS u32x4*)stage_addr(rr, c);
+                    const u32x4 v = *(const MOE_LDS u32x4*)stage_addr(buf, rr, c);
                     const int mloc = row_base(mt) + rr;
                     const int n = hc0 + 8 * c;
                     if (mloc < valid && n < p.N) *(u32x4*)(dst + (int64_t)(row0 + mloc) * ld + col0 + n) = v;
                 }
             };
             // lane (r, hh) holds columns 8*j4 + 4*hh + 0..3 of 32-column block i2 in row r
-            auto put = [&](int i2, int j4, u32x2 w) { *(MOE_LDS u32x2*)(stage_addr(r, 4 * i2 + j4) + 8 * hh) = w; };
+            auto put = [&](int buf, int i2, int j4, u32x2 w) {
+                *(MOE_LDS u32x2*)(stage_addr(buf, r, 4 * i2 + j4) + 8 * hh) = w;
+            };
+            // the saved a (or b) values of block mt, into staging block buf
+            auto put_ab = [&](int buf, int mt, int half) {
+#pragma unroll
+                for (int i2 = 0; i2 < 2; ++i2) {
+                    const f32x16& v = acc[mt][2 * half + i2];
+#pragma unroll
+                    for (int j4 = 0; j4 < 4; ++j4)
+                        put(buf, i2, j4, u32x2{pack_bf2(v[4 * j4], v[4 * j4 + 1]), pack_bf2(v[4 * j4 + 2], v[4 * j4 + 3])});
+                }
+            };
 #pragma unroll
             for (int mt = 0; mt < MTW; ++mt) {
                 if (row_base(mt) >= valid) continue;  // no valid row in this block (uniform)
@@ -1162,22 +1187,24 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
                         float hv[4];
 #pragma unroll
                         for (int i = 0; i < 4; ++i) hv[i] = silu_f(ga[4 * j4 + i]) * ub[4 * j4 + i];
-                        put(i2, j4, u32x2{pack_bf2(hv[0], hv[1]), pack_bf2(hv[2], hv[3])});
+                        put(0, i2, j4, u32x2{pack_bf2(hv[0], hv[1]), pack_bf2(hv[2], hv[3])});
                     }
                 }
-                flush(mt, p.c, p.ldc, 0);
                 if (p.c2) {
-#pragma unroll
-                    for (int half = 0; half < 2; ++half) {
-#pragma unroll
-                        for (int i2 = 0; i2 < 2; ++i2) {
-                            const f32x16& v = acc[mt][2 * half + i2];
-#pragma unroll
-                            for (int j4 = 0; j4 < 4; ++j4)
-                                put(i2, j4, u32x2{pack_bf2(v[4 * j4], v[4 * j4 + 1]), pack_bf2(v[4 * j4 + 2], v[4 * j4 + 3])});
-                        }
-                        flush(mt, p.c2, 2 * (int64_t)p.N, half * p.N);
+                    if (kBufs == 2) {
+                        // h and a staged together, then b
+                        put_ab(kBufs - 1, mt, 0);
+                        flush(0, mt, p.c, p.ldc, 0);
+                        flush(kBufs - 1, mt, p.c2, 2 * (int64_t)p.N, 0);
+                    } else {
+                        flush(0, mt, p.c, p.ldc, 0);
+                        put_ab(0, mt, 0);
+                        flush(0, mt, p.c2, 2 * (int64_t)p.N, 0);
                     }
+                    put_ab(0, mt, 1);
+                    flush(0, mt, p.c2, 2 * (int64_t)p.N, p.N);
+                } else {
+                    flush(0, mt, p.c, p.ldc, 0);
                 }
             }
             __syncthreads();  // every wave is done with the slot before the next stage refills it
