@@ -197,25 +197,34 @@ def calib_copy():
 
 
 def measured_copy_gbps(stream):
-    """Read+write GB/s of a plain 1 GiB device-to-device copy on this GPU: the practical HBM ceiling
-    that a kernel moving as many bytes in as out can approach."""
+    """Read+write GB/s of plain 1 GiB device-to-device copies on this GPU: torch's copy and the copy
+    probe with each load/store hint (bit 0 non-temporal loads, bit 1 stores).  The best is the practical
+    ceiling of a kernel that moves as many bytes in as out, beside the data sheet's 8 TB/s."""
     import torch
+    from routing_permute_groupgemm_amd import _lib
     n = 1 << 30
     a = torch.empty(n, dtype=torch.uint8, device="cuda")
     b = torch.empty(n, dtype=torch.uint8, device="cuda")
     a.fill_(1)
-    for _ in range(2):
-        b.copy_(a)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(5):
-        b.copy_(a)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / 5
+
+    def rate(fn):
+        for _ in range(2):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(5):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return round(2 * n / (e0.elapsed_time(e1) / 5 * 1e-3) / 1e9, 1)
+
+    rates = {"torch": rate(lambda: b.copy_(a))}
+    for nt in range(4):
+        rates[f"probe_nt{nt}"] = rate(lambda: _lib.moe_probe_copy(a, b, nontemporal=nt, stream=stream))
     del a, b
-    return round(2 * n / (ms * 1e-3) / 1e9, 1)
+    rates["best"] = max(rates.values())
+    return rates
 
 
 def measured_mfma_tflops(stream, target_ms=20.0, shape=32):
@@ -492,9 +501,11 @@ def main():
     rl["launch_ms"] = round(dom_ms, 4)  # the kernel's mean time between the events around it
     rl["kernel"] = dom
     rl["traffic"] = measured_traffic(dom, shape.name)
+    # the rate plain copies reach on this GPU: the practical ceiling of the HBM-bound steps
+    copy_rates = measured_copy_gbps(stream)
     if rl["bound"] == "hbm":
-        # the spec peak above; beside it the rate a plain copy reaches on this GPU
-        rl["measured_copy_gbps"] = measured_copy_gbps(stream)
+        # the spec peak above; beside it the best plain copy
+        rl["measured_copy_gbps"] = copy_rates["best"]
     else:
         # likewise the rate back-to-back MFMAs on random operands reach on this GPU
         rl["measured_mfma_tflops"] = measured_mfma_tflops(stream)
@@ -552,6 +563,9 @@ def main():
         "combine_gbps": round(comb_gbs, 1),
         "combine_hbm_frac": round(comb_gbs / HBM_PEAK_GBS, 4),
         "hbm_frac": summ["hbm_frac"],
+        # plain 1 GiB copies (torch's and the copy probe's), and each HBM-bound step against the best
+        "copy_gbps": copy_rates,
+        "hbm_frac_of_copy": {k: round(v * HBM_PEAK_GBS / copy_rates["best"], 4) for k, v in summ["hbm_frac"].items()},
         "step_ms": summ["step_ms"],
     }
     if "wgrad_bw_vs_nb" in summ:

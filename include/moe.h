@@ -384,6 +384,21 @@ int moe_probe_mfma(const moe_bf16* operands, int blocks, int iters, float* out, 
  */
 int moe_probe_mfma16(const moe_bf16* operands, int blocks, int iters, float* out, moe_stream stream);
 
+/*
+ * Measurement aid, not a step of the layer: the rate of a plain streaming
+ * copy, the practical ceiling of a kernel that reads and writes as many bytes
+ * as it moves.  Copies bytes from src to dst (device buffers, no overlap)
+ * with 16-byte coalesced loads and stores.
+ *   nontemporal  bit 0: non-temporal loads; bit 1: non-temporal stores.
+ *   blocks       workgroups of 256 lanes, each copying 16 KiB per pass over
+ *                the buffer; 0 picks 8 per compute unit.
+ * bytes >= 0 and a multiple of 16, nontemporal in 0..3, blocks in 0..2^20
+ * (MOE_EINVAL; a null pointer with bytes > 0 too); both pointers 16-byte
+ * aligned (MOE_EALIGN).  bytes = 0 launches nothing.  The caller owns both
+ * buffers; nothing is allocated.
+ */
+int moe_probe_copy(const void* src, void* dst, int64_t bytes, int nontemporal, int blocks, moe_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -17,6 +17,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so"
 _p = ctypes.c_void_p
 _i = ctypes.c_int
 _z = ctypes.c_size_t
+_i64 = ctypes.c_int64
 
 # every symbol declared in include/moe.h, with its ctypes signature
 SIGNATURES = {
@@ -42,6 +43,7 @@ SIGNATURES = {
     "moe_router_backward": ([_p, _i, _i, _p, _i, _p, _p, _p, _p, _z, _p], _i),
     "moe_probe_mfma": ([_p, _i, _i, _p, _p], _i),
     "moe_probe_mfma16": ([_p, _i, _i, _p, _p], _i),
+    "moe_probe_copy": ([_p, _p, _i64, _i, _i, _p], _i),
 }
 
 MOE_EPI_NONE = 0
@@ -510,3 +512,16 @@ def moe_probe_mfma16(operands, iters, out=None, stream=None):
     _shape(out, (waves, 64), "out")
     _check(load().moe_probe_mfma16(_ptr(operands), waves // 4, iters, _ptr(out), _stream(stream)))
     return out
+
+
+def moe_probe_copy(src, dst, nontemporal=0, blocks=0, stream=None):
+    """Measurement aid: a plain streaming copy of src into dst (contiguous device tensors of the same
+    byte size, a multiple of 16).  nontemporal: bit 0 loads, bit 1 stores; blocks 0 = 8 per CU."""
+    for name, t in (("src", src), ("dst", dst)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise MoeError(f"{name}: expected a contiguous device tensor")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise MoeError("src and dst differ in byte size")
+    _check(load().moe_probe_copy(_ptr(src), _ptr(dst), nbytes, nontemporal, blocks, _stream(stream)))
+    return dst

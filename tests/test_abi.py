@@ -217,6 +217,14 @@ def test_probe_rejects():
     assert p(None, 4, 10, FAKE, None) == -1
     assert p(FAKE, 4, 10, None, None) == -1
     assert p(MIS, 4, 10, FAKE, None) == -3
+    c = lib.moe_probe_copy
+    assert c(FAKE, FAKE, 24, 0, 0, None) == -1           # not a multiple of 16 bytes
+    assert c(FAKE, FAKE, -16, 0, 0, None) == -1
+    assert c(FAKE, FAKE, 64, 4, 0, None) == -1           # hint bits beyond 0..3
+    assert c(FAKE, FAKE, 64, 0, -1, None) == -1
+    assert c(None, FAKE, 64, 0, 0, None) == -1
+    assert c(MIS, FAKE, 64, 0, 0, None) == -3
+    assert c(None, None, 0, 3, 0, None) == 0             # nothing to copy: no launch
 
 
 def test_permute_noalloc_rejects_on_the_host():

@@ -4,7 +4,9 @@ its register-held fragments.  With operands in {-1, 0, 1} every product and
 sum is exact in fp32, so the sum over a wave's lanes must equal the closed
 form of the header exactly: each 16-deep contraction splits into the lanes
 0..31 and 32..63 halves, and the sum of all entries of A.B is the sum over
-the contraction index of (column sums of A) x (row sums of B)."""
+the contraction index of (column sums of A) x (row sums of B).  The copy
+probe (the HBM-side measurement aid) must reproduce its source byte for
+byte, whatever the load/store hints and grid, tail included."""
 import numpy as np
 import pytest
 import torch
@@ -58,3 +60,17 @@ def test_probe16_matches_closed_form(blocks, iters):
     torch.cuda.synchronize()
     got = out.double().sum(dim=1).cpu().numpy()
     np.testing.assert_array_equal(got, expected_wave_sums16(ops, iters))
+
+
+@pytest.mark.parametrize("nbytes,nontemporal,blocks", [
+    (16, 0, 0), (16 * (3 * 1024 + 17), 1, 0), (16 * (3 * 1024 + 17), 2, 3), (16 * 1024 * 1024 + 48, 3, 0),
+    (16 * 5000, 3, 1)])
+def test_copy_probe_copies_exactly(nbytes, nontemporal, blocks):
+    g = torch.Generator().manual_seed(nbytes + nontemporal)
+    src = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, generator=g).cuda()
+    pad = 4096
+    dst = torch.full((nbytes + pad,), 0xA5, dtype=torch.uint8, device="cuda")
+    _lib.moe_probe_copy(src, dst[:nbytes], nontemporal=nontemporal, blocks=blocks)
+    torch.cuda.synchronize()
+    assert torch.equal(dst[:nbytes].cpu(), src.cpu())
+    assert bool((dst[nbytes:] == 0xA5).all())  # nothing past the end
