@@ -112,8 +112,9 @@ __device__ __forceinline__ void select_rounds(uint32_t (&key)[EPL], int K, int l
 // choices.  Tokens with more than 64 candidates (ties, or flat scores) take
 // the K rounds instead.  Both paths give the same choices.
 //
-// A wave takes a batch of 64 / KP consecutive tokens (KP: the next power of
-// two >= K), one token at a time with the next row in flight.  The choices
+// A wave takes a batch of tb_n consecutive tokens (at most 64 / KP, KP the
+// next power of two >= K; fewer when T is small, so that more waves share the
+// work), one token at a time with the next row in flight.  The choices
 // (expert id and score - s_max) go to LDS, slot KP*token + rank; after the
 // batch, lane KP*i + k computes choice k of token i's gate,
 // exp(s_k - s_max) / sum_k' exp(s_k' - s_max) with the sum taken over k'
@@ -121,14 +122,13 @@ __device__ __forceinline__ void select_rounds(uint32_t (&key)[EPL], int K, int l
 // store each.  FULL: E is a multiple of 64 (no absent lanes).
 template <int EPL, bool FULL>
 __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int T, int E, int K,
-                                                    int kp_log2, int32_t* __restrict__ topk_idx,
+                                                    int kp_log2, int tb_n, int32_t* __restrict__ topk_idx,
                                                     float* __restrict__ gates) {
     __shared__ __attribute__((aligned(16))) uint64_t s_cand[4][72];  // 64 candidates and 8 zero words
     __shared__ int s_bid[4][64];    // batch: chosen expert id, slot KP*token + rank
     __shared__ float s_bsc[4][64];  // batch: chosen score - s_max, then exp of it
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar loop control
-    const int tb_n = 64 >> kp_log2;  // tokens per batch
     const int64_t n_batches = ((int64_t)T + tb_n - 1) / tb_n;
     const int64_t stride = (int64_t)gridDim.x * 4;
     uint64_t* cand = s_cand[wave];
@@ -330,10 +330,14 @@ extern "C" int moe_route(const float* logits, int T, int E, int K, int32_t* topk
     if (moe_host::misaligned(logits) || moe_host::misaligned(topk_idx) || moe_host::misaligned(gates))
         return MOE_EALIGN;
     hipStream_t s = (hipStream_t)stream;
-    // waves loop over batches of 64 / KP tokens (KP: the next power of two >= K)
+    // waves loop over batches of tb tokens: at most 64 / KP (KP: the next power
+    // of two >= K), so that a batch's choices fill one wave, and fewer (down to
+    // 2) while that leaves under 4 waves per SIMD to run them
     int kp = 1;
     while (kp < K) kp <<= 1;
-    const int64_t batches = ((int64_t)T + 64 / kp - 1) / (64 / kp);
+    int tb = 64 / kp;
+    while (tb > 2 && ((int64_t)T + tb - 1) / tb < (int64_t)moe_host::num_cus() * 16) tb >>= 1;
+    const int64_t batches = ((int64_t)T + tb - 1) / tb;
     const dim3 grid((unsigned)std::min<int64_t>((batches + 3) / 4, (int64_t)moe_host::num_cus() * 8)), block(256);
     int kp_log2 = 0;
     while ((1 << kp_log2) < K) ++kp_log2;
@@ -341,8 +345,8 @@ extern "C" int moe_route(const float* logits, int T, int E, int K, int32_t* topk
     const bool full = E % 64 == 0;
 #define MOE_ROUTE_CASE(N)                                                                                  \
     case N:                                                                                                \
-        if (full) route_kernel<N, true><<<grid, block, 0, s>>>(logits, T, E, K, kp_log2, topk_idx, gates); \
-        else route_kernel<N, false><<<grid, block, 0, s>>>(logits, T, E, K, kp_log2, topk_idx, gates);     \
+        if (full) route_kernel<N, true><<<grid, block, 0, s>>>(logits, T, E, K, kp_log2, tb, topk_idx, gates); \
+        else route_kernel<N, false><<<grid, block, 0, s>>>(logits, T, E, K, kp_log2, tb, topk_idx, gates);     \
         break;
     switch (epl) {
         MOE_ROUTE_CASE(1)

@@ -226,10 +226,10 @@ def test_route_ties_and_signed_zeros(E, K):
 def _threshold_rows(E, rng):
     """Router scores that exercise both ways the route kernel selects: rows of distinct N(0,1) scores
     (a few candidates above the threshold), flat rows and rows with 64 or 65 experts tied at the top
-    (64 candidates: the rank count over all ties; 65: the K rounds), and a row of signed zeros."""
+    (64 candidates: the rank count over all ties; 65: the K rounds), 32 and 33, and a row of signed zeros."""
     rows = [rng.standard_normal(E).astype(np.float32) for _ in range(40)]
     rows.append(np.full(E, 0.5, np.float32))
-    for n_top in (64, 65, E // 2, E - 1):
+    for n_top in (32, 33, 64, 65, E // 2, E - 1):
         if 0 < n_top <= E:
             r = (rng.standard_normal(E) - 5.0).astype(np.float32)
             r[rng.permutation(E)[:n_top]] = 3.0
@@ -243,7 +243,8 @@ def _threshold_rows(E, rng):
     return np.stack(rows)
 
 
-@pytest.mark.parametrize("E,K", [(8, 8), (64, 8), (65, 1), (128, 9), (256, 8), (256, 16), (512, 8), (512, 13)])
+@pytest.mark.parametrize("E,K", [(8, 8), (64, 8), (65, 1), (100, 3), (128, 9), (250, 8), (256, 8), (256, 16), (257, 8),
+                                 (512, 8), (512, 13)])
 def test_route_threshold_and_rounds(E, K):
     """Choices exactly the oracle's (score desc, id asc) on rows that take the threshold-and-rank path and
     rows that take the K rounds, interleaved so that one wave meets both; gates within tolerance; a rerun
