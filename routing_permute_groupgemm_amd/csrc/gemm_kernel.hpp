@@ -59,6 +59,9 @@ constexpr int kLdsBudget = 128 * 1024;  // LDS per workgroup for the stage ring
 #ifndef MOE_GEMM_MFMA16
 #define MOE_GEMM_MFMA16 1  // the down dgrad's 256 x 256 body computes with 16x16x32 MFMAs (0: 32x32x16)
 #endif
+#ifndef MOE_GEMM_DGRAD_STAGED
+#define MOE_GEMM_DGRAD_STAGED 1  // 0: the down dgrad's epilogue loads and stores straight from the MFMA layout
+#endif
 #ifndef MOE_GEMM_MFMA16_WGRAD
 #define MOE_GEMM_MFMA16_WGRAD 0  // 1: the weight gradient's too (measured 5% slower, so off)
 #endif
@@ -899,7 +902,80 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
                 continue;
             }
             static_assert(EPI == EPI_SWIGLU_BWD || SCHED == SCHED_WGRAD, "16x16x32 body: the down dgrad or dW");
-            if constexpr (EPI == EPI_SWIGLU_BWD) {  // the accumulators are dh
+            if constexpr (EPI == EPI_SWIGLU_BWD && MOE_GEMM_DGRAD_STAGED) {  // the accumulators are dh
+                // The saved (a, b) pairs come in, and (da, db) go out, as whole
+                // 256-byte row pieces through the wave's 8 KiB of the free slot:
+                // one 16-row block at a time, a in its first 4 KiB and b in the
+                // second (16 rows x 256 bytes each, 16-byte chunks XOR-swizzled by
+                // row).  Each lane reads its MFMA-layout values from there, writes
+                // (da, db) over them, and the rows go back out whole.  The next
+                // block's rows are loaded while this block is worked on.
+                static_assert(TL::kStage / TL::kWaves >= 8192 && BN / WN == 128, "staging space per wave");
+                uint8_t* stg = smem + ((gs + S - 1) % S) * TL::kStage + wave * 8192;
+                const int ln = lane_id_here();
+                auto sa = [&](int hb, int row, int chunk) {
+                    return (MOE_LDS uint8_t*)(stg + hb * 4096 + row * 256 + ((chunk ^ row) << 4));
+                };
+                // row-wise: instruction i covers rows 4i..4i+3, lane ln row 4i + ln/16 and chunk ln%16
+                const int rw = ln >> 4, cc = ln & 15;
+                const int ncol = ni * BN + wn * (BN / WN) + 8 * cc;  // the chunk's first column
+                const bool col_ok = ncol < p.N;
+                u32x4 ld[2][4];
+                auto issue_loads = [&](int m) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int mloc = row16(m) + 4 * i + rw;
+                        ld[0][i] = ld[1][i] = u32x4{0u, 0u, 0u, 0u};
+                        if (mloc < valid && col_ok) {
+                            const uint16_t* src = p.ab + (int64_t)(row0 + mloc) * 2 * p.N + ncol;
+                            ld[0][i] = *(const u32x4*)src;
+                            ld[1][i] = *(const u32x4*)(src + p.N);
+                        }
+                    }
+                };
+                // MFMA layout: row ln%16, columns 4q..4q+3 of each 16-column block
+                const int r = ln & 15, q = ln >> 4;
+                issue_loads(0);
+#pragma unroll
+                for (int m = 0; m < MB16; ++m) {
+#pragma unroll
+                    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) *(MOE_LDS u32x4*)sa(hb, 4 * i + rw, cc) = ld[hb][i];
+                    asm volatile("" ::: "memory");  // a wave's LDS accesses execute in order
+                    if (m + 1 < MB16) issue_loads(m + 1);
+#pragma unroll
+                    for (int nb = 0; nb < NB16; ++nb) {
+                        MOE_LDS uint8_t* pa = sa(0, r, 2 * nb + (q >> 1)) + 8 * (q & 1);
+                        MOE_LDS uint8_t* pb = sa(1, r, 2 * nb + (q >> 1)) + 8 * (q & 1);
+                        const u32x2 aw = *(const MOE_LDS u32x2*)pa, bw = *(const MOE_LDS u32x2*)pb;
+                        float da[4], db[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const float v = acc16[m][nb][i];
+                            const float a = (i & 1) ? bf_hi(aw[i >> 1]) : bf_lo(aw[i >> 1]);
+                            const float b = (i & 1) ? bf_hi(bw[i >> 1]) : bf_lo(bw[i >> 1]);
+                            const float sg = sigmoid_f(a);
+                            da[i] = v * b * sg * (1.0f + a * (1.0f - sg));
+                            db[i] = v * a * sg;
+                        }
+                        *(MOE_LDS u32x2*)pa = u32x2{pack_bf2(da[0], da[1]), pack_bf2(da[2], da[3])};
+                        *(MOE_LDS u32x2*)pb = u32x2{pack_bf2(db[0], db[1]), pack_bf2(db[2], db[3])};
+                    }
+                    asm volatile("" ::: "memory");
+#pragma unroll
+                    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const u32x4 v = *(const MOE_LDS u32x4*)sa(hb, 4 * i + rw, cc);
+                            const int mloc = row16(m) + 4 * i + rw;
+                            if (mloc < valid && col_ok)
+                                *(u32x4*)(p.c + (int64_t)(row0 + mloc) * p.ldc + hb * p.N + ncol) = v;
+                        }
+                    asm volatile("" ::: "memory");  // this block's rows are read before the next is written
+                }
+                __syncthreads();  // every wave is done with the slot before the next stage refills it
+            } else if constexpr (EPI == EPI_SWIGLU_BWD) {  // the accumulators are dh
                 const int cq = 4 * (lane >> 4);
 #pragma unroll
                 for (int mp = 0; mp < MB16 / 2; ++mp) {
