@@ -955,9 +955,11 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
                             const float v = acc16[m][nb][i];
                             const float a = (i & 1) ? bf_hi(aw[i >> 1]) : bf_lo(aw[i >> 1]);
                             const float b = (i & 1) ? bf_hi(bw[i >> 1]) : bf_lo(bw[i >> 1]);
+                            // da = dh b s (1 + a (1 - s)), db = dh a s, with s = sigmoid(a)
                             const float sg = sigmoid_f(a);
-                            da[i] = v * b * sg * (1.0f + a * (1.0f - sg));
-                            db[i] = v * a * sg;
+                            const float u = v * sg, w = u * b;
+                            db[i] = u * a;
+                            da[i] = __builtin_fmaf(w, __builtin_fmaf(-a, sg, a), w);
                         }
                         *(MOE_LDS u32x2*)pa = u32x2{pack_bf2(da[0], da[1]), pack_bf2(da[2], da[3])};
                         *(MOE_LDS u32x2*)pb = u32x2{pack_bf2(db[0], db[1]), pack_bf2(db[2], db[3])};
