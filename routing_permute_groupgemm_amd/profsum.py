@@ -42,6 +42,7 @@ OTHER = [("route_kernel", "route"), ("perm_count_kernel", "permute (count)"), ("
          ("perm_rank_kernel", "permute (rank)"), ("perm_copy_kernel", "permute (row copy)"),
          ("gather_kernel", "bwd_gather"), ("route_backward_kernel", "route_bwd"),
          ("combine_kernel<true", "combine"), ("combine_kernel<false", "bwd_combine"),
+         ("copy_probe_kernel", "copy probe (after the timed steps)"),
          ("mfma16_probe_kernel", "MFMA probe 16x16x32 (after the timed steps)"),
          ("mfma_probe_kernel", "MFMA probe 32x32x16 (after the timed steps)"),
          ("split_offsets_kernel", "wgrad split (offsets)"), ("sum_split_kernel", "wgrad split (sum)"),
@@ -118,8 +119,8 @@ def work_of(bj):
 
 
 def headline_part(trace):
-    """The dispatches of the bench's headline workload: those before its first MFMA probe (the bench
-    measures the probes' rate after the headline's steps, then runs any other workloads)."""
+    """The dispatches of the bench's headline workload: those before its first probe kernel (the bench
+    measures the copy and MFMA probes' rates after the headline's steps, then runs any other workloads)."""
     trace = sorted(trace, key=lambda r: int(r["Dispatch_Id"]))
     for i, r in enumerate(trace):
         if "probe_kernel" in r["Kernel_Name"]:
@@ -144,7 +145,7 @@ def cmd_stats(a):
     L = [f"# Kernel time per step, {bj['config']['workload']}\n",
          "Command (MI355X, ROCm 7.2, from the repository root):\n",
          f"`{a.command}`\n",
-         ("The headline workload's dispatches (those before the bench's first MFMA probe), each " if a.headline_only
+         ("The headline workload's dispatches (those before the bench's first probe kernel), each " if a.headline_only
           else "Every dispatch of the run, ") +
          "labelled with the layer step it belongs to (the two weight-gradient launches of a step share one "
          "kernel and are told apart by their order in the step; launches after the last step, such as the "
