@@ -70,7 +70,56 @@ def parse():
                          "bitwise one on workloads with a backward")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration under rocprofv3)")
+    ap.add_argument("--tile-sweep", action="store_true",
+                    help="only time single row-tiled GroupGEMMs (128 experts x 1024 rows) over contraction "
+                         "lengths, to split their time into a per-k-step and a per-tile part")
     return ap.parse_args()
+
+
+def tile_sweep():
+    """The down GEMM (bf16 epilogue, N = 2048) and the down dgrad (SwiGLU-backward epilogue, N = 768) on 128
+    experts of 1024 rows each, at several contraction lengths; a least-squares line through
+    (k-steps per tile, µs per round of 256 tiles) gives the cost per k-step and per tile."""
+    import torch
+    from routing_permute_groupgemm_amd import _lib
+    _lib.load()
+    EL, rows = 128, 1024
+    cap = EL * rows
+    off = torch.arange(EL + 1, dtype=torch.int32, device="cuda") * rows
+    g = torch.Generator(device="cuda").manual_seed(7)
+    res = {}
+    for name, N, epi, kds in (("down (bf16 epilogue)", 2048, _lib.MOE_EPI_NONE, (256, 512, 768, 1536, 3072)),
+                              ("down dgrad (SwiGLU-backward epilogue)", 768, _lib.MOE_EPI_SWIGLU_BWD,
+                               (512, 1024, 2048, 4096))):
+        pts = []
+        for kd in kds:
+            a = torch.randn(cap, kd, device="cuda", generator=g).to(torch.bfloat16)
+            w = (torch.randn(EL, N, kd, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+            ab = torch.randn(cap, 2 * N, device="cuda", generator=g).to(torch.bfloat16) if epi else None
+            c = torch.empty(cap, 2 * N if epi else N, dtype=torch.bfloat16, device="cuda")
+            f = lambda: _lib.moe_grouped_gemm(a, w, None, 1, off, kd, N, cap, c, epilogue=epi, ab=ab)  # noqa: E731
+            for _ in range(3):
+                f()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(10):
+                f()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / 10
+            rounds = EL * (rows // 256) * ((N + 255) // 256) / 256
+            pts.append((kd // 32, ms * 1e3 / rounds))
+            res.setdefault(name, {})[f"K={kd}"] = dict(ms=round(ms, 4), k_steps=kd // 32,
+                                                       us_per_tile_round=round(ms * 1e3 / rounds, 2),
+                                                       tflops=round(2 * cap * kd * N / ms / 1e9, 1))
+            del a, w, ab, c
+        n = len(pts)
+        mx = sum(x for x, _ in pts) / n
+        my = sum(y for _, y in pts) / n
+        slope = sum((x - mx) * (y - my) for x, y in pts) / sum((x - mx) ** 2 for x, _ in pts)
+        res[name]["fit"] = dict(us_per_k_step=round(slope, 3), us_per_tile=round(my - slope * mx, 2))
+    print(json.dumps(res, indent=1))
 
 
 def algorithmic_work(shape, R, T_act, n_active, zero_copy=False, router=False):
@@ -489,6 +538,9 @@ def main():
 
     if args.calib_copy:
         calib_copy()
+        return
+    if args.tile_sweep:
+        tile_sweep()
         return
     from routing_permute_groupgemm_amd import _lib, synth
 
