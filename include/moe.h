@@ -215,8 +215,9 @@ int moe_grouped_gemm_swiglu(const moe_bf16* x_perm, const moe_bf16* w_gate,
  *   x    bf16 [T,H], the tokens;  src int32 [cap_rows] from moe_permute
  *        (src[r] = t*K + k);  K the top-k of src's encoding;
  *   other arguments as moe_grouped_gemm_swiglu.
- * Errors: T*H*2 must be below 2^31 and cap_rows <= T*K (MOE_EINVAL).  A src
- * value outside [0, T*K) reads a zero row (no access outside x).
+ * Errors: x must be at most 0xF0000000 bytes (T*H*2 <= 3.75 GiB; T up to
+ * 280870 at H = 7168), H*F*2 below 2^31, and cap_rows <= T*K (MOE_EINVAL).
+ * A src value outside [0, T*K) reads a zero row (no access outside x).
  * The weight gradient needs x_perm, so a forward that is followed by the
  * backward keeps the row copy.
  */

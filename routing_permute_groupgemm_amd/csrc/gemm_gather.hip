@@ -14,7 +14,7 @@ extern "C" int moe_grouped_gemm_swiglu_gather(const moe_bf16* x, int T, const in
     if (H % 64 || F % 64) return MOE_ESHAPE;
     // every A load offset (row * H * 2 + column bytes) must stay below the
     // out-of-range offset that masks rows past an expert's end
-    if ((int64_t)T * H * 2 >= (1ll << 31) || (int64_t)H * F * 2 >= (1ll << 31)) return MOE_EINVAL;
+    if ((int64_t)T * H * 2 > (int64_t)kOOB_GATHER || (int64_t)H * F * 2 >= (1ll << 31)) return MOE_EINVAL;
     if ((int64_t)cap_rows > (int64_t)T * K) return MOE_EINVAL;
     if (!offsets) return MOE_EINVAL;
     if (e_local == 0 || cap_rows == 0 || F == 0) return MOE_OK;

@@ -496,7 +496,7 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
     // covers.
     uint32_t c_rowoff[LA];
 #pragma unroll
-    for (int u = 0; u < LA; ++u) c_rowoff[u] = kOOB;
+    for (int u = 0; u < LA; ++u) c_rowoff[u] = kOOB_GATHER;
     int idx_buf = 0;
     bool pf_issued = false;  // the last advance() issued a prefetch (LA more loads)
     i32x4 srd_src = {0, 0, 0, 0};
@@ -541,7 +541,7 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
                     const uint32_t lt = LY::kc_period(u * TL::kWaves + wave) ? lt_a1 : lt_a0;
                     c_rowoff[u] = a_rowl < ic.valid - a_row0(u) && tok < (uint32_t)p.a_rows
                                       ? tok * (uint32_t)(p.lda * 2) + lt
-                                      : kOOB;
+                                      : kOOB_GATHER;
                 }
                 idx_buf ^= 1;
                 if (itile + G < n_tiles_total) {
@@ -647,7 +647,7 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
                         if (kEachLoad) lt = lane_term(lt);
                         voff = lt + (uint32_t)((q * LY::kRowsPerLoad * p.lda + k0) * 2);
                     }
-                    lds_load16(c_srdA, sA + q * 1024, live ? voff : kOOB);
+                    lds_load16(c_srdA, sA + q * 1024, live ? voff : (GATHER ? kOOB_GATHER : kOOB));
                 } else {
                     const int col = ic.mi_w * BM + mn_sub(u) * 64;
                     const uint32_t voff = col < p.M ? la0 + (uint32_t)((mn_kr(u) * 8 * p.lda + col) * 2) : kOOB;

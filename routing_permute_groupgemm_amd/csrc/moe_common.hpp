@@ -45,6 +45,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 
 // An offset that is always outside any resource built by make_rsrc here.
 constexpr uint32_t kOOB = 0x80000000u;
+// The same for the one resource that covers all tokens of the zero-copy
+// gate/up GEMM, which may be up to this many bytes (3.75 GiB): its in-range
+// offsets stay below it, and this plus any column offset of a row still fits
+// in 32 bits.
+constexpr uint32_t kOOB_GATHER = 0xF0000000u;
 
 }  // namespace moe
 

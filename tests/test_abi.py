@@ -130,7 +130,8 @@ def test_gather_gemm_rejects():
     assert g(FAKE, 64, FAKE, 0, FAKE, FAKE, FAKE, 4, 64, 64, 16, FAKE, None, None) == -1   # K < 1
     assert g(FAKE, 64, FAKE, 17, FAKE, FAKE, FAKE, 4, 64, 64, 16, FAKE, None, None) == -1  # K > 16
     assert g(FAKE, 8, FAKE, 1, FAKE, FAKE, FAKE, 4, 64, 64, 16, FAKE, None, None) == -1    # cap > T*K
-    assert g(FAKE, 1 << 20, FAKE, 8, FAKE, FAKE, FAKE, 4, 1024, 64, 16, FAKE, None, None) == -1  # T*H*2 = 2^31
+    # x past 0xF0000000 bytes: T*H*2 = 0xF0000000 + 2048
+    assert g(FAKE, 1966081, FAKE, 8, FAKE, FAKE, FAKE, 4, 1024, 64, 16, FAKE, None, None) == -1
     assert g(FAKE, 64, None, 2, FAKE, FAKE, FAKE, 4, 64, 64, 16, FAKE, None, None) == -1   # no src
     assert g(FAKE, 64, MIS, 2, FAKE, FAKE, FAKE, 4, 64, 64, 16, FAKE, None, None) == -3    # misaligned
 

@@ -153,3 +153,44 @@ def test_large_combine_and_gather(big):
                                big.gates[toks], K, n)
     rows = torch.from_numpy(pos[toks].reshape(-1).astype(np.int64)).cuda()
     assert_close("dy_perm", bits(dy[rows]), ref_dy)
+
+
+def test_gather_past_2gib():
+    """The zero-copy gate/up GEMM addresses all tokens through one 32-bit offset range of up to 3.75 GiB:
+    x of 2.87 GB (T = 200000, H = 7168), rows gathered from both ends and around the 2 GiB byte mark (tokens
+    149796 and up lie past it), against the copy path bit for bit and sampled rows against the oracle."""
+    Tg, Hg, Fg, Kg = 200000, 7168, 128, 1
+    assert Tg * Hg * 2 > 2 ** 31
+    rng = np.random.default_rng(21)
+    mark = 2 ** 31 // (2 * Hg)
+    toks = np.unique(np.concatenate([np.arange(0, 64), np.arange(mark - 64, mark + 64), np.arange(Tg - 64, Tg),
+                                     rng.integers(0, Tg, 200)]))
+    e_rows = np.array([len(toks) // 2, len(toks) - len(toks) // 2])
+    offsets = np.concatenate([[0], np.cumsum(e_rows)]).astype(np.int32)
+    src = toks.astype(np.int32)  # K = 1: src[r] = t
+    R = len(toks)
+    print(f"[large] zero-copy gate/up, x {Tg * Hg * 2 / 2 ** 30:.2f} GiB, {R} rows", flush=True)
+    # x rows by a closed form that both sides evaluate: x[t, c] = ((29 t + 7 c) mod 53 - 26) / 32, exact in bf16
+    x = torch.empty((Tg, Hg), dtype=torch.bfloat16, device="cuda")
+    c = torch.arange(Hg, dtype=torch.int64, device="cuda")[None, :]
+    for lo in range(0, Tg, 8192):
+        r = torch.arange(lo, min(Tg, lo + 8192), dtype=torch.int64, device="cuda")[:, None]
+        x[lo:lo + r.shape[0]] = (((29 * r + 7 * c) % 53 - 26).to(torch.float32) / 32.0).to(torch.bfloat16)
+    wg = synth.operand_bf16((2, Hg, Fg), seed=21, tag=31, std=0.02)
+    wu = synth.operand_bf16((2, Hg, Fg), seed=21, tag=32, std=0.02)
+    dev = pipeline.to_device(dict(wg=wg, wu=wu, offsets=offsets, src=src))
+    hz = torch.empty((R, Fg), dtype=torch.bfloat16, device="cuda")
+    _lib.moe_grouped_gemm_swiglu_gather(x, dev["src"], Kg, dev["wg"], dev["wu"], dev["offsets"], R, h=hz)
+    xp = x[torch.from_numpy(toks).cuda()].contiguous()
+    h = torch.empty_like(hz)
+    _lib.moe_grouped_gemm_swiglu(xp, dev["wg"], dev["wu"], dev["offsets"], R, h=h)
+    torch.cuda.synchronize()
+    assert torch.equal(h.view(torch.int16), hz.view(torch.int16))
+    del x, xp
+    torch.cuda.empty_cache()
+    rows = np.array(sorted({0, R - 1} | set(np.searchsorted(toks, [mark - 1, mark, mark + 1]).tolist())
+                           | set(rng.integers(0, R, 12).tolist())), np.int64)
+    tr = toks[rows].astype(np.int64)[:, None]
+    xs = synth.f32_to_bf16_bits((((29 * tr + 7 * np.arange(Hg)[None, :]) % 53 - 26).astype(np.float32)) / 32.0)
+    ref_h, _ = oracle.expert_up(xs, wg, wu, compact_offsets(offsets, rows), len(rows), want_ab=False)
+    assert_close("h", bits(hz)[rows], ref_h)
