@@ -65,6 +65,9 @@ def parse():
                          "rows x depth x width, as a vendor-library reference on this GPU")
     ap.add_argument("--copy-rows", action="store_true",
                     help="forward-only workloads: permute with the row copy instead of zero-copy dispatch")
+    ap.add_argument("--zero-copy", action="store_true",
+                    help="forward+backward workloads too: no row copy, the gate/up GEMM and its weight "
+                         "gradient read the tokens through src")
     ap.add_argument("--no-nb", action="store_true",
                     help="skip timing the non-bitwise (two row chunks per expert) weight gradient beside the "
                          "bitwise one on workloads with a backward")
@@ -370,8 +373,11 @@ def layer_steps(shape, dev, buf, router):
             ("bwd_up_dgrad", lambda: _lib.moe_grouped_gemm(buf.dab, dev["w_gate"], dev["w_up"], 1, buf.offsets, F,
                                                            H, cap, buf.dx_perm)),
             ("bwd_combine", lambda: _lib.moe_combine(buf.dx_perm, buf.pos, None, out=buf.dx)),
-            ("wgrad_gate_up", lambda: _lib.moe_wgrad_gate_up(buf.x_perm, buf.dab, buf.offsets, EL, cap,
-                                                             dw_gate=buf.dw_gate, dw_up=buf.dw_up)),
+            ("wgrad_gate_up",
+             (lambda: _lib.moe_wgrad_gate_up_gather(dev["x"], buf.src, shape.K, buf.dab, buf.offsets, EL, cap,
+                                                    dw_gate=buf.dw_gate, dw_up=buf.dw_up)) if buf.zero_copy else
+             (lambda: _lib.moe_wgrad_gate_up(buf.x_perm, buf.dab, buf.offsets, EL, cap, dw_gate=buf.dw_gate,
+                                             dw_up=buf.dw_up))),
             ("wgrad_down", lambda: _lib.moe_wgrad(buf.h, F, buf.dy_perm, H, buf.offsets, EL, F, H, cap,
                                                   dw=buf.dw_down)),
         ]
@@ -487,7 +493,7 @@ def run_workload(name, args, n_steps, warmup, log):
     log(f"{shape.name}: generating inputs")
     inp = synth.make_inputs(shape, seed=args.seed, router=args.router)
     dev = pipeline.to_device(inp)
-    zero_copy = not shape.backward and not args.copy_rows
+    zero_copy = not args.copy_rows and (not shape.backward or args.zero_copy)
     buf = pipeline.MoeBuffers.allocate(shape, zero_copy=zero_copy)
     stream = torch.cuda.current_stream()
     steps = layer_steps(shape, dev, buf, args.router)
@@ -520,7 +526,7 @@ def run_workload(name, args, n_steps, warmup, log):
     )
     if rs["status"] != 0:
         summ["warning"] = "row capacity overflow: rows were dropped"
-    if shape.backward and not args.no_nb:
+    if shape.backward and not args.no_nb and not zero_copy:  # the two modes are timed on x_perm
         log(f"{shape.name}: weight gradient, bitwise vs non-bitwise")
         summ["wgrad_bw_vs_nb"] = time_wgrad_modes(shape, buf)
     state = dict(shape=shape, inp=inp, dev=dev, buf=buf, steps=steps, t=t, work=work, rs=rs, zero_copy=zero_copy,

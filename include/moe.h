@@ -298,6 +298,26 @@ int moe_wgrad_gate_up(const moe_bf16* x_perm, int H, const moe_bf16* dab, int F,
                       float* dw_gate, float* dw_up, moe_stream stream);
 
 /*
+ * moe_wgrad_gate_up without the permuted copy of the tokens, the backward
+ * half of zero-copy dispatch (MoonEP page, "How Redundant Expert Planning
+ * Achieves Perfect Balance": tokens are used where they are, with no copy
+ * through an intermediate buffer).  Row r of the expert-grouped order is
+ * read from x[src[r] / K], so a training step needs no x_perm: the forward
+ * runs moe_grouped_gemm_swiglu_gather on the index-only moe_permute.
+ * dw_gate and dw_up are bit-identical to moe_wgrad_gate_up on the x_perm
+ * that moe_permute would have written (the same fixed order per element).
+ *   x    bf16 [T,H], the tokens;  src int32 [cap_rows] from moe_permute
+ *        (src[r] = t*K + k);  K the top-k of src's encoding;
+ *   dab, F, offsets, e_local, cap_rows, dw_gate, dw_up as moe_wgrad_gate_up.
+ * Errors: as moe_grouped_gemm_swiglu_gather for x, T, src, K (x at most
+ * 0xF0000000 bytes, cap_rows <= T*K: MOE_EINVAL); H, F multiples of 64
+ * (MOE_ESHAPE).  A src value outside [0, T*K) reads a zero row.
+ */
+int moe_wgrad_gate_up_gather(const moe_bf16* x, int T, const int32_t* src, int K, int H,
+                             const moe_bf16* dab, int F, const int32_t* offsets, int e_local,
+                             int cap_rows, float* dw_gate, float* dw_up, moe_stream stream);
+
+/*
  * The non-bitwise variant of moe_wgrad (UniEP evaluation, "Performance Cost
  * of Bitwise Reproducibility" and Table 7: splitting the weight gradient's
  * reduction over tokens gives more parallel work but changes the summation

@@ -36,6 +36,7 @@ SIGNATURES = {
     "moe_combine": ([_p, _p, _p, _i, _i, _i, _p, _p], _i),
     "moe_wgrad": ([_p, _i, _p, _i, _p, _i, _i, _i, _i, _p, _p], _i),
     "moe_wgrad_gate_up": ([_p, _i, _p, _i, _p, _i, _i, _p, _p, _p], _i),
+    "moe_wgrad_gate_up_gather": ([_p, _i, _p, _i, _i, _p, _i, _p, _i, _i, _p, _p, _p], _i),
     "moe_wgrad_split_workspace_size": ([_i, _i, _i, _i], _z),
     "moe_wgrad_split": ([_p, _i, _p, _i, _p, _i, _i, _i, _i, _i, _p, _p, _z, _p], _i),
     "moe_router_workspace_size": ([_i, _i, _i], _z),
@@ -396,6 +397,35 @@ def moe_wgrad_gate_up(x_perm, dab, offsets, e_local, cap_rows, dw_gate=None, dw_
         out.append(t)
     _check(load().moe_wgrad_gate_up(_ptr(x_perm), H, _ptr(dab), F, _ptr(offsets), e_local, cap_rows, _ptr(out[0]),
                                     _ptr(out[1]), _stream(stream)))
+    return out[0], out[1]
+
+
+def moe_wgrad_gate_up_gather(x, src, K, dab, offsets, e_local, cap_rows, dw_gate=None, dw_up=None, stream=None):
+    """moe_wgrad_gate_up reading row r of the expert-grouped order straight from x[src[r] // K] (no x_perm)."""
+    _need(x, torch.bfloat16, "x")
+    _need(src, torch.int32, "src")
+    _need(dab, torch.bfloat16, "dab")
+    _need(offsets, torch.int32, "offsets")
+    if x.dim() != 2:
+        raise MoeError(f"x: expected [T, H], got {tuple(x.shape)}")
+    T, H = x.shape
+    F = dab.shape[1] // 2
+    if dab.dim() != 2 or dab.shape[1] != 2 * F:
+        raise MoeError(f"dab: expected [rows, 2F], got {tuple(dab.shape)}")
+    _rows(dab, cap_rows, 2 * F, "dab")
+    if src.numel() < cap_rows:
+        raise MoeError(f"src: expected at least {cap_rows} entries, got {src.numel()}")
+    if offsets.numel() < e_local + 1:
+        raise MoeError(f"offsets: expected {e_local + 1} entries, got {offsets.numel()}")
+    out = []
+    for t, name in ((dw_gate, "dw_gate"), (dw_up, "dw_up")):
+        if t is None:
+            t = torch.empty((e_local, H, F), dtype=torch.float32, device=x.device)
+        _need(t, torch.float32, name)
+        _shape(t, (e_local, H, F), name)
+        out.append(t)
+    _check(load().moe_wgrad_gate_up_gather(_ptr(x), T, _ptr(src), int(K), H, _ptr(dab), F, _ptr(offsets), e_local,
+                                           cap_rows, _ptr(out[0]), _ptr(out[1]), _stream(stream)))
     return out[0], out[1]
 
 

@@ -299,7 +299,10 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
     using LY = Lay<BK>;
     constexpr int MTW = TL::kMTW, NTW = TL::kNTW, LPW = TL::kLoadsPerWave, S = TL::kStages, KK = TL::kKK;
     constexpr int LA = TL::kALoads / TL::kWaves;  // A loads per wave and stage
-    static_assert(!GATHER || (SCHED == SCHED_ROWS && EPI == EPI_SWIGLU), "gathered A rows: gate/up GEMM only");
+    static_assert(!GATHER || (SCHED == SCHED_ROWS && EPI == EPI_SWIGLU) || (SCHED == SCHED_WGRAD && EPI == EPI_F32),
+                  "gathered A rows: the gate/up GEMM and the weight gradient");
+    // gathered rows of the weight gradient's contraction (GATHER with SCHED_WGRAD)
+    constexpr bool kGW = GATHER && SCHED == SCHED_WGRAD;
     // The 256 x 256 body of the down dgrad (SwiGLU-backward epilogue) computes
     // with v_mfma_f32_16x16x32_bf16: its 128 x 128 wave tile is 8 x 8 blocks of
     // 16 x 16, one 32-deep MFMA step per stage.  Each lane then holds 4
@@ -390,7 +393,8 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
             lt_b0 = LY::lane_mn(lane, p.ldw);
         }
     } else {
-        lt_a0 = LY::lane_mn(lane, p.lda);
+        // gathered rows (kGW): the row term comes from the row's token
+        lt_a0 = LY::lane_mn(lane, kGW ? 0 : p.lda);
         lt_b0 = LY::lane_mn(lane, p.ldb);
     }
 
@@ -504,6 +508,18 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
         c_srdA = make_srd(p.a, (uint32_t)(p.a_rows * p.lda * 2));
         srd_src = make_srd(p.src, (uint32_t)(p.cap * 4));
     }
+    // Gathered rows of the weight gradient (kGW): a stage's A rows are rows
+    // k0 .. k0+31 of the expert, wave w loading rows k0 + 8w + (l / 8), so
+    // each wave needs 8 tokens per stage.  They are fetched by one LDS-direct
+    // dword load per stage (lanes 0..7; the other lanes read nothing) into
+    // the wave's slice of one of two buffers in s_idx, two stages ahead of
+    // the cursor, so the end-of-stage wait that publishes the ring's stages
+    // covers them too (that fetch is the newest load of its stage, one more
+    // than the ring's count).  tk counts the cursor's stages: its tokens are
+    // in buffer tk & 1.
+    int tk = 0;
+    int itile_n = 0;  // the cursor tile's successor with stages (kGW)
+    TileDesc ic_n = {0, 0, 0, 0, 0, 0, 0};
     // lane's row in A load u of this wave: rows q*16 + l/4 of the tile, the
     // uniform part q*16 and the lane part l/4
     // (per-tile code reads the lane id afresh, so that nothing derived from
@@ -574,6 +590,32 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
             c_rowB = (uint64_t)(p.b + (int64_t)ic.row0 * p.ldb);
             asm volatile("" : "+s"(c_rowA), "+s"(c_rowB));
         }
+        if (kGW) {
+            for (itile_n = itile + G; itile_n < n_tiles_total; itile_n += G) {
+                ic_n = decode(itile_n);
+                if (ic_n.KT > 0) break;
+            }
+        }
+    };
+    // kGW: fetch the 8 tokens of this wave's rows of the cursor's stage
+    // (ahead = 0) or of the stage after it (ahead = 1: the next stage of its
+    // tile, or the first of the next tile) into buffer (tk + ahead) & 1; a
+    // load of nothing when there is no such stage.
+    auto fetch_tokens = [&](int ahead) {
+        if constexpr (kGW) {
+            int row0 = 0, rows = 0, k0 = 0;
+            if (itile < n_tiles_total) {
+                if (ik + ahead < ic.KT) {
+                    row0 = ic.row0, rows = ic.valid, k0 = (ik + ahead) * BK;
+                } else if (itile_n < n_tiles_total) {
+                    row0 = ic_n.row0, rows = ic_n.valid, k0 = 0;
+                }
+            }
+            const int ln = lane_id_here();
+            const int r = k0 + 8 * wave + ln;  // lanes 0..7: the wave's 8 rows
+            const uint32_t base = lds_addr(s_idx) + (uint32_t)((((tk + ahead) & 1) * TL::kWaves + wave) * 256);
+            lds_load4(srd_src, base, ln < 8 && r < rows ? (uint32_t)(row0 + r) * 4u : kOOB);
+        }
     };
     auto advance = [&]() {
         if (itile < n_tiles_total && ++ik >= ic.KT) {
@@ -581,8 +623,12 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
             itile += G;
             seek();
         }
+        if constexpr (kGW) {
+            ++tk;
+            fetch_tokens(1);
+        }
     };
-    if (GATHER && tile0 < n_tiles_total) {
+    if (GATHER && !kGW && tile0 < n_tiles_total) {
         // the first tile's indices (row-tiled schedules skip no tile)
         prefetch_rows(tile0, 0);
         wait_vmcnt_mem<0>();
@@ -598,10 +644,24 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
     // built once per stage rather than once per load.
     struct StageSrd {
         i32x4 a, b;
+        uint32_t arow;  // kGW: byte offset of the lane's A row in a, or kOOB_GATHER
     };
     auto stage_srd = [&](int kt) {
         StageSrd r{};
-        if constexpr (SCHED == SCHED_WGRAD) {
+        if constexpr (kGW) {
+            // the lane's row of the stage and its token (fetched two stages ago)
+            const int k0 = kt * BK;
+            const uint32_t rows = (uint32_t)max(0, min(BK, ic.valid - k0));
+            r.a = c_srdA;
+            r.b = make_srd((const uint16_t*)c_rowB + (int64_t)k0 * p.ldb, rows * (uint32_t)(p.ldb * 2));
+            const int ln = lane_id_here();
+            const uint32_t v = (uint32_t)*(const MOE_LDS int*)(s_idx + ((tk & 1) * TL::kWaves + wave) * 64 + (ln >> 3));
+            // src = t*K + k; the quotient estimate is t or t - 1
+            uint32_t tok = __umulhi(v, p.topk_rcp);
+            if (v - tok * (uint32_t)p.topk >= (uint32_t)p.topk) ++tok;
+            r.arow = k0 + 8 * wave + (ln >> 3) < ic.valid && tok < (uint32_t)p.a_rows ? tok * (uint32_t)(p.lda * 2)
+                                                                                       : kOOB_GATHER;
+        } else if constexpr (SCHED == SCHED_WGRAD) {
             const int k0 = kt * BK;
             const uint32_t rows = (uint32_t)max(0, min(BK, ic.valid - k0));
             r.a = make_srd((const uint16_t*)c_rowA + (int64_t)k0 * p.lda, rows * (uint32_t)(p.lda * 2));
@@ -648,6 +708,12 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
                         voff = lt + (uint32_t)((q * LY::kRowsPerLoad * p.lda + k0) * 2);
                     }
                     lds_load16(c_srdA, sA + q * 1024, live ? voff : (GATHER ? kOOB_GATHER : kOOB));
+                } else if (kGW) {
+                    // the row term is the lane's token row (mn_kr(u) is the wave, so the
+                    // stage's row of this lane is the one stage_srd looked up)
+                    const int col = ic.mi_w * BM + mn_sub(u) * 64;
+                    const uint32_t voff = col < p.M ? ss.arow + la0 + (uint32_t)(col * 2) : kOOB_GATHER;
+                    lds_load16(ss.a, sA + q * 1024, live ? voff : kOOB_GATHER);
                 } else {
                     const int col = ic.mi_w * BM + mn_sub(u) * 64;
                     const uint32_t voff = col < p.M ? la0 + (uint32_t)((mn_kr(u) * 8 * p.lda + col) * 2) : kOOB;
@@ -727,9 +793,15 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
     // stages at the end of stage gs.  The barrier after it publishes stage gs+2
     // (first read in the last step of stage gs+1) and frees the slot of stage
     // gs, which stage gs+1's loads refill.
-    constexpr int kWaitLoads = (S - 3) * LPW;
+    constexpr int kWaitLoads = (S - 3) * LPW + (kGW ? 1 : 0);
+    if constexpr (kGW) {
+        // the first cursor stage's tokens (buffer 0), then the next stage's
+        fetch_tokens(0);
+        fetch_tokens(1);
+    }
 #pragma unroll
     for (int t = 0; t < S - 1; ++t) {
+        if constexpr (kGW) wait_vmcnt_mem<0>();  // this stage's tokens have landed
         issue(ik, t, itile < n_tiles_total);
         advance();
     }

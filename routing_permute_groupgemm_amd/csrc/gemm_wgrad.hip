@@ -16,6 +16,9 @@ using moe_host::misaligned;
 namespace moe {
 
 int launch_wgrad(const GemmParams& p, hipStream_t s) { return launch<LAY_MN, EPI_F32, SCHED_WGRAD>(p, s); }
+static int launch_wgrad_gather(const GemmParams& p, hipStream_t s) {
+    return launch<LAY_MN, EPI_F32, SCHED_WGRAD, true>(p, s);
+}
 
 // Offsets of the split groups: group j*S + c holds chunk c of expert j, rows
 // [off[j] + min(c*len, n), off[j] + min((c+1)*len, n)) with n the expert's
@@ -101,6 +104,43 @@ extern "C" int moe_wgrad_gate_up(const moe_bf16* x_perm, int H, const moe_bf16* 
     p.cf2 = dw_up;
     p.n_split = F;
     return launch_wgrad(p, (hipStream_t)stream);
+}
+
+extern "C" int moe_wgrad_gate_up_gather(const moe_bf16* x, int T, const int32_t* src, int K, int H,
+                                        const moe_bf16* dab, int F, const int32_t* offsets, int e_local,
+                                        int cap_rows, float* dw_gate, float* dw_up, moe_stream stream) {
+    using namespace moe;
+    if (e_local < 0 || e_local > kMaxGroups || H < 0 || F < 0 || cap_rows < 0 || T < 0 || K < 1 || K > 16)
+        return MOE_EINVAL;
+    if (H % 64 || F % 64) return MOE_ESHAPE;
+    // every A load offset (token * H * 2 + column bytes) must stay below the
+    // out-of-range offset that masks rows past an expert's end
+    if ((int64_t)T * H * 2 > (int64_t)kOOB_GATHER || (int64_t)64 * 2 * F * 2 >= (1ll << 31)) return MOE_EINVAL;
+    if ((int64_t)cap_rows > (int64_t)T * K) return MOE_EINVAL;
+    if (!offsets) return MOE_EINVAL;
+    if (e_local == 0 || H == 0 || F == 0) return MOE_OK;
+    if (!dw_gate || !dw_up || (cap_rows > 0 && (!x || !src || !dab))) return MOE_EINVAL;
+    if (misaligned(x) || misaligned(src) || misaligned(dab) || misaligned(offsets) || misaligned(dw_gate) ||
+        misaligned(dw_up))
+        return MOE_EALIGN;
+    GemmParams p{};
+    p.a = x;
+    p.lda = H;
+    p.a_rows = T;
+    p.src = src;
+    p.topk = K;
+    p.topk_rcp = 0xffffffffu / (uint32_t)K;
+    p.b = dab;
+    p.ldb = 2 * F;
+    p.offsets = offsets;
+    p.e_local = e_local;
+    p.cap = cap_rows;
+    p.M = H;
+    p.N = 2 * F;
+    p.cf = dw_gate;
+    p.cf2 = dw_up;
+    p.n_split = F;
+    return launch_wgrad_gather(p, (hipStream_t)stream);
 }
 
 extern "C" size_t moe_wgrad_split_workspace_size(int e_local, int M, int N, int splits) {

@@ -40,15 +40,13 @@ class MoeBuffers:
     dw_down: torch.Tensor | None = None
     dgates: torch.Tensor | None = None
     dlogits: torch.Tensor | None = None
-    # zero-copy dispatch: the permutation is index-only and the gate/up
-    # GroupGEMM reads x[src[r] // K]; forward only (the weight gradient reads x_perm)
+    # zero-copy dispatch: the permutation is index-only, and the gate/up
+    # GroupGEMM and the gate/up weight gradient read x[src[r] // K]
     zero_copy: bool = False
 
     @classmethod
     def allocate(cls, shape: MoeShape, cap: int | None = None, device="cuda", backward=None, zero_copy=False):
         backward = shape.backward if backward is None else backward
-        if zero_copy and backward:
-            raise ValueError("zero_copy is forward-only: the weight gradient reads x_perm")
         T, H, F, K, EL = shape.T, shape.H, shape.F, shape.K, shape.EL
         cap = shape.cap if cap is None else cap
         capn = max(cap, 1)
@@ -114,7 +112,8 @@ def forward(buf: MoeBuffers, inp: dict):
 
 
 def backward(buf: MoeBuffers, inp: dict):
-    """inp additionally holds d_out. Needs the forward's ab_save."""
+    """inp additionally holds d_out (and x, read by the zero-copy weight gradient). Needs the forward's
+    ab_save."""
     s = buf.shape
     H, F, EL, cap = s.H, s.F, s.EL, buf.cap
     _lib.moe_gather_gate_grad(inp["d_out"], buf.pos, buf.gates, buf.y, buf.dy_perm, buf.dgates)
@@ -123,7 +122,11 @@ def backward(buf: MoeBuffers, inp: dict):
                           epilogue=_lib.MOE_EPI_SWIGLU_BWD, ab=buf.ab)
     _lib.moe_grouped_gemm(buf.dab, inp["w_gate"], inp["w_up"], 1, buf.offsets, F, H, cap, buf.dx_perm)
     _lib.moe_combine(buf.dx_perm, buf.pos, None, out=buf.dx)
-    _lib.moe_wgrad_gate_up(buf.x_perm, buf.dab, buf.offsets, EL, cap, dw_gate=buf.dw_gate, dw_up=buf.dw_up)
+    if buf.zero_copy:
+        _lib.moe_wgrad_gate_up_gather(inp["x"], buf.src, s.K, buf.dab, buf.offsets, EL, cap, dw_gate=buf.dw_gate,
+                                      dw_up=buf.dw_up)
+    else:
+        _lib.moe_wgrad_gate_up(buf.x_perm, buf.dab, buf.offsets, EL, cap, dw_gate=buf.dw_gate, dw_up=buf.dw_up)
     _lib.moe_wgrad(buf.h, F, buf.dy_perm, H, buf.offsets, EL, F, H, cap, dw=buf.dw_down)
     return buf.dx
 

@@ -121,6 +121,23 @@ def test_router_rejects():
     assert lib.moe_router_workspace_size(T, H, 8) == 0
 
 
+def test_gather_wgrad_rejects():
+    lib = _lib.load()
+    g = lib.moe_wgrad_gate_up_gather
+    # (x, T, src, K, H, dab, F, offsets, e_local, cap, dw_gate, dw_up, stream)
+    assert g(FAKE, 64, FAKE, 2, 96, FAKE, 64, FAKE, 4, 16, FAKE, FAKE, None) == -2   # H % 64
+    assert g(FAKE, 64, FAKE, 2, 64, FAKE, 48, FAKE, 4, 16, FAKE, FAKE, None) == -2   # F % 64
+    assert g(FAKE, 64, FAKE, 0, 64, FAKE, 64, FAKE, 4, 16, FAKE, FAKE, None) == -1   # K < 1
+    assert g(FAKE, 64, FAKE, 17, 64, FAKE, 64, FAKE, 4, 16, FAKE, FAKE, None) == -1  # K > 16
+    assert g(FAKE, 8, FAKE, 1, 64, FAKE, 64, FAKE, 4, 16, FAKE, FAKE, None) == -1    # cap > T*K
+    assert g(FAKE, 1966081, FAKE, 8, 1024, FAKE, 64, FAKE, 4, 16, FAKE, FAKE, None) == -1  # x past 0xF0000000 B
+    assert g(FAKE, 64, FAKE, 2, 64, FAKE, 64, None, 4, 16, FAKE, FAKE, None) == -1   # no offsets
+    assert g(FAKE, 64, None, 2, 64, FAKE, 64, FAKE, 4, 16, FAKE, FAKE, None) == -1   # no src
+    assert g(FAKE, 64, FAKE, 2, 64, FAKE, 64, FAKE, 4, 16, None, FAKE, None) == -1   # no dw_gate
+    assert g(MIS, 64, FAKE, 2, 64, FAKE, 64, FAKE, 4, 16, FAKE, FAKE, None) == -3    # misaligned
+    assert g(None, 64, None, 2, 64, None, 64, FAKE, 0, 16, None, None, None) == 0    # no experts: nothing to do
+
+
 def test_gather_gemm_rejects():
     lib = _lib.load()
     g = lib.moe_grouped_gemm_swiglu_gather

@@ -223,6 +223,19 @@ def test_wgrad_sampled(case, which):
         assert_close(f"dw[{j}]", got[j][:, cols], ref[j][:, cols])
 
 
+def test_zero_copy_wgrad_gate_up_full(case):
+    """The gate/up weight gradient reading its rows from x through src, at full size in the bench's launch
+    configuration: bit-identical to the copy path's dW_gate and dW_up of the same backward."""
+    c = case
+    _bwd_only(c)
+    s = c.shape
+    gz, uz = _lib.moe_wgrad_gate_up_gather(c.dev["x"], c.buf.src, s.K, c.buf.dab, c.buf.offsets, s.EL, c.buf.cap)
+    torch.cuda.synchronize()
+    assert torch.equal(gz.view(torch.int32), c.buf.dw_gate.view(torch.int32))
+    assert torch.equal(uz.view(torch.int32), c.buf.dw_up.view(torch.int32))
+    del gz, uz
+
+
 def test_wgrad_split_sampled(case):
     """The non-bitwise weight gradient (two row chunks per expert) at full size: sampled experts and
     columns against the oracle's serial sum, and a bitwise rerun."""

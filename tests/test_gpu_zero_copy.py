@@ -4,7 +4,9 @@ expert-grouped order straight from the tokens, x[src[r] // K], after an
 index-only permutation.  Its h and ab_save must be bit-identical to the
 copy path (same kernel, same accumulation order, only the address of the A
 rows differs) and within tolerance of the oracle; the whole zero-copy
-forward must give the copy path's output bit for bit."""
+forward must give the copy path's output bit for bit.  The backward half:
+the gate/up weight gradient reads its contraction rows through src too, so
+a whole training step runs with no x_perm, bit for bit the copy path's."""
 import numpy as np
 import pytest
 import torch
@@ -110,6 +112,84 @@ def test_gather_every_topk(K):
     assert_equal("ab_save", bits(ab)[:R], bits(ref.ab)[:R])
 
 
-def test_zero_copy_is_forward_only():
-    with pytest.raises(ValueError):
-        pipeline.MoeBuffers.allocate(SHAPES["tiny"], backward=True, zero_copy=True)
+def wgrad_both_ways(shape, inp, cap, seed):
+    """dW_gate, dW_up from x_perm (copy path) and from x through src (zero-copy), on a seeded [da | db]."""
+    dev = pipeline.to_device(inp)
+    ref = pipeline.MoeBuffers.allocate(shape, cap=cap, backward=False)
+    pipeline.route(ref, dev["logits"])
+    pipeline.permute(ref, dev["x"])
+    capn = max(cap, 1)
+    dab = pipeline.to_device(dict(d=synth.operand_bf16((capn, 2 * shape.F), seed=seed, tag=41)))["d"]
+    gw, uw = _lib.moe_wgrad_gate_up(ref.x_perm, dab, ref.offsets, shape.EL, cap)
+    gz, uz = _lib.moe_wgrad_gate_up_gather(dev["x"], ref.src, shape.K, dab, ref.offsets, shape.EL, cap)
+    torch.cuda.synchronize()
+    return ref, (gw, uw), (gz, uz)
+
+
+# experts of every size around a stage (32 rows), empty ones among them, many tiles per workgroup
+SPARSE = synth.MoeShape("zc_sparse", 96, T=700, H=192, F=64, E=64, K=2, e_begin=3, e_local=40, zipf_s=1.5)
+
+
+@pytest.mark.parametrize("tile", ["auto", "128"])
+@pytest.mark.parametrize("name", list(SHAPES) + ["sparse"])
+def test_gather_wgrad_equals_copy_path(name, tile, monkeypatch):
+    """The weight gradient of gate/up reading its rows through src: bit for bit the copy path's, which the
+    oracle pins (tests/test_gpu_parity.py); here also sampled against the oracle directly."""
+    if tile != "auto":
+        monkeypatch.setenv("MOE_GEMM_TILE", tile)
+    shape = SPARSE if name == "sparse" else SHAPES[name]
+    print(f"[zero-copy wgrad] {name} tile={tile} T={shape.T} H={shape.H} F={shape.F} EL={shape.EL}", flush=True)
+    inp = synth.make_inputs(shape, seed=16)
+    ref, (gw, uw), (gz, uz) = wgrad_both_ways(shape, inp, shape.cap, seed=16)
+    assert torch.equal(gw.view(torch.int32), gz.view(torch.int32))
+    assert torch.equal(uw.view(torch.int32), uz.view(torch.int32))
+    counts = bits(ref.counts)
+    assert (counts == 0).any() or name != "sparse"  # empty experts are skipped by the schedule
+
+
+@pytest.mark.parametrize("name", ["ep_share_small", "sparse"])
+def test_gather_wgrad_with_dropped_rows(name):
+    """Capacity below R: rows past cap_rows take part in neither path."""
+    shape = SPARSE if name == "sparse" else SHAPES[name]
+    inp = synth.make_inputs(shape, seed=17)
+    idx, _ = oracle.route(inp["logits"], shape.K)
+    R_full = int(oracle.permute(idx, shape.e_begin, shape.EL, inp["x"], shape.cap)["offsets"][-1])
+    cap = max(R_full // 2 + 5, 1)
+    ref, (gw, uw), (gz, uz) = wgrad_both_ways(shape, inp, cap, seed=17)
+    assert int(bits(ref.status)[0]) == 1
+    assert torch.equal(gw.view(torch.int32), gz.view(torch.int32))
+    assert torch.equal(uw.view(torch.int32), uz.view(torch.int32))
+
+
+@pytest.mark.parametrize("K", [1, 3, 16])
+def test_gather_wgrad_every_topk(K):
+    shape = synth.MoeShape(f"zcw_k{K}", 97, T=333, H=128, F=64, E=max(16, K), K=K)
+    inp = synth.make_inputs(shape, seed=K + 30)
+    _, (gw, uw), (gz, uz) = wgrad_both_ways(shape, inp, shape.cap, seed=K)
+    assert torch.equal(gw.view(torch.int32), gz.view(torch.int32))
+    assert torch.equal(uw.view(torch.int32), uz.view(torch.int32))
+
+
+@pytest.mark.parametrize("name", ["ep_share_small", "long_small", "sparse"])
+def test_zero_copy_training_step_equals_copy_step(name):
+    """A whole forward and backward with no x_perm at all: every output of the step bit for bit the copy
+    path's, and the weight gradients within tolerance of the oracle."""
+    shape = SPARSE if name == "sparse" else SHAPES[name]
+    inp = synth.make_inputs(shape, seed=19, d_out=True)
+    dev = pipeline.to_device(inp)
+    a = pipeline.MoeBuffers.allocate(shape, backward=True)
+    b = pipeline.MoeBuffers.allocate(shape, backward=True, zero_copy=True)
+    assert b.x_perm is None
+    for buf in (a, b):
+        pipeline.forward(buf, dev)
+        pipeline.backward(buf, dev)
+    torch.cuda.synchronize()
+    for f in ("out", "dx", "dlogits"):
+        assert torch.equal(getattr(a, f).view(torch.int16 if getattr(a, f).dtype == torch.bfloat16 else torch.int32),
+                           getattr(b, f).view(torch.int16 if getattr(b, f).dtype == torch.bfloat16 else torch.int32)), f
+    for f in ("dw_gate", "dw_up", "dw_down"):
+        assert torch.equal(getattr(a, f).view(torch.int32), getattr(b, f).view(torch.int32)), f
+    o = oracle.forward(inp, shape.e_begin, shape.EL, shape.K, shape.cap)
+    ob = oracle.backward(inp, o, shape.cap)
+    assert_close("dw_gate", bits(b.dw_gate), ob["dw_gate"])
+    assert_close("dw_up", bits(b.dw_up), ob["dw_up"])
