@@ -675,16 +675,17 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
         const int k0 = kt * BK;
         // re-materialise the lane terms each load (cheap adds) rather than
         // keeping one hoisted offset per load alive across the loop: the terms
-        // pass through an opaque copy, one v_mov each per load.  The weight
-        // gradient uses two of them, the dgrad GEMMs (contraction-contiguous
-        // weights) take the one each load needs; the forward GEMMs keep all
-        // four, which measured faster for them (the backward ones gain 2%).
+        // pass through an opaque copy, one v_mov per load.  The row-tiled GEMMs
+        // copy just the term each load needs; copying all four per load cost
+        // the forward GEMMs 24 VALU instructions per stage, and with one wave
+        // per SIMD the stage's instruction stream is what its time follows
+        // (gate/up 4% slower).  The weight gradient copies two.
         uint32_t la0 = lt_a0, la1 = lt_a1, lb0 = lt_b0, lb1 = lt_b1;
         auto lane_term = [](uint32_t v) {
             asm volatile("" : "+v"(v));
             return v;
         };
-        constexpr bool kEachLoad = SCHED == SCHED_ROWS && LB == LAY_KC;
+        constexpr bool kEachLoad = SCHED == SCHED_ROWS;
         if constexpr (SCHED == SCHED_WGRAD) asm volatile("" : "+v"(la0), "+v"(lb0));
         else if constexpr (!kEachLoad) asm volatile("" : "+v"(la0), "+v"(la1), "+v"(lb0), "+v"(lb1));
         {
@@ -738,8 +739,9 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
                         r = c_srdB0;
                         col = ic.ni * BN + sub * 64;
                     }
+                    const uint32_t lbt = kEachLoad ? lane_term(lb0) : lb0;
                     const uint32_t voff =
-                        col < p.N ? lb0 + (uint32_t)(((mn_kr(u - LA) * 8 + k0) * p.ldw + col) * 2) : kOOB;
+                        col < p.N ? lbt + (uint32_t)(((mn_kr(u - LA) * 8 + k0) * p.ldw + col) * 2) : kOOB;
                     if constexpr (NTB) lds_load16_nt(r, sB + q * 1024, live ? voff : kOOB);
                     else lds_load16(r, sB + q * 1024, live ? voff : kOOB);
                 } else {
