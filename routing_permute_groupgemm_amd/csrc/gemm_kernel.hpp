@@ -290,9 +290,12 @@ struct Tile {
 // The GEMM of one workgroup for one tile shape.  smem is the stage ring;
 // s_off holds the clamped row offsets (already loaded); s_start and s_wave are
 // scratch for the schedule; s_idx (GATHER only) holds the prefetched source
-// indices of the A rows.  NTB: every expert fits one row tile, so each weight
+// indices of the A rows.  FULLC: every tile's columns (and, for the weight
+// gradient, rows) lie inside the output, so the loads skip those bounds
+// checks.  NTB: every expert fits one row tile, so each weight
 // byte is read once and the weight loads carry the non-temporal hint.
-template <int BM, int BN, int BK, int WM, int WN, int LB, int EPI, int SCHED, int LDSB, bool GATHER, bool NTB>
+template <int BM, int BN, int BK, int WM, int WN, int LB, int EPI, int SCHED, int LDSB, bool GATHER, bool NTB,
+          bool FULLC = false>
 __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, const int* s_off, int* s_start,
                                         int* s_wave, int* s_idx) {
     using TL = Tile<BM, BN, BK, WM, WN, LDSB>;
@@ -322,6 +325,11 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
                             (MOE_GEMM_MFMA16_WGRAD && EPI == EPI_F32 && SCHED == SCHED_WGRAD)) &&
                            BM == 256 && BN == 256 && WM == 2 && WN == 2 && BK == 32;
     constexpr int MB16 = kMf16 ? BM / WM / 16 : 1;  // 16-row blocks per wave
+    // Past the last tile the cursor's loads read zeros: through descriptors of
+    // range 0 (no per-load select), or, in the 16x16x32 body, whose registers
+    // are the scarcest (the descriptors kept in scalar registers made it spill
+    // in its stage loop), through the out-of-range offset chosen per load.
+    constexpr bool kSrdLive = !kMf16;
     constexpr int NB16 = kMf16 ? BN / WN / 16 : 1;  // 16-column blocks per wave
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -584,6 +592,12 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
             // opaque from here on: kept in SGPRs rather than rebuilt from the
             // tile indices in every stage
             asm volatile("" : "+s"(c_srdA), "+s"(c_srdB0), "+s"(c_srdB1));
+        } else if (SCHED == SCHED_ROWS && kSrdLive) {
+            // no tile left: descriptors of range 0, so every load the cursor
+            // still issues (to keep the count per stage fixed) reads zeros
+            c_srdA = make_srd(p.a, 0);
+            c_srdB0 = c_srdB1 = make_srd(p.a, 0);
+            asm volatile("" : "+s"(c_srdA), "+s"(c_srdB0), "+s"(c_srdB1));
         }
         if (SCHED == SCHED_WGRAD && itile < n_tiles_total) {
             c_rowA = (uint64_t)(p.a + (int64_t)ic.row0 * p.lda);
@@ -636,9 +650,10 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
     seek();
 
     // Load u (0..LPW-1) of this wave for stage kt of the issue cursor's tile
-    // into LDS slot `slot`.  With live == false (no tile left) it loads from
-    // the out-of-range offset: zeros, no memory traffic, and the same number
-    // of loads per stage, so the vmcnt bookkeeping stays fixed.
+    // into LDS slot `slot`.  With no tile left the cursor's descriptors have
+    // range 0 (seek, stage_srd), so its loads read zeros with no memory
+    // traffic, and every stage keeps the same number of loads, so the vmcnt
+    // bookkeeping stays fixed.
     // Weight gradient: the buffer descriptors of one stage (its BK rows of A
     // and of B, cut at the group's last row, so rows past it load zeros),
     // built once per stage rather than once per load.
@@ -649,10 +664,12 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
     auto stage_srd = [&](int kt) {
         StageSrd r{};
         if constexpr (kGW) {
-            // the lane's row of the stage and its token (fetched two stages ago)
+            // the lane's row of the stage and its token (fetched two stages ago);
+            // no tile left: descriptors of range 0 (loads of zeros)
             const int k0 = kt * BK;
-            const uint32_t rows = (uint32_t)max(0, min(BK, ic.valid - k0));
-            r.a = c_srdA;
+            const bool live = itile < n_tiles_total;
+            const uint32_t rows = live ? (uint32_t)max(0, min(BK, ic.valid - k0)) : 0u;
+            r.a = live ? c_srdA : make_srd(p.a, 0);
             r.b = make_srd((const uint16_t*)c_rowB + (int64_t)k0 * p.ldb, rows * (uint32_t)(p.ldb * 2));
             const int ln = lane_id_here();
             const uint32_t v = (uint32_t)*(const MOE_LDS int*)(s_idx + ((tk & 1) * TL::kWaves + wave) * 64 + (ln >> 3));
@@ -662,8 +679,9 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
             r.arow = k0 + 8 * wave + (ln >> 3) < ic.valid && tok < (uint32_t)p.a_rows ? tok * (uint32_t)(p.lda * 2)
                                                                                        : kOOB_GATHER;
         } else if constexpr (SCHED == SCHED_WGRAD) {
+            // no tile left: range 0 (loads of zeros)
             const int k0 = kt * BK;
-            const uint32_t rows = (uint32_t)max(0, min(BK, ic.valid - k0));
+            const uint32_t rows = itile < n_tiles_total ? (uint32_t)max(0, min(BK, ic.valid - k0)) : 0u;
             r.a = make_srd((const uint16_t*)c_rowA + (int64_t)k0 * p.lda, rows * (uint32_t)(p.lda * 2));
             r.b = make_srd((const uint16_t*)c_rowB + (int64_t)k0 * p.ldb, rows * (uint32_t)(p.ldb * 2));
         }
@@ -708,24 +726,26 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
                         if (kEachLoad) lt = lane_term(lt);
                         voff = lt + (uint32_t)((q * LY::kRowsPerLoad * p.lda + k0) * 2);
                     }
-                    lds_load16(c_srdA, sA + q * 1024, live ? voff : (GATHER ? kOOB_GATHER : kOOB));
+                    lds_load16(c_srdA, sA + q * 1024, kSrdLive || live ? voff : (GATHER ? kOOB_GATHER : kOOB));
                 } else if (kGW) {
                     // the row term is the lane's token row (mn_kr(u) is the wave, so the
                     // stage's row of this lane is the one stage_srd looked up)
                     const int col = ic.mi_w * BM + mn_sub(u) * 64;
-                    const uint32_t voff = col < p.M ? ss.arow + la0 + (uint32_t)(col * 2) : kOOB_GATHER;
-                    lds_load16(ss.a, sA + q * 1024, live ? voff : kOOB_GATHER);
+                    const uint32_t voff = FULLC || col < p.M ? ss.arow + la0 + (uint32_t)(col * 2) : kOOB_GATHER;
+                    lds_load16(ss.a, sA + q * 1024, voff);
                 } else {
                     const int col = ic.mi_w * BM + mn_sub(u) * 64;
-                    const uint32_t voff = col < p.M ? la0 + (uint32_t)((mn_kr(u) * 8 * p.lda + col) * 2) : kOOB;
-                    lds_load16(ss.a, sA + q * 1024, live ? voff : kOOB);
+                    const uint32_t voff =
+                        FULLC || col < p.M ? la0 + (uint32_t)((mn_kr(u) * 8 * p.lda + col) * 2) : kOOB;
+                    lds_load16(ss.a, sA + q * 1024, voff);
                 }
             } else {
                 const int q = (u - LA) * TL::kWaves + wave;
                 if (SCHED == SCHED_WGRAD) {
                     const int col = ic.ni * BN + mn_sub(u - LA) * 64;
-                    const uint32_t voff = col < p.N ? lb0 + (uint32_t)((mn_kr(u - LA) * 8 * p.ldb + col) * 2) : kOOB;
-                    lds_load16(ss.b, sB + q * 1024, live ? voff : kOOB);
+                    const uint32_t voff =
+                        FULLC || col < p.N ? lb0 + (uint32_t)((mn_kr(u - LA) * 8 * p.ldb + col) * 2) : kOOB;
+                    lds_load16(ss.b, sB + q * 1024, voff);
                 } else if (LB == LAY_MN) {
                     // weight [Kd][ldw], N contiguous: [BK][64] sub-tiles
                     const int sub = mn_sub(u - LA);
@@ -741,9 +761,9 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
                     }
                     const uint32_t lbt = kEachLoad ? lane_term(lb0) : lb0;
                     const uint32_t voff =
-                        col < p.N ? lbt + (uint32_t)(((mn_kr(u - LA) * 8 + k0) * p.ldw + col) * 2) : kOOB;
-                    if constexpr (NTB) lds_load16_nt(r, sB + q * 1024, live ? voff : kOOB);
-                    else lds_load16(r, sB + q * 1024, live ? voff : kOOB);
+                        FULLC || col < p.N ? lbt + (uint32_t)(((mn_kr(u - LA) * 8 + k0) * p.ldw + col) * 2) : kOOB;
+                    if constexpr (NTB) lds_load16_nt(r, sB + q * 1024, kSrdLive || live ? voff : kOOB);
+                    else lds_load16(r, sB + q * 1024, kSrdLive || live ? voff : kOOB);
                 } else {
                     // weight [N][Kd], contraction contiguous; second segment from w1
                     const bool seg1 = p.two_seg && k0 >= p.Kd;
@@ -751,7 +771,7 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
                     const int kk0 = seg1 ? k0 - p.Kd : k0;
                     const uint32_t lt = lane_term(LY::kc_period(q) ? lb1 : lb0);
                     const uint32_t voff = lt + (uint32_t)((q * LY::kRowsPerLoad * p.ldw + kk0) * 2);
-                    lds_load16(r, sB + q * 1024, live ? voff : kOOB);
+                    lds_load16(r, sB + q * 1024, kSrdLive || live ? voff : kOOB);
                 }
             }
         }
@@ -1542,9 +1562,28 @@ void gg_kernel(GemmParams p) {
             return;
         }
     }
+    // the 256 x 256 body also comes without the loads' column bounds checks,
+    // for outputs whose every tile is whole (all the layer's workloads)
+    constexpr bool kFullBody = BM == 256 && BN == 256;
+    const bool fullc = kFullBody && (SCHED == SCHED_WGRAD ? p.M % BM == 0 && p.N % BN == 0
+                                                          : p.N % (EPI == EPI_SWIGLU ? BN / 2 : BN) == 0);
     if constexpr (kNtPath) {
         if (max_rows <= BM) {
+            if constexpr (kFullBody) {
+                if (fullc) {
+                    gg_body<BM, BN, BK, WM, WN, LB, EPI, SCHED, LDSB, GATHER, true, true>(p, smem, s_off, s_start,
+                                                                                          s_wave, s_idx);
+                    return;
+                }
+            }
             gg_body<BM, BN, BK, WM, WN, LB, EPI, SCHED, LDSB, GATHER, true>(p, smem, s_off, s_start, s_wave, s_idx);
+            return;
+        }
+    }
+    if constexpr (kFullBody) {
+        if (fullc) {
+            gg_body<BM, BN, BK, WM, WN, LB, EPI, SCHED, LDSB, GATHER, false, true>(p, smem, s_off, s_start, s_wave,
+                                                                                   s_idx);
             return;
         }
     }
