@@ -495,7 +495,11 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
     // once per tile: the A rows, and the B weight of each half / segment
     i32x4 c_srdA = {0, 0, 0, 0}, c_srdB0 = {0, 0, 0, 0}, c_srdB1 = {0, 0, 0, 0};
     // weight gradient: the group's first A and B rows
-    uint64_t c_rowA = 0, c_rowB = 0;
+    // (c_stA, c_stB: the cursor stage's first A and B rows, c_rem the group's
+    // rows from there on; stepped by one stage per advance rather than rebuilt
+    // from the stage index, which took 64-bit products per stage)
+    uint64_t c_stA = 0, c_stB = 0;
+    int c_rem = 0;
 
     // Gathered A rows (GATHER): one descriptor over all of a; per lane, the
     // byte offset of the row behind each of its LA loads (kOOB past the
@@ -600,9 +604,10 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
             asm volatile("" : "+s"(c_srdA), "+s"(c_srdB0), "+s"(c_srdB1));
         }
         if (SCHED == SCHED_WGRAD && itile < n_tiles_total) {
-            c_rowA = (uint64_t)(p.a + (int64_t)ic.row0 * p.lda);
-            c_rowB = (uint64_t)(p.b + (int64_t)ic.row0 * p.ldb);
-            asm volatile("" : "+s"(c_rowA), "+s"(c_rowB));
+            c_stA = (uint64_t)(p.a + (int64_t)ic.row0 * p.lda);
+            c_stB = (uint64_t)(p.b + (int64_t)ic.row0 * p.ldb);
+            c_rem = ic.valid;
+            asm volatile("" : "+s"(c_stA), "+s"(c_stB), "+s"(c_rem));
         }
         if (kGW) {
             for (itile_n = itile + G; itile_n < n_tiles_total; itile_n += G) {
@@ -636,6 +641,11 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
             ik = 0;
             itile += G;
             seek();
+        } else if constexpr (SCHED == SCHED_WGRAD) {
+            // the next stage of the same group (or no tile left: unused)
+            c_stA += (uint64_t)(BK * 2) * (uint64_t)p.lda;
+            c_stB += (uint64_t)(BK * 2) * (uint64_t)p.ldb;
+            c_rem -= BK;
         }
         if constexpr (kGW) {
             ++tk;
@@ -666,24 +676,24 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
         if constexpr (kGW) {
             // the lane's row of the stage and its token (fetched two stages ago);
             // no tile left: descriptors of range 0 (loads of zeros)
-            const int k0 = kt * BK;
+            (void)kt;  // the cursor's stage: c_stB, c_rem
             const bool live = itile < n_tiles_total;
-            const uint32_t rows = live ? (uint32_t)max(0, min(BK, ic.valid - k0)) : 0u;
+            const uint32_t rows = live ? (uint32_t)max(0, min(BK, c_rem)) : 0u;
             r.a = live ? c_srdA : make_srd(p.a, 0);
-            r.b = make_srd((const uint16_t*)c_rowB + (int64_t)k0 * p.ldb, rows * (uint32_t)(p.ldb * 2));
+            r.b = make_srd((const void*)c_stB, rows * (uint32_t)(p.ldb * 2));
             const int ln = lane_id_here();
             const uint32_t v = (uint32_t)*(const MOE_LDS int*)(s_idx + ((tk & 1) * TL::kWaves + wave) * 64 + (ln >> 3));
             // src = t*K + k; the quotient estimate is t or t - 1
             uint32_t tok = __umulhi(v, p.topk_rcp);
             if (v - tok * (uint32_t)p.topk >= (uint32_t)p.topk) ++tok;
-            r.arow = k0 + 8 * wave + (ln >> 3) < ic.valid && tok < (uint32_t)p.a_rows ? tok * (uint32_t)(p.lda * 2)
-                                                                                       : kOOB_GATHER;
+            r.arow = 8 * wave + (ln >> 3) < c_rem && tok < (uint32_t)p.a_rows ? tok * (uint32_t)(p.lda * 2)
+                                                                               : kOOB_GATHER;
         } else if constexpr (SCHED == SCHED_WGRAD) {
-            // no tile left: range 0 (loads of zeros)
-            const int k0 = kt * BK;
-            const uint32_t rows = itile < n_tiles_total ? (uint32_t)max(0, min(BK, ic.valid - k0)) : 0u;
-            r.a = make_srd((const uint16_t*)c_rowA + (int64_t)k0 * p.lda, rows * (uint32_t)(p.lda * 2));
-            r.b = make_srd((const uint16_t*)c_rowB + (int64_t)k0 * p.ldb, rows * (uint32_t)(p.ldb * 2));
+            // the cursor's stage (c_stA, c_stB, c_rem); no tile left: range 0 (loads of zeros)
+            (void)kt;
+            const uint32_t rows = itile < n_tiles_total ? (uint32_t)max(0, min(BK, c_rem)) : 0u;
+            r.a = make_srd((const void*)c_stA, rows * (uint32_t)(p.lda * 2));
+            r.b = make_srd((const void*)c_stB, rows * (uint32_t)(p.ldb * 2));
         }
         return r;
     };
