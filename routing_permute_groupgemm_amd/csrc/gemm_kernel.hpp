@@ -1254,6 +1254,7 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
             static_assert(kRounds % kBufs == 0, "rounds in whole pairs");
 #pragma unroll
             for (int mt = 0; mt < MTW; ++mt) {
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int np0 = 0; np0 < kRounds; np0 += kBufs) {
 #pragma unroll
@@ -1264,7 +1265,7 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
 #pragma unroll
                             for (int j4 = 0; j4 < 4; ++j4) {
                                 if (EPI == EPI_BF16) {
-                                    u32x2 w = {pack_bf2(a[4 * j4], a[4 * j4 + 1]), pack_bf2(a[4 * j4 + 2], a[4 * j4 + 3])};
+                                    u32x2 w = {pack_bf2x(a[4 * j4], a[4 * j4 + 1]), pack_bf2x(a[4 * j4 + 2], a[4 * j4 + 3])};
                                     *(MOE_LDS u32x2*)(stage_addr(b, r, 4 * q + j4) + 8 * h) = w;
                                 } else {
                                     f32x4 w = {a[4 * j4], a[4 * j4 + 1], a[4 * j4 + 2], a[4 * j4 + 3]};

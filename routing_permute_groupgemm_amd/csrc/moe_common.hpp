@@ -36,6 +36,15 @@ __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
     return f2bf(lo) | (f2bf(hi) << 16);
 }
 
+// The same pair converted by one packed conversion instruction (identical
+// rounding on each half).
+__device__ __forceinline__ uint32_t pack_bf2x(float lo, float hi) {
+    typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+    const bf16x2_t v = __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t);
+    return __builtin_bit_cast(uint32_t, v);
+}
+
 // Buffer resource for raw (unstructured) buffer loads: `bytes` bounds the
 // valid range; loads at or past it return zero (and write zero to LDS for
 // LDS-direct loads).
