@@ -1042,6 +1042,13 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
                 issue_loads(0);
 #pragma unroll
                 for (int m = 0; m < MB16; ++m) {
+                    // An empty asm that reads and rewrites this block's accumulators in
+                    // AGPRs keeps the compiler from copying later blocks into VGPRs at
+                    // the start of the epilogue; without it the 256-row body ran out of
+                    // VGPRs and spilled, and each reload waited for every store issued
+                    // before it.  (The 32x32 epilogues do not gain from the same.)
+#pragma unroll
+                    for (int nb = 0; nb < NB16; ++nb) asm volatile("" : "+a"(acc16[m][nb]));
 #pragma unroll
                     for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
