@@ -62,6 +62,9 @@ constexpr int kLdsBudget = 128 * 1024;  // LDS per workgroup for the stage ring
 #ifndef MOE_GEMM_DGRAD_STAGED
 #define MOE_GEMM_DGRAD_STAGED 1  // 0: the down dgrad's epilogue loads and stores straight from the MFMA layout
 #endif
+#ifndef MOE_GEMM_DGRAD_PREFETCH
+#define MOE_GEMM_DGRAD_PREFETCH 2  // 16-row blocks of saved (a, b) rows in flight in the staged epilogue
+#endif
 #ifndef MOE_GEMM_MFMA16_WGRAD
 #define MOE_GEMM_MFMA16_WGRAD 0  // 1: the weight gradient's too (measured 5% slower, so off)
 #endif
@@ -1012,8 +1015,8 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
                 // one 16-row block at a time, a in its first 4 KiB and b in the
                 // second (16 rows x 256 bytes each, 16-byte chunks XOR-swizzled by
                 // row).  Each lane reads its MFMA-layout values from there, writes
-                // (da, db) over them, and the rows go back out whole.  The next
-                // block's rows are loaded while this block is worked on.
+                // (da, db) over them, and the rows go back out whole.  The rows of
+                // the next kPre blocks are in flight while a block is worked on.
                 static_assert(TL::kStage / TL::kWaves >= 8192 && BN / WN == 128, "staging space per wave");
                 uint8_t* stg = smem + ((gs + S - 1) % S) * TL::kStage + wave * 8192;
                 const int ln = lane_id_here();
@@ -1024,22 +1027,25 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
                 const int rw = ln >> 4, cc = ln & 15;
                 const int ncol = ni * BN + wn * (BN / WN) + 8 * cc;  // the chunk's first column
                 const bool col_ok = ncol < p.N;
-                u32x4 ld[2][4];
+                constexpr int kPre = MOE_GEMM_DGRAD_PREFETCH;
+                u32x4 ld[kPre][2][4];
                 auto issue_loads = [&](int m) {
+                    u32x4(&l)[2][4] = ld[m % kPre];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int mloc = row16(m) + 4 * i + rw;
-                        ld[0][i] = ld[1][i] = u32x4{0u, 0u, 0u, 0u};
+                        l[0][i] = l[1][i] = u32x4{0u, 0u, 0u, 0u};
                         if (mloc < valid && col_ok) {
                             const uint16_t* src = p.ab + (int64_t)(row0 + mloc) * 2 * p.N + ncol;
-                            ld[0][i] = *(const u32x4*)src;
-                            ld[1][i] = *(const u32x4*)(src + p.N);
+                            l[0][i] = *(const u32x4*)src;
+                            l[1][i] = *(const u32x4*)(src + p.N);
                         }
                     }
                 };
                 // MFMA layout: row ln%16, columns 4q..4q+3 of each 16-column block
                 const int r = ln & 15, q = ln >> 4;
-                issue_loads(0);
+#pragma unroll
+                for (int m = 0; m < kPre && m < MB16; ++m) issue_loads(m);
 #pragma unroll
                 for (int m = 0; m < MB16; ++m) {
                     // An empty asm that reads and rewrites this block's accumulators in
@@ -1052,9 +1058,9 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
 #pragma unroll
                     for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) *(MOE_LDS u32x4*)sa(hb, 4 * i + rw, cc) = ld[hb][i];
+                        for (int i = 0; i < 4; ++i) *(MOE_LDS u32x4*)sa(hb, 4 * i + rw, cc) = ld[m % kPre][hb][i];
                     asm volatile("" ::: "memory");  // a wave's LDS accesses execute in order
-                    if (m + 1 < MB16) issue_loads(m + 1);
+                    if (m + kPre < MB16) issue_loads(m + kPre);
 #pragma unroll
                     for (int nb = 0; nb < NB16; ++nb) {
                         MOE_LDS uint8_t* pa = sa(0, r, 2 * nb + (q >> 1)) + 8 * (q & 1);
