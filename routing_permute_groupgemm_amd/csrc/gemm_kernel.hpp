@@ -1078,8 +1078,8 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
                             db[i] = u * a;
                             da[i] = __builtin_fmaf(w, __builtin_fmaf(-a, sg, a), w);
                         }
-                        *(MOE_LDS u32x2*)pa = u32x2{pack_bf2(da[0], da[1]), pack_bf2(da[2], da[3])};
-                        *(MOE_LDS u32x2*)pb = u32x2{pack_bf2(db[0], db[1]), pack_bf2(db[2], db[3])};
+                        *(MOE_LDS u32x2*)pa = u32x2{pack_bf2x(da[0], da[1]), pack_bf2x(da[2], da[3])};
+                        *(MOE_LDS u32x2*)pb = u32x2{pack_bf2x(db[0], db[1]), pack_bf2x(db[2], db[3])};
                     }
                     asm volatile("" ::: "memory");
 #pragma unroll
@@ -1383,7 +1383,7 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
                         float hv[4];
 #pragma unroll
                         for (int i = 0; i < 4; ++i) hv[i] = silu_f(ga[4 * j4 + i]) * ub[4 * j4 + i];
-                        put(0, i2, j4, u32x2{pack_bf2(hv[0], hv[1]), pack_bf2(hv[2], hv[3])});
+                        put(0, i2, j4, u32x2{pack_bf2x(hv[0], hv[1]), pack_bf2x(hv[2], hv[3])});
                     }
                 }
                 if (p.c2) {
