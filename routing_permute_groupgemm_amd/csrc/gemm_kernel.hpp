@@ -1267,6 +1267,9 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
             static_assert(kRounds % kBufs == 0, "rounds in whole pairs");
 #pragma unroll
             for (int mt = 0; mt < MTW; ++mt) {
+                // one row block after another (the scheduler does not interleave
+                // blocks); with the packed pair conversion below, the 256-row
+                // bodies of this epilogue do not spill
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int np0 = 0; np0 < kRounds; np0 += kBufs) {
@@ -1361,7 +1364,8 @@ __device__ __forceinline__ void gg_body(const GemmParams& p, uint8_t* smem, cons
             auto put = [&](int buf, int i2, int j4, u32x2 w) {
                 *(MOE_LDS u32x2*)(stage_addr(buf, r, 4 * i2 + j4) + 8 * hh) = w;
             };
-            // the saved a (or b) values of block mt, into staging block buf
+            // the saved a (or b) values of block mt, into staging block buf (with
+            // single conversions: the packed form made this body spill)
             auto put_ab = [&](int buf, int mt, int half) {
 #pragma unroll
                 for (int i2 = 0; i2 < 2; ++i2) {
