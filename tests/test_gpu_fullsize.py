@@ -50,11 +50,12 @@ def case(request):
     torch.cuda.empty_cache()
 
 
-def sample_rows(c, n_random=24, whole_tiles=False):
+def sample_rows(c, n_random=128, whole_tiles=False):
     """Rows at the ends and middle of the first, last, largest and smallest experts plus random rows;
-    with whole_tiles, also every row of two whole 256-row GEMM tiles: the largest expert's first tile
-    and the last expert's last (ragged) tile, so that every lane, MFMA row block and epilogue row of
-    those tiles is compared element by element."""
+    with whole_tiles, also every row of five whole 256-row GEMM tiles: the largest expert's first tile,
+    the last expert's last (ragged) tile, the smallest expert's first tile and a tile in the middle of
+    each of two randomly chosen experts, so that every lane, MFMA row block and epilogue row of those
+    tiles is compared element by element."""
     off = c.ref_pm["offsets"]
     counts = np.diff(off)
     nz = np.nonzero(counts)[0]
@@ -72,6 +73,13 @@ def sample_rows(c, n_random=24, whole_tiles=False):
         j = nz[-1]
         lo, hi = int(off[j]), int(min(off[j + 1], c.shape.cap))
         rows |= set(range(lo + (hi - lo - 1) // 256 * 256, hi))
+        j = nz[np.argmin(counts[nz])]
+        lo, hi = int(off[j]), int(min(off[j + 1], c.shape.cap))
+        rows |= set(range(lo, min(hi, lo + 256)))
+        for j in c.rng.choice(nz, 2):
+            lo, hi = int(off[j]), int(min(off[j + 1], c.shape.cap))
+            t0 = lo + ((hi - lo) // 2) // 256 * 256
+            rows |= set(range(t0, min(hi, t0 + 256)))
     return np.array(sorted(r for r in rows if r < c.R), np.int64)
 
 
@@ -142,7 +150,7 @@ def test_combine_sampled_tokens(case):
     out = _lib.moe_combine(yd, c.buf.pos, c.buf.gates)
     out1 = _lib.moe_combine(yd, c.buf.pos, None)
     torch.cuda.synchronize()
-    toks = np.unique(np.concatenate([[0, s.T - 1], c.rng.integers(0, s.T, 48),
+    toks = np.unique(np.concatenate([[0, s.T - 1], c.rng.integers(0, s.T, 512),
                                      np.nonzero(np.all(c.ref_pm["pos"] < 0, axis=1))[0][:4]])).astype(np.int64)
     # gates: the oracle's own (bit-exact indices; gate values are the oracle's)
     ref = oracle.combine(yin, c.ref_pm["pos"], c.ref_g, tokens=toks)
@@ -160,7 +168,7 @@ def test_gather_sampled_rows(case):
     c = case
     _bwd_only(c)
     s = c.shape
-    rows = sample_rows(c)
+    rows = sample_rows(c, whole_tiles=True)
     ref = oracle.bwd_gather(c.inp["d_out"], c.ref_pm["src"], c.ref_pm["offsets"], c.ref_g, s.K, s.cap)
     assert_close("dy_perm", bits(c.buf.dy_perm)[rows], ref[rows])
 
@@ -214,8 +222,11 @@ def test_wgrad_sampled(case, which):
     torch.cuda.synchronize()
     assert torch.equal(dw.view(torch.int32), dw2.view(torch.int32)), "wgrad rerun differs"
     counts = c.ref_pm["counts"]
-    groups = np.unique([int(np.argmax(counts)), int(np.argmin(counts)), 0]).astype(np.int32)
-    cols = np.unique(np.concatenate([[0, N - 1], c.rng.integers(0, N, 10)])).astype(np.int32)
+    groups = np.unique([int(np.argmax(counts)), int(np.argmin(counts)), 0, s.EL - 1,
+                        *c.rng.integers(0, s.EL, 3).tolist()]).astype(np.int32)
+    # both ends, the columns on either side of each of the first 256-column tile edges, and random ones
+    edges = [e + d for e in range(256, min(N, 1024), 256) for d in (-1, 0)]
+    cols = np.unique(np.concatenate([[0, N - 1], edges, c.rng.integers(0, N, 64)])).astype(np.int32)
     ref = np.zeros((s.EL, M, N), np.float32)
     oracle.wgrad(A, lda, B, ldb, c.ref_pm["offsets"], M, N, s.cap, groups=groups, cols=cols, out=ref)
     got = dw.cpu().numpy()
