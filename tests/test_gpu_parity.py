@@ -374,3 +374,57 @@ def test_binding_rejects_undersized_outputs():
         _lib.moe_grouped_gemm_swiglu(buf.x_perm, dev["w_gate"], dev["w_up"], buf.offsets, buf.cap,
                                      h=torch.empty((buf.cap - 1, shape.F), dtype=torch.bfloat16, device="cuda"))
     torch.cuda.synchronize()
+
+
+def _bf16_exact(x):
+    """bf16 bit patterns of float32 values that bf16 represents exactly (checked)."""
+    u = np.ascontiguousarray(x, np.float32).view(np.uint32)
+    assert not np.any(u & 0xFFFF), "value not exactly representable in bf16"
+    return (u >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("trans_w", [0, 1])
+@pytest.mark.parametrize("tile", ["0", "256", "192", "128"])
+def test_bf16_epilogue_rounds_exact_ties_to_even(trans_w, tile, monkeypatch):
+    """The plain bf16 epilogue (down GEMM: weights [Kd][N]; dgrad bodies: [N][Kd]) on dot products that
+    are exact in fp32 and sit on a bf16 rounding tie (both parities of the mantissa below it) or one fp32
+    step to either side of one: the stored bits must equal the oracle's round-to-nearest-even exactly.
+    Two non-zero terms per row make every sum exact, so the order of accumulation cannot matter."""
+    monkeypatch.setenv("MOE_GEMM_TILE", tile)
+    rng = np.random.default_rng(5)
+    counts = np.array([300, 211], np.int32)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R, EL, Kd, N = int(offsets[-1]), len(counts), 64, 320
+    e = rng.integers(-20, 20, R).astype(np.float64)
+    kind = rng.integers(0, 5, R)
+    big = 2.0 ** e
+    # relative to the bf16 ulp 2^(e-7) of big: half an ulp above an odd or an even mantissa (exact ties),
+    # and just above and below a tie
+    small = np.select([kind == 0, kind == 1, kind == 2, kind == 3],
+                      [3 * 2.0 ** (e - 8), 2.0 ** (e - 8), 2.0 ** (e - 8) * (1 + 2.0 ** -7),
+                       2.0 ** (e - 9) * (2 - 2.0 ** -7)], 2.0 ** (e - 8) * 5)
+    a = rng.standard_normal((R, Kd)).astype(np.float32)
+    a[:, 0] = big
+    a[:, 1] = small
+    # the other columns: any bf16 values (their weights are 0)
+    a_bits = _bf16_exact((a.view(np.uint32) & 0xFFFF0000).view(np.float32))
+    a_bits[:, 0] = _bf16_exact(big.astype(np.float32))
+    a_bits[:, 1] = _bf16_exact(small.astype(np.float32))
+    w = np.zeros((EL, Kd, N), np.float32)  # [Kd][N]: rows 0 and 1 scale by a power of two, the rest 0
+    scale = 2.0 ** ((np.arange(N) % 4) - 1)
+    w[:, 0, :] = scale
+    w[:, 1, :] = scale
+    w_bits = _bf16_exact(w)
+    ref = oracle.expert_down(a_bits, w_bits, offsets, R)
+    dev = pipeline.to_device(dict(a=a_bits, off=offsets))
+    wt = np.ascontiguousarray(w_bits.transpose(0, 2, 1)) if trans_w else w_bits
+    wdev = pipeline.to_device(dict(w=wt))["w"]
+    y = torch.empty((R, N), dtype=torch.bfloat16, device="cuda")
+    _lib.moe_grouped_gemm(dev["a"], wdev, None, trans_w, dev["off"], Kd, N, R, y)
+    torch.cuda.synchronize()
+    got = bits(y)
+    assert_equal("y", got, ref)
+    # the construction really exercises both tie directions
+    exact = (big + small)[:, None] * scale[None, :]
+    assert np.any((kind == 0)) and np.any(kind == 1)
+    assert np.all(np.float32(exact) == exact)
