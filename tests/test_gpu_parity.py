@@ -428,3 +428,35 @@ def test_bf16_epilogue_rounds_exact_ties_to_even(trans_w, tile, monkeypatch):
     exact = (big + small)[:, None] * scale[None, :]
     assert np.any((kind == 0)) and np.any(kind == 1)
     assert np.all(np.float32(exact) == exact)
+
+
+@pytest.mark.parametrize("gated", [True, False])
+def test_combine_rounds_exact_ties_to_even(gated):
+    """The combine (gated forward and ungated combine-gradient) on tokens whose K = 3 contributions (one of
+    them a row absent from the layer's share, pos < 0) sum exactly in fp32 to a bf16 tie of either mantissa
+    parity, or one step beside one: the stored bits must equal the oracle's round-to-nearest-even."""
+    rng = np.random.default_rng(9)
+    T, K, H = 777, 3, 192
+    e = rng.integers(-20, 20, (T, 1)).astype(np.float64)
+    kind = rng.integers(0, 5, (T, 1))
+    big = np.broadcast_to(2.0 ** e, (T, H))
+    small = np.select([kind == 0, kind == 1, kind == 2, kind == 3],
+                      [3 * 2.0 ** (e - 8), 2.0 ** (e - 8), 2.0 ** (e - 8) * (1 + 2.0 ** -7),
+                       2.0 ** (e - 9) * (2 - 2.0 ** -7)], 2.0 ** (e - 8) * 5)
+    small = np.broadcast_to(small, (T, H)) * np.where(rng.random((1, H)) < 0.5, 1.0, -1.0)
+    # rows: token t's contributions at rows 2t (big) and 2t + 1 (small); the third pair is absent
+    y = np.zeros((2 * T, H), np.float32)
+    y[0::2] = big / 2  # the gate 2 (a power of two) makes the products exact
+    y[1::2] = small
+    pos = np.stack([np.arange(T) * 2, np.full(T, -1), np.arange(T) * 2 + 1], axis=1).astype(np.int32)
+    g = np.stack([np.full(T, 2.0), np.full(T, 0.75), np.full(T, 1.0)], axis=1).astype(np.float32)
+    if not gated:
+        y[0::2] = big
+    y_bits = _bf16_exact(y)
+    ref = oracle.combine(y_bits, pos, g if gated else None)
+    dev = pipeline.to_device(dict(y=y_bits, pos=pos, g=g))
+    out = _lib.moe_combine(dev["y"], dev["pos"], dev["g"] if gated else None)
+    torch.cuda.synchronize()
+    assert_equal("out", bits(out), ref)
+    exact = big + small
+    assert np.all(np.float32(exact) == exact)
