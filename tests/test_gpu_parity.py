@@ -460,3 +460,31 @@ def test_combine_rounds_exact_ties_to_even(gated):
     assert_equal("out", bits(out), ref)
     exact = big + small
     assert np.all(np.float32(exact) == exact)
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_gather_rounds_exact_ties_to_even(fused):
+    """The output-gradient gather (alone and fused with the gate gradient): g * dOut with dOut a signed
+    power of two and g chosen so that the fp32 product is exact and sits on a bf16 tie of either mantissa
+    parity, beside one, or on a representable value; the stored rows must equal the oracle's bits."""
+    rng = np.random.default_rng(13)
+    T, K, H = 600, 2, 128
+    d_out = (2.0 ** rng.integers(-12, 12, (T, H))) * np.where(rng.random((T, H)) < 0.5, 1.0, -1.0)
+    choices = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, 1 + 2.0 ** -7, 0.75, 1 + 2.0 ** -8 + 2.0 ** -20],
+                       np.float64)
+    g = choices[rng.integers(0, len(choices), (T, K))].astype(np.float32)
+    pos = (np.arange(T * K, dtype=np.int32).reshape(T, K))
+    d_bits = _bf16_exact(d_out.astype(np.float32))
+    offsets = np.array([0, T * K], np.int32)
+    ref = oracle.bwd_gather(d_bits, np.arange(T * K, dtype=np.int32), offsets, g, K, T * K)
+    dev = pipeline.to_device(dict(d=d_bits, pos=pos, g=g))
+    dy = torch.empty((T * K, H), dtype=torch.bfloat16, device="cuda")
+    if fused:
+        y = torch.zeros((T * K, H), dtype=torch.bfloat16, device="cuda")
+        _lib.moe_gather_gate_grad(dev["d"], dev["pos"], dev["g"], y, dy)
+    else:
+        _lib.moe_gather(dev["d"], dev["pos"], dev["g"], dy)
+    torch.cuda.synchronize()
+    assert_equal("dy_perm", bits(dy), ref)
+    exact = d_out[:, None, :] * g.astype(np.float64)[:, :, None]
+    assert np.all(np.float32(exact) == exact)
