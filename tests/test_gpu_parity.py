@@ -488,3 +488,58 @@ def test_gather_rounds_exact_ties_to_even(fused):
     assert_equal("dy_perm", bits(dy), ref)
     exact = d_out[:, None, :] * g.astype(np.float64)[:, :, None]
     assert np.all(np.float32(exact) == exact)
+
+
+def _int_bf16(rng, shape, lo, hi):
+    """bf16 bits of small integers (exact in bf16) drawn from [lo, hi]."""
+    return _bf16_exact(rng.integers(lo, hi + 1, shape).astype(np.float32))
+
+
+@pytest.mark.parametrize("tile", ["0", "256", "192", "128"])
+def test_gemms_exact_on_integer_operands(tile, monkeypatch):
+    """Every GroupGEMM data path on integer operands, whose products and sums are exact in fp32, so that
+    any order of accumulation gives the same sum and the stored bits must equal the oracle's exactly: a
+    row, column or k-step taken twice, skipped or taken from a neighbouring expert changes them.  Experts
+    sit at every row-block and tile edge; N is not a multiple of the tile width.  Checked: the saved
+    (a, b) of the gate/up GEMM (copy and zero-copy), the down GEMM, the gate/up dgrad over both
+    weights, and dW_gate, dW_up (one pass, copy and zero-copy) and dW_down in fp32."""
+    monkeypatch.setenv("MOE_GEMM_TILE", tile)
+    rng = np.random.default_rng(17)
+    counts = np.array(EDGE_COUNTS, np.int32)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R, EL, H, F, K = int(offsets[-1]), len(counts), 320, 192, 1
+    x = _int_bf16(rng, (R, H), -2, 2)
+    wg = _int_bf16(rng, (EL, H, F), -1, 1)
+    wu = _int_bf16(rng, (EL, H, F), -1, 1)
+    wd = _int_bf16(rng, (EL, F, H), -1, 1)
+    hin = _int_bf16(rng, (R, F), -2, 2)
+    dabin = _int_bf16(rng, (R, 2 * F), -2, 2)
+    dev = pipeline.to_device(dict(x=x, wg=wg, wu=wu, wd=wd, h=hin, dab=dabin, off=offsets,
+                                  src=np.arange(R, dtype=np.int32)))
+    h = torch.empty((R, F), dtype=torch.bfloat16, device="cuda")
+    ab = torch.empty((R, 2 * F), dtype=torch.bfloat16, device="cuda")
+    _lib.moe_grouped_gemm_swiglu(dev["x"], dev["wg"], dev["wu"], dev["off"], R, h=h, ab_save=ab)
+    abz = torch.empty_like(ab)
+    _lib.moe_grouped_gemm_swiglu_gather(dev["x"], dev["src"], K, dev["wg"], dev["wu"], dev["off"], R,
+                                        h=torch.empty_like(h), ab_save=abz)
+    y = torch.empty((R, H), dtype=torch.bfloat16, device="cuda")
+    _lib.moe_grouped_gemm(dev["h"], dev["wd"], None, 0, dev["off"], F, H, R, y)
+    dx = torch.empty((R, H), dtype=torch.bfloat16, device="cuda")
+    # [W_gate; W_up] as stored, [H][F] each: the contraction runs over F of both segments
+    _lib.moe_grouped_gemm(dev["dab"], dev["wg"], dev["wu"], 1, dev["off"], F, H, R, dx)
+    dwg, dwu = _lib.moe_wgrad_gate_up(dev["x"], dev["dab"], dev["off"], EL, R)
+    zwg, zwu = _lib.moe_wgrad_gate_up_gather(dev["x"], dev["src"], K, dev["dab"], dev["off"], EL, R)
+    dwd = _lib.moe_wgrad(dev["h"], F, dev["x"], H, dev["off"], EL, F, H, R)
+    torch.cuda.synchronize()
+    _, ref_ab = oracle.expert_up(x, wg, wu, offsets, R, want_ab=True)
+    assert_equal("ab_save", bits(ab), ref_ab)
+    assert_equal("ab_save (zero-copy)", bits(abz), ref_ab)
+    assert_equal("y", bits(y), oracle.expert_down(hin, wd, offsets, R))
+    assert_equal("dx_perm", bits(dx), oracle.bwd_up(dabin, wg, wu, offsets, R))
+    ref_g = oracle.wgrad(x, H, dabin, 2 * F, offsets, H, F, R)
+    ref_u = oracle.wgrad(x, H, dabin.reshape(-1)[F:], 2 * F, offsets, H, F, R)  # db: columns F.. of dab
+    assert_equal("dW_gate", dwg.cpu().numpy(), ref_g)
+    assert_equal("dW_up", dwu.cpu().numpy(), ref_u)
+    assert_equal("dW_gate (zero-copy)", zwg.cpu().numpy(), ref_g)
+    assert_equal("dW_up (zero-copy)", zwu.cpu().numpy(), ref_u)
+    assert_equal("dW_down", dwd.cpu().numpy(), oracle.wgrad(hin, F, x, H, offsets, F, H, R))
