@@ -339,3 +339,67 @@ def test_literal_zipf_bias_full_size_forward():
     h, _ = oracle.expert_up(pm["x_perm"], inp["w_gate"], inp["w_up"], pm["offsets"], shape.cap, rows=rows,
                             want_ab=False)
     assert_close("h", bits(buf.h)[rows], h[rows])
+
+
+def _int_bits(rng, shape, lo, hi):
+    """bf16 bits of integers drawn from [lo, hi] (|v| <= 2: exact in bf16), built through a lookup table."""
+    table = np.array([np.float32(v).view(np.uint32) >> 16 for v in range(lo, hi + 1)], np.uint16)
+    return table[rng.integers(0, hi - lo + 1, shape, dtype=np.int8)]
+
+
+def test_integer_operands_exact_at_full_size(case):
+    """The GroupGEMMs at full size on small-integer operands (products and sums exact in fp32 in any order,
+    so the stored bits must equal the oracle's exactly): the saved (a, b) of the gate/up GEMM and the down
+    GEMM on the sampled rows and whole tiles, and for training workloads the gate/up dgrad and dW_gate,
+    dW_up, dW_down on the sampled experts and columns."""
+    c = case
+    s = c.shape
+    rng = np.random.default_rng(23)
+    R = c.R
+    x = _int_bits(rng, (s.cap, s.H), -2, 2)
+    x[R:] = 0
+    wg = _int_bits(rng, (s.EL, s.H, s.F), -1, 1)
+    wu = _int_bits(rng, (s.EL, s.H, s.F), -1, 1)
+    wd = _int_bits(rng, (s.EL, s.F, s.H), -1, 1)
+    hin = _int_bits(rng, (s.cap, s.F), -2, 2)
+    d = pipeline.to_device(dict(x=x, wg=wg, wu=wu, wd=wd, h=hin))
+    h = torch.empty((s.cap, s.F), dtype=torch.bfloat16, device="cuda")
+    ab = torch.empty((s.cap, 2 * s.F), dtype=torch.bfloat16, device="cuda")
+    _lib.moe_grouped_gemm_swiglu(d["x"], d["wg"], d["wu"], c.buf.offsets, s.cap, h=h, ab_save=ab)
+    y = torch.empty((s.cap, s.H), dtype=torch.bfloat16, device="cuda")
+    _lib.moe_grouped_gemm(d["h"], d["wd"], None, 0, c.buf.offsets, s.F, s.H, s.cap, y)
+    torch.cuda.synchronize()
+    rows = sample_rows(c, whole_tiles=True)
+    off = c.ref_pm["offsets"]
+    _, ref_ab = oracle.expert_up(x, wg, wu, off, s.cap, rows=rows, want_ab=True)
+    assert_equal("ab_save", bits(ab)[rows], ref_ab[rows])
+    ref_y = oracle.expert_down(hin, wd, off, s.cap, rows=rows)
+    assert_equal("y", bits(y)[rows], ref_y[rows])
+    del h, ab, y
+    if not s.backward:
+        return
+    dab = _int_bits(rng, (s.cap, 2 * s.F), -2, 2)
+    dab[R:] = 0
+    d2 = pipeline.to_device(dict(dab=dab))
+    dx = torch.empty((s.cap, s.H), dtype=torch.bfloat16, device="cuda")
+    _lib.moe_grouped_gemm(d2["dab"], d["wg"], d["wu"], 1, c.buf.offsets, s.F, s.H, s.cap, dx)
+    dwg, dwu = _lib.moe_wgrad_gate_up(d["x"], d2["dab"], c.buf.offsets, s.EL, s.cap)
+    dwd = _lib.moe_wgrad(d["h"], s.F, d["x"], s.H, c.buf.offsets, s.EL, s.F, s.H, s.cap)
+    torch.cuda.synchronize()
+    ref_dx = oracle.bwd_up(dab, wg, wu, off, s.cap, rows=rows)
+    assert_equal("dx_perm", bits(dx)[rows], ref_dx[rows])
+    counts = c.ref_pm["counts"]
+    groups = np.unique([int(np.argmax(counts)), int(np.argmin(counts)), 0, s.EL - 1,
+                        *c.rng.integers(0, s.EL, 2).tolist()]).astype(np.int32)
+    for name, got, A, lda, B, ldb, M, N in (
+            ("dW_gate", dwg, x, s.H, dab, 2 * s.F, s.H, s.F),
+            ("dW_up", dwu, x, s.H, dab.reshape(-1)[s.F:], 2 * s.F, s.H, s.F),
+            ("dW_down", dwd, hin, s.F, x, s.H, s.F, s.H)):
+        edges = [e + dd for e in range(256, min(N, 1024), 256) for dd in (-1, 0)]
+        cols = np.unique(np.concatenate([[0, N - 1], edges, c.rng.integers(0, N, 32)])).astype(np.int32)
+        ref = np.zeros((s.EL, M, N), np.float32)
+        oracle.wgrad(A, lda, B, ldb, off, M, N, s.cap, groups=groups, cols=cols, out=ref)
+        g = got.cpu().numpy()
+        for j in groups:
+            assert_equal(f"{name}[{j}]", g[j][:, cols], ref[j][:, cols])
+    del dx, dwg, dwu, dwd
