@@ -151,3 +151,31 @@ def test_route_backward_shapes(T, E, K):
     again = _lib.moe_route_backward(d_idx, d_g, d_dg, E)
     torch.cuda.synchronize()
     assert np.array_equal(again.cpu().numpy().view(np.uint32), got.view(np.uint32))
+
+
+def _int_bits(rng, shape, lo, hi):
+    table = np.array([np.float32(v).view(np.uint32) >> 16 for v in range(lo, hi + 1)], np.uint16)
+    return table[rng.integers(0, hi - lo + 1, shape, dtype=np.int8)]
+
+
+@pytest.mark.parametrize("k", range(len(SMALL)))
+def test_router_exact_on_integer_operands(k):
+    """The router projection and its backward on small-integer x, W_r, bias and dlogits: every product and
+    sum is exact in fp32 in any order (the contraction chunks and their partial sums included), so logits,
+    dx and dW_r must equal the oracle's bits exactly."""
+    shape, why = SMALL[k]
+    T, H, E = shape.T, shape.H, shape.E
+    rng = np.random.default_rng(41 + k)
+    x = _int_bits(rng, (T, H), -2, 2)
+    w = _int_bits(rng, (H, E), -1, 1)
+    bias = rng.integers(-3, 4, E).astype(np.float32)
+    dl = rng.integers(-2, 3, (T, E)).astype(np.float32)
+    dev = pipeline.to_device(dict(x=x, w=w, b=bias))
+    logits = _lib.moe_router_logits(dev["x"], dev["w"], dev["b"])
+    dx, dw = _lib.moe_router_backward(dev["x"], dev["w"], torch.from_numpy(dl).cuda())
+    torch.cuda.synchronize()
+    ref = oracle.router_logits(x, w, bias)
+    assert_equal("logits", bits(logits), ref.astype(np.float32))
+    rdx, rdw = oracle.router_backward(x, w, dl)
+    assert_equal("dx", bits(dx), rdx)
+    assert_equal("dw_r", bits(dw), rdw)

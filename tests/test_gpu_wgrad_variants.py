@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import oracle
-from helpers import assert_close
+from helpers import assert_close, assert_equal
 from routing_permute_groupgemm_amd import _lib, pipeline, synth
 
 pytestmark = pytest.mark.gpu
@@ -104,3 +104,21 @@ def test_gate_up_pair_is_two_bitwise_wgrads(H, F):
     ref_u = oracle.wgrad(a, H, np.ascontiguousarray(dab[:, F:]), F, offsets, H, F, R)
     assert_close("dw_gate", g.cpu().numpy(), ref_g)
     assert_close("dw_up", u.cpu().numpy(), ref_u)
+
+
+@pytest.mark.parametrize("S", [2, 3, 5])
+def test_split_exact_on_integer_operands(S):
+    """The non-bitwise weight gradient on small-integer operands: the chunk partials and their sum are
+    exact in fp32, so dW must equal the oracle's (bitwise path's) bits, whatever the chunking."""
+    M, N = 192, 320
+    rng = np.random.default_rng(60 + S)
+    counts = COUNTS
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R = int(offsets[-1])
+    table = np.array([np.float32(v).view(np.uint32) >> 16 for v in range(-2, 3)], np.uint16)
+    a = table[rng.integers(0, 5, (R, M), dtype=np.int8)]
+    b = table[rng.integers(0, 5, (R, N), dtype=np.int8)]
+    dev = pipeline.to_device(dict(a=a, b=b, offsets=offsets))
+    dw = _lib.moe_wgrad_split(dev["a"], M, dev["b"], N, dev["offsets"], len(counts), M, N, R, S)
+    torch.cuda.synchronize()
+    assert_equal("dw", dw.cpu().numpy(), oracle.wgrad(a, M, b, N, offsets, M, N, R))
