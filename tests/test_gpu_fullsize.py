@@ -350,8 +350,9 @@ def _int_bits(rng, shape, lo, hi):
 def test_integer_operands_exact_at_full_size(case):
     """The GroupGEMMs at full size on small-integer operands (products and sums exact in fp32 in any order,
     so the stored bits must equal the oracle's exactly): the saved (a, b) of the gate/up GEMM and the down
-    GEMM on the sampled rows and whole tiles, and for training workloads the gate/up dgrad and dW_gate,
-    dW_up, dW_down on the sampled experts and columns."""
+    GEMM on the sampled rows and whole tiles, and for training workloads the gate/up dgrad, the down
+    dgrad at a saved a of 0 (its SwiGLU backward then exact) and dW_gate, dW_up, dW_down on the sampled
+    experts and columns."""
     c = case
     s = c.shape
     rng = np.random.default_rng(23)
@@ -385,9 +386,20 @@ def test_integer_operands_exact_at_full_size(case):
     _lib.moe_grouped_gemm(d2["dab"], d["wg"], d["wu"], 1, c.buf.offsets, s.F, s.H, s.cap, dx)
     dwg, dwu = _lib.moe_wgrad_gate_up(d["x"], d2["dab"], c.buf.offsets, s.EL, s.cap)
     dwd = _lib.moe_wgrad(d["h"], s.F, d["x"], s.H, c.buf.offsets, s.EL, s.F, s.H, s.cap)
+    # the down dgrad with a saved a of 0 (sigmoid 1/2 exactly): exact da = dh * b / 2 and db = 0
+    ab0 = dab.copy()
+    ab0[:, :s.F] = 0
+    dy = _int_bits(rng, (s.cap, s.H), -2, 2)
+    d3 = pipeline.to_device(dict(ab0=ab0, dy=dy))
+    dab_o = torch.empty((s.cap, 2 * s.F), dtype=torch.bfloat16, device="cuda")
+    _lib.moe_grouped_gemm(d3["dy"], d["wd"], None, 1, c.buf.offsets, s.H, s.F, s.cap, dab_o,
+                          epilogue=_lib.MOE_EPI_SWIGLU_BWD, ab=d3["ab0"])
     torch.cuda.synchronize()
     ref_dx = oracle.bwd_up(dab, wg, wu, off, s.cap, rows=rows)
     assert_equal("dx_perm", bits(dx)[rows], ref_dx[rows])
+    ref_dab = oracle.bwd_down(dy, wd, ab0, off, s.cap, rows=rows)
+    assert_equal("dab (a = 0)", bits(dab_o)[rows], ref_dab[rows])
+    del dab_o, d3
     counts = c.ref_pm["counts"]
     groups = np.unique([int(np.argmax(counts)), int(np.argmin(counts)), 0, s.EL - 1,
                         *c.rng.integers(0, s.EL, 2).tolist()]).astype(np.int32)

@@ -502,7 +502,8 @@ def test_gemms_exact_on_integer_operands(tile, monkeypatch):
     row, column or k-step taken twice, skipped or taken from a neighbouring expert changes them.  Experts
     sit at every row-block and tile edge; N is not a multiple of the tile width.  Checked: the saved
     (a, b) of the gate/up GEMM (copy and zero-copy), the down GEMM, the gate/up dgrad over both
-    weights, and dW_gate, dW_up (one pass, copy and zero-copy) and dW_down in fp32."""
+    weights, dW_gate, dW_up (one pass, copy and zero-copy) and dW_down in fp32, and the down dgrad with
+    its SwiGLU-backward epilogue at a saved a of 0, where the sigmoid is exactly 1/2."""
     monkeypatch.setenv("MOE_GEMM_TILE", tile)
     rng = np.random.default_rng(17)
     counts = np.array(EDGE_COUNTS, np.int32)
@@ -530,6 +531,14 @@ def test_gemms_exact_on_integer_operands(tile, monkeypatch):
     dwg, dwu = _lib.moe_wgrad_gate_up(dev["x"], dev["dab"], dev["off"], EL, R)
     zwg, zwu = _lib.moe_wgrad_gate_up_gather(dev["x"], dev["src"], K, dev["dab"], dev["off"], EL, R)
     dwd = _lib.moe_wgrad(dev["h"], F, dev["x"], H, dev["off"], EL, F, H, R)
+    # the down dgrad with a saved a of 0 (sigmoid 1/2 exactly): da = dh * b / 2 and db = 0, exact
+    ab0 = dabin.copy()
+    ab0[:, :F] = 0
+    dy = _int_bf16(rng, (R, H), -2, 2)
+    d3 = pipeline.to_device(dict(ab0=ab0, dy=dy))
+    dab = torch.empty((R, 2 * F), dtype=torch.bfloat16, device="cuda")
+    _lib.moe_grouped_gemm(d3["dy"], dev["wd"], None, 1, dev["off"], H, F, R, dab, epilogue=_lib.MOE_EPI_SWIGLU_BWD,
+                          ab=d3["ab0"])
     torch.cuda.synchronize()
     _, ref_ab = oracle.expert_up(x, wg, wu, offsets, R, want_ab=True)
     assert_equal("ab_save", bits(ab), ref_ab)
@@ -543,3 +552,4 @@ def test_gemms_exact_on_integer_operands(tile, monkeypatch):
     assert_equal("dW_gate (zero-copy)", zwg.cpu().numpy(), ref_g)
     assert_equal("dW_up (zero-copy)", zwu.cpu().numpy(), ref_u)
     assert_equal("dW_down", dwd.cpu().numpy(), oracle.wgrad(hin, F, x, H, offsets, F, H, R))
+    assert_equal("dab (a = 0)", bits(dab), oracle.bwd_down(dy, wd, ab0, offsets, R))
