@@ -553,3 +553,29 @@ def test_gemms_exact_on_integer_operands(tile, monkeypatch):
     assert_equal("dW_up (zero-copy)", zwu.cpu().numpy(), ref_u)
     assert_equal("dW_down", dwd.cpu().numpy(), oracle.wgrad(hin, F, x, H, offsets, F, H, R))
     assert_equal("dab (a = 0)", bits(dab), oracle.bwd_down(dy, wd, ab0, offsets, R))
+
+
+def test_gate_grad_and_route_backward_exact_on_exact_values():
+    """The gate gradient (the fused gather's fp32 dot products, finished by a lane butterfly) and the
+    softmax/top-k backward (a fused multiply-add chain) on values whose every product and sum is exact in
+    fp32 (small integers; gates of a few bits), so that any order of the sums gives the same result: both
+    must equal the oracle's bits, with exactly 0 at pairs without a local row and at unchosen experts."""
+    rng = np.random.default_rng(29)
+    T, K, H, E = 500, 8, 192, 64
+    table = np.array([np.float32(v).view(np.uint32) >> 16 for v in range(-2, 3)], np.uint16)
+    d_out = table[rng.integers(0, 5, (T, H), dtype=np.int8)]
+    R = T * K
+    y = table[rng.integers(0, 5, (R, H), dtype=np.int8)]
+    pos = np.arange(R, dtype=np.int32).reshape(T, K)
+    pos[rng.random((T, K)) < 0.2] = -1  # pairs without a local row
+    gates = (rng.integers(1, 8, (T, K)) / 8.0).astype(np.float32)
+    dev = pipeline.to_device(dict(d=d_out, y=y, pos=pos, g=gates))
+    dy = torch.empty((R, H), dtype=torch.bfloat16, device="cuda")
+    _, dg = _lib.moe_gather_gate_grad(dev["d"], dev["pos"], dev["g"], dev["y"], dy)
+    idx = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
+    dgi = rng.integers(-4, 5, (T, K)).astype(np.float32)
+    d2 = pipeline.to_device(dict(idx=idx, dgi=dgi))
+    dl = _lib.moe_route_backward(d2["idx"], dev["g"], d2["dgi"], E)
+    torch.cuda.synchronize()
+    assert_equal("dgates", dg.cpu().numpy(), oracle.gate_grad(d_out, y, pos))
+    assert_equal("dlogits", dl.cpu().numpy(), oracle.route_backward(idx, gates, dgi, E))
